@@ -1,0 +1,6 @@
+"""CPU oracle (test infrastructure; see kvd_oracle's header)."""
+from .kvd_oracle import (  # noqa: F401
+    ConcatCache, accept, argmax_rows, attend, attend_cross, attend_self,
+    decode_step, full_causal_attention, narrow, reorder, rope, verify_accept,
+    widen,
+)

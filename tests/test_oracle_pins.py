@@ -1,0 +1,377 @@
+"""Pins for the CPU oracle: each test ties an oracle function to something
+other than itself (values the pages print, closed forms, invariants, library
+routines computing the same definition, brute force on tiny inputs)."""
+import json
+import math
+import os
+import struct
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from kv_cached_decode_amd import inputs as I
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- dtypes ----
+
+def test_widen_f16_matches_struct_for_every_bit_pattern():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    mine = O.widen(bits.view(np.float16), "f16")
+    ref = np.array([struct.unpack("<e", struct.pack("<H", int(b)))[0] for b in bits])
+    same = (mine == ref) | (np.isnan(mine) & np.isnan(ref))
+    assert same.all()
+
+
+def test_widen_bf16_matches_torch_for_every_bit_pattern():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    mine = O.widen(bits, "bf16")
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    same = (mine == ref) | (np.isnan(mine) & np.isnan(ref))
+    assert same.all()
+
+
+def test_narrow_bf16_matches_torch_on_float32_values():
+    g = np.random.default_rng(7)
+    x32 = np.concatenate([
+        g.standard_normal(200000).astype(np.float32),
+        (g.standard_normal(20000) * 1e-39).astype(np.float32),     # bf16 subnormals
+        (g.standard_normal(20000) * 1e30).astype(np.float32),
+        # exact ties: low 16 bits == 0x8000
+        ((g.integers(0, 1 << 15, 20000, dtype=np.uint32) << 16) | 0x8000).view(np.float32),
+    ])
+    x32 = x32[np.isfinite(x32)]
+    mine = O.narrow(x32.astype(np.float64), "bf16")
+    ref = torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(mine, ref)
+
+
+def test_narrow_rounds_once_from_float64():
+    # just above a bf16 / f16 tie: a value rounded through float32 first would
+    # land exactly on the tie and go to even (down); direct rounding goes up.
+    ulp_bf16 = 2.0 ** -7
+    x = 1.0 + ulp_bf16 / 2 * (1 + 2.0 ** -40)
+    assert O.widen(O.narrow(np.array([x]), "bf16"), "bf16")[0] == 1.0 + ulp_bf16
+    ulp_f16 = 2.0 ** -10
+    y = 1.0 + ulp_f16 / 2 * (1 + 2.0 ** -40)
+    assert O.widen(O.narrow(np.array([y]), "f16"), "f16")[0] == 1.0 + ulp_f16
+    # exact ties go to the even neighbour
+    assert O.widen(O.narrow(np.array([1.0 + ulp_bf16 / 2]), "bf16"), "bf16")[0] == 1.0
+    assert O.widen(O.narrow(np.array([1.0 + 3 * ulp_bf16 / 2]), "bf16"), "bf16")[0] == 1.0 + 2 * ulp_bf16
+
+
+# ------------------------------------------------------------------ rope ----
+
+def test_rope_position_zero_is_identity():
+    x = np.random.default_rng(0).standard_normal((3, 5, 64))
+    assert np.array_equal(O.rope(x, np.zeros(5), 10000.0), x)
+
+
+def test_rope_first_pair_closed_form():
+    # theta_0 = 1: unit vector e_0 at position p goes to (cos p, sin p) in slots (0, D/2)
+    D = 64
+    for p in (1, 7, 511, 1023):
+        e0 = np.zeros((1, D)); e0[0, 0] = 1.0
+        r = O.rope(e0, [p], 10000.0)[0]
+        assert r[0] == pytest.approx(math.cos(p), abs=1e-15)
+        assert r[D // 2] == pytest.approx(math.sin(p), abs=1e-15)
+        eh = np.zeros((1, D)); eh[0, D // 2] = 1.0
+        r = O.rope(eh, [p], 10000.0)[0]
+        assert r[0] == pytest.approx(-math.sin(p), abs=1e-15)
+        assert r[D // 2] == pytest.approx(math.cos(p), abs=1e-15)
+    # pair i = D/4 turns at base^(-1/2) = 1/100 per position
+    ei = np.zeros((1, D)); ei[0, D // 4] = 1.0
+    r = O.rope(ei, [300], 10000.0)[0]
+    assert r[D // 4] == pytest.approx(math.cos(3.0), abs=1e-13)
+    assert r[D // 4 + D // 2] == pytest.approx(math.sin(3.0), abs=1e-13)
+
+
+def test_rope_equals_complex_rotation():
+    g = np.random.default_rng(1)
+    D, T = 64, 9
+    x = g.standard_normal((T, D))
+    pos = g.integers(0, 2000, T)
+    r = O.rope(x, pos, 10000.0)
+    z = x[:, : D // 2] + 1j * x[:, D // 2:]
+    theta = 10000.0 ** (-np.arange(0, D, 2) / D)
+    zr = z * np.exp(1j * pos[:, None] * theta[None, :])
+    assert np.allclose(r[:, : D // 2], zr.real, atol=1e-12)
+    assert np.allclose(r[:, D // 2:], zr.imag, atol=1e-12)
+
+
+def test_rope_scores_depend_on_relative_position_only():
+    g = np.random.default_rng(2)
+    q, k = g.standard_normal((1, 64)), g.standard_normal((1, 64))
+    base = [float(O.rope(q, [p], 1e4)[0] @ O.rope(k, [p - 5], 1e4)[0]) for p in (5, 100, 700)]
+    assert np.allclose(base, base[0], atol=1e-11)
+    norms = np.linalg.norm(O.rope(q, [321], 1e4)), np.linalg.norm(q)
+    assert norms[0] == pytest.approx(norms[1], rel=1e-14)
+
+
+# ------------------------------------------------------------- attention ----
+
+def _sdpa(q, k, v, scale, causal_offset):
+    """torch's own attention (CPU, float64) on [B, H, N, D] / [B, Hk, L, D]."""
+    B, Hq, N, D = q.shape
+    Hk, L = k.shape[1], k.shape[2]
+    kk = torch.from_numpy(np.repeat(k, Hq // Hk, axis=1)).expand(B, Hq, L, D)
+    vv = torch.from_numpy(np.repeat(v, Hq // Hk, axis=1)).expand(B, Hq, L, D)
+    mask = None
+    if causal_offset is not None:
+        mask = torch.from_numpy(np.arange(L)[None, :] <= (causal_offset + np.arange(N))[:, None])
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), kk, vv, attn_mask=mask, scale=scale).numpy()
+
+
+@pytest.mark.parametrize("B,Bkv,Hq,Hkv,N,L,offset", [
+    (1, 1, 6, 6, 1, 33, 32),       # single decode query
+    (2, 2, 4, 4, 5, 40, 35),       # five offset-causal queries
+    (2, 2, 9, 3, 7, 30, 23),       # grouped heads
+    (5, 1, 4, 4, 1, 50, None),     # shared cross cache, no mask
+    (1, 1, 3, 1, 16, 16, 0),       # prefill from an empty cache
+])
+def test_attend_matches_torch_sdpa(B, Bkv, Hq, Hkv, N, L, offset):
+    g = np.random.default_rng(3)
+    q = g.standard_normal((B, Hq, N, 64)) * 2
+    k = g.standard_normal((Bkv, Hkv, L, 64))
+    v = g.standard_normal((Bkv, Hkv, L, 64))
+    mine = O.attend(q, k, v, 0.125, offset)
+    ref = _sdpa(q, np.broadcast_to(k, (B,) + k.shape[1:]).copy(),
+                np.broadcast_to(v, (B,) + v.shape[1:]).copy(), 0.125, offset)
+    assert np.max(np.abs(mine - ref)) < 1e-12
+
+
+def test_attend_closed_forms():
+    g = np.random.default_rng(4)
+    v = g.standard_normal((1, 1, 20, 64))
+    k = g.standard_normal((1, 1, 20, 64))
+    q = g.standard_normal((1, 1, 1, 64))
+    # one key: the output is that value row, exactly
+    assert np.array_equal(O.attend(q, k[:, :, :1], v[:, :, :1], 0.125, None)[0, 0, 0], v[0, 0, 0])
+    # all keys equal: uniform weights, the mean of V
+    keq = np.repeat(k[:, :, :1], 20, axis=2)
+    assert np.allclose(O.attend(q, keq, v, 0.125, None)[0, 0, 0], v[0, 0].mean(0), atol=1e-14)
+    # q = 0: uniform weights too
+    assert np.allclose(O.attend(np.zeros_like(q), k, v, 0.125, None)[0, 0, 0], v[0, 0].mean(0), atol=1e-14)
+    # one key ahead by 60 in score: its value row within e^-60
+    kd = np.zeros((1, 1, 20, 64)); kd[0, 0, 13, 0] = 60.0 / 0.125
+    qd = np.zeros((1, 1, 1, 64)); qd[0, 0, 0, 0] = 1.0
+    assert np.allclose(O.attend(qd, kd, v, 0.125, None)[0, 0, 0], v[0, 0, 13], atol=1e-20 + 30 * math.exp(-60))
+    # prefill query 0 sees only key 0
+    qq = g.standard_normal((1, 1, 4, 64))
+    assert np.array_equal(O.attend(qq, k[:, :, :4], v[:, :, :4], 0.125, 0)[0, 0, 0], v[0, 0, 0])
+
+
+def test_attend_sentinel_mask_one_hot_values():
+    # V = identity rows: the output of each query is its weight vector, so it
+    # names exactly which keys were seen.
+    L, N = 24, 5
+    g = np.random.default_rng(5)
+    q = g.standard_normal((1, 2, N, 64))
+    k = g.standard_normal((1, 2, L, 64))
+    v = np.zeros((1, 2, L, 64)); v[0, :, np.arange(L), np.arange(L)] = 1.0
+    out = O.attend(q, k, v, 0.125, L - N)
+    for i in range(N):
+        seen = L - N + i + 1
+        assert np.all(out[0, :, i, :seen] > 0)
+        assert np.all(out[0, :, i, seen:] == 0)
+        assert np.allclose(out[0, :, i].sum(-1), 1.0, atol=1e-14)
+
+
+def test_attend_cross_is_key_permutation_invariant():
+    g = np.random.default_rng(6)
+    q = g.standard_normal((2, 3, 2, 64))
+    k = g.standard_normal((2, 3, 31, 64))
+    v = g.standard_normal((2, 3, 31, 64))
+    perm = g.permutation(31)
+    a = O.attend(q, k, v, 0.125, None)
+    b = O.attend(q, k[:, :, perm], v[:, :, perm], 0.125, None)
+    assert np.allclose(a, b, atol=1e-13)
+
+
+# ------------------------------------- cached incremental == recompute ------
+
+def _int_tokens(g, T, d_model):
+    return g.integers(-3, 4, size=(T, d_model)).astype(np.float64)
+
+
+def test_incremental_decode_equals_full_recompute():
+    """The cache only removes redundant work: appending each token's K/V and
+    attending its query over the cache equals full causal recomputation from
+    the hidden states at every step. Integer-valued inputs make every
+    projection exact in float32 storage, so both routes see the same K/V."""
+    g = np.random.default_rng(8)
+    T, d_model, H, D = 20, 16, 2, 64
+    X = _int_tokens(g, T, d_model)
+    Wq, Wk, Wv = (g.integers(-2, 3, size=(d_model, H * D)).astype(np.float64) for _ in range(3))
+    scale = 1.0 / 8.0 / 8.0
+    cache = O.ConcatCache(1, H, D, "f32")
+    for t in range(T):
+        x = X[t:t + 1]
+        k_new = (x @ Wk).reshape(1, H, 1, D)
+        v_new = (x @ Wv).reshape(1, H, 1, D)
+        q = (x @ Wq).reshape(1, H, 1, D)
+        cache.append(O.narrow(k_new, "f32"), O.narrow(v_new, "f32"))
+        inc = O.attend_self(O.narrow(q, "f32"), cache, scale)[0, :, 0]
+        # recompute: project every token so far again, causal attention, row t
+        Xs = X[: t + 1]
+        Q = (Xs @ Wq).reshape(t + 1, H, D).transpose(1, 0, 2)
+        K = (Xs @ Wk).reshape(t + 1, H, D).transpose(1, 0, 2)
+        V = (Xs @ Wv).reshape(t + 1, H, D).transpose(1, 0, 2)
+        full = O.full_causal_attention(Q, K, V, scale)[:, t]
+        assert np.max(np.abs(inc - full)) < 1e-12
+
+
+def test_prefill_then_decode_with_rope_equals_recompute():
+    """GQA + rotary: prefill T0 tokens in one append, then decode one token at
+    a time; every query's output equals full causal recomputation with q and
+    k rotated at their absolute positions."""
+    g = np.random.default_rng(9)
+    B, Hq, Hk, D, T0, T = 2, 6, 2, 64, 12, 20
+    dt = "f32"
+    Qall = O.narrow(g.standard_normal((B, Hq, T, D)), dt)
+    Kall = O.narrow(g.standard_normal((B, Hk, T, D)), dt)
+    Vall = O.narrow(g.standard_normal((B, Hk, T, D)), dt)
+    cache = O.ConcatCache(B, Hk, D, dt)
+    cache.append(Kall[:, :, :T0], Vall[:, :, :T0], rope_base=1e4)
+    outs = [O.attend_self(Qall[:, :, :T0], cache, 0.125, rope_base=1e4)]
+    for t in range(T0, T):
+        cache.append(Kall[:, :, t:t + 1], Vall[:, :, t:t + 1], rope_base=1e4)
+        outs.append(O.attend_self(Qall[:, :, t:t + 1], cache, 0.125, rope_base=1e4))
+    inc = np.concatenate(outs, axis=2)
+    pos = np.arange(T)
+    Krot = O.widen(O.narrow(O.rope(O.widen(Kall, dt), pos, 1e4), dt), dt)
+    Qrot = O.rope(O.widen(Qall, dt), pos, 1e4)
+    V = O.widen(Vall, dt)
+    for b in range(B):
+        for h in range(Hq):
+            full = O.full_causal_attention(Qrot[b, h][None], Krot[b, h // 3][None], V[b, h // 3][None], 0.125)[0]
+            assert np.max(np.abs(inc[b, h] - full)) < 1e-12
+
+
+# --------------------------------------------------------------- reorder ----
+
+def test_reorder_brute_force_and_composition():
+    g = np.random.default_rng(10)
+    x = g.standard_normal((5, 2, 7, 4))
+    for _ in range(20):
+        p = g.integers(0, 5, 5)
+        got = O.reorder(x, p)
+        for b in range(5):
+            for h in range(2):
+                for s in range(7):
+                    for d in range(4):
+                        assert got[b, h, s, d] == x[p[b], h, s, d]
+        p2 = g.integers(0, 5, 5)
+        assert np.array_equal(O.reorder(O.reorder(x, p), p2), O.reorder(x, p[p2]))
+    assert np.array_equal(O.reorder(x, np.arange(5)), x)
+    # duplicate parents, in the direction of the beam step: new[b] = old[parent[b]]
+    got = O.reorder(x, [2, 2, 0, 4, 2])
+    assert np.array_equal(got[0], x[2]) and np.array_equal(got[2], x[0]) and np.array_equal(got[4], x[2])
+
+
+def test_cache_reorder_moves_k_and_v_together():
+    c = O.ConcatCache(3, 1, 4, "f16")
+    k = np.arange(3 * 4 * 2, dtype=np.float16).reshape(3, 1, 2, 4)
+    c.append(k, -k)
+    c.reorder([1, 1, 0])
+    assert np.array_equal(c.k[0], k[1]) and np.array_equal(c.v[0], -k[1]) and np.array_equal(c.k[2], k[0])
+
+
+# ---------------------------------------------------------------- argmax ----
+
+def test_argmax_matches_numpy_first_occurrence():
+    g = np.random.default_rng(11)
+    x = g.standard_normal((7, 3001)).astype(np.float32)
+    x[1, [5, 900, 3000]] = 9.0          # ties: lowest index wins
+    x[2, :] = -np.inf                   # all -inf -> 0
+    x[3, :100] = -np.inf
+    x[4, :] = 1.0                       # all equal -> 0
+    x[5, 3000] = 50.0                   # last element
+    assert np.array_equal(O.argmax_rows(x), np.argmax(x, axis=-1))
+    assert O.argmax_rows(x)[1] == 5 and O.argmax_rows(x)[2] == 0 and O.argmax_rows(x)[5] == 3000
+
+
+def test_argmax_after_inf_mask_language_detection_style():
+    # -inf masking of every entry but a subset, then argmax over the rest
+    g = np.random.default_rng(12)
+    x = g.standard_normal((4, 500))
+    allowed = np.array([3, 70, 71, 400])
+    masked = np.full_like(x, -np.inf)
+    masked[:, allowed] = x[:, allowed]
+    got = O.argmax_rows(masked)
+    assert np.array_equal(got, allowed[np.argmax(x[:, allowed], axis=1)])
+
+
+# ---------------------------------------------------------------- accept ----
+
+def test_accept_worked_example_from_the_page():
+    fx = json.load(open(os.path.join(GOLDEN, "spec_worked_example.json")))
+    vocab = fx["vocab"]
+    draft = np.array([vocab[w] for w in fx["draft_words"]])
+    main = np.array([vocab[w] for w in fx["main_words"]])
+    n, nxt = O.accept(main, draft)
+    assert n == fx["expected_accept_len"]
+    assert nxt == vocab[fx["expected_next_word"]]
+    emitted = list(draft[:n]) + [nxt]
+    assert emitted == [vocab[w] for w in fx["expected_emitted_words"]]
+
+
+def test_accept_edge_rows():
+    assert O.accept(np.array([1, 2, 3, 4, 5]), np.array([1, 2, 3, 4, 5])) == (5, -1)
+    assert O.accept(np.array([1, 2, 3, 4, 5, 6]), np.array([1, 2, 3, 4, 5])) == (5, 6)
+    assert O.accept(np.array([9, 2, 3, 4, 5]), np.array([1, 2, 3, 4, 5])) == (0, 9)
+    assert O.accept(np.array([1, 2, 3, 4, 7]), np.array([1, 2, 3, 4, 5])) == (4, 7)
+
+
+def _toy_main_model(V, seed):
+    """A deterministic 'main model': the next token is a fixed function of
+    the last two tokens and the position."""
+    table = np.random.default_rng(seed).integers(0, V, size=(V, V, 64))
+    return lambda seq: int(table[seq[-2], seq[-1], len(seq) % 64])
+
+
+@pytest.mark.parametrize("R_extra", [0, 1])
+def test_speculative_loop_emits_the_greedy_stream(R_extra):
+    """Output identity: drafting N tokens and keeping the verified prefix plus
+    the main model's correction reproduces plain greedy decoding exactly."""
+    V, N, total = 23, 5, 300
+    main = _toy_main_model(V, 13)
+    g = np.random.default_rng(14)
+    greedy = [1, 2]
+    while len(greedy) < total + 2:
+        greedy.append(main(greedy))
+    seq = [1, 2]
+    while len(seq) < total + 2:
+        drafts, ctx = [], list(seq)
+        for _ in range(N):
+            t = main(ctx) if g.random() < 0.75 else int(g.integers(0, V))
+            drafts.append(t); ctx.append(t)
+        # the main model scores context + drafts in one pass: row i is its
+        # choice for the slot of draft i (R = N) plus a bonus row (R = N + 1)
+        rows = [main(seq + drafts[:i]) for i in range(N + R_extra)]
+        logits = np.full((1, len(rows), V), -1.0)
+        logits[0, np.arange(len(rows)), rows] = 1.0
+        _, acc, nxt = O.verify_accept(logits, np.array([drafts]))
+        seq += drafts[: acc[0]] + ([int(nxt[0])] if nxt[0] >= 0 else [])
+    assert seq[: total + 2] == greedy[: total + 2]
+
+
+def test_accept_length_distribution_at_p_075():
+    """Drafts copy the planted argmax with p = 0.75: P(n = k) = 0.75^k * 0.25
+    for k < 5 and 0.75^5 for k = 5."""
+    w = I.WHISPER_VERIFY
+    counts = np.zeros(6)
+    trials = 1500
+    for t in range(trials):
+        logits, draft = I.verify_logits(w, t, V=2000)
+        _, acc, _ = O.verify_accept(logits, draft)
+        counts[acc[0]] += 1
+    p = np.array([0.75 ** k * 0.25 for k in range(5)] + [0.75 ** 5])
+    sd = np.sqrt(trials * p * (1 - p))
+    assert np.all(np.abs(counts - trials * p) < 4 * sd + 1)
+    mean_tokens = (counts * np.array([1, 2, 3, 4, 5, 5])).sum() / trials
+    assert mean_tokens == pytest.approx(sum(p * np.array([1, 2, 3, 4, 5, 5])), abs=0.15)
