@@ -1,0 +1,291 @@
+"""Decode-step benchmark: Whisper-large-v2-shaped greedy decoding on one GPU.
+
+One step = for each of the 32 decoder layers: append the new token's K/V to
+the self cache (kv_append, T=1), self attention of the token's query over the
+cache (decode_attn_self, N=1), cross attention over the 1500-frame cache built
+once before timing (decode_attn_cross). B=1, 20 heads of 64, fp16 storage,
+fp32 accumulation. Steps walk the self cache from length 1 to 448 and wrap.
+
+Prints one JSON line. `value` is decode steps/s over the timed steps (hipGraph
+replay of one captured graph per step, inputs resident in HBM). Also reported:
+effective KV GB/s and its fraction of the 8 TB/s HBM peak, the dominant
+kernel's roofline (cross attention, timed with HIP events on its stream), and
+the CPU oracle timed on a bounded sample of the same steps.
+
+    python bench.py [--gpus 1] [--steps 448] [--warmup 64] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+LAYERS, H, D, S_MAX, FRAMES = 32, 20, 64, 448, 1500
+ROW_BYTES = H * D * 2                      # one position of one layer, K or V, fp16
+CROSS_BYTES = 2 * FRAMES * ROW_BYTES       # K+V read by one cross-attention launch
+METRIC = "decode-attn steps/s + effective KV GB/s (% HBM peak), large-v2 shape, 1 GPU"
+WORKLOAD = ("whisper-large-v2 greedy decode step: 32 layers x [kv_append T=1, self attention "
+            "N=1 over len 1..448, cross attention over 1500 frames], B1, 20 heads x 64, fp16 "
+            "storage / fp32 accumulate")
+KERNEL_SOURCES = ["kv_cached_decode_amd/csrc/kvd_kernels.hip",
+                  "kv_cached_decode_amd/csrc/kvd_device.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_cross_attention.json")
+
+
+def kv_bytes_per_step(L: int) -> int:
+    """Algorithmic KV bytes of one step at self length L (after the append):
+    self K+V read, cross K+V read, new K+V written, over every layer."""
+    return LAYERS * (2 * L * ROW_BYTES + CROSS_BYTES + 2 * ROW_BYTES)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per cross-attention launch from the committed rocprofv3
+    counter runs, if they were taken on the current kernel source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Engine:
+    """Device state of the benchmark: caches, per-step inputs, outputs."""
+
+    def __init__(self, torch, kb, I):
+        self.torch, self.kb = torch, kb
+        w = I.WHISPER_GREEDY
+        self.w = w
+        dev = "cuda"
+        self.scale = w.attn_scale
+        self.self_c, self.cross_c = [], []
+        self.k_new, self.v_new, self.q_self, self.q_cross = [], [], [], []
+        g = np.random.default_rng([w.seed, 77])
+        for l in range(LAYERS):
+            k_all, v_all = I.self_kv(w, l)                          # [1, 20, 448, 64]
+            # token-major so that token t's [1, 20, 1, 64] rows are contiguous
+            self.k_new.append(torch.from_numpy(np.ascontiguousarray(
+                k_all.transpose(2, 0, 1, 3)[:, :, :, None, :])).to(dev))
+            self.v_new.append(torch.from_numpy(np.ascontiguousarray(
+                v_all.transpose(2, 0, 1, 3)[:, :, :, None, :])).to(dev))
+            xk, xv = I.cross_kv(w, l)
+            xc = kb.Cache(1, H, FRAMES, torch.float16, dev)
+            kb.kv_append(xc, torch.from_numpy(xk).to(dev), torch.from_numpy(xv).to(dev), 0)
+            self.cross_c.append(xc)
+            self.self_c.append(kb.Cache(1, H, S_MAX, torch.float16, dev))
+            qs = I.to_storage(g.standard_normal((S_MAX, 1, H, 1, D), dtype=np.float32) / 8, "f16")
+            qx = I.to_storage(g.standard_normal((S_MAX, 1, H, 1, D), dtype=np.float32) / 8, "f16")
+            self.q_self.append(torch.from_numpy(qs).to(dev))
+            self.q_cross.append(torch.from_numpy(qx).to(dev))
+        self.out_self = [torch.empty((1, H, 1, D), dtype=torch.float32, device=dev) for _ in range(LAYERS)]
+        self.out_cross = [torch.empty((1, H, 1, D), dtype=torch.float32, device=dev) for _ in range(LAYERS)]
+        self.ws = kb.workspace(max(kb.attn_workspace_bytes(1, H, 1, S_MAX),
+                                   kb.attn_workspace_bytes(1, H, 1, FRAMES)), dev)
+        torch.cuda.synchronize()
+
+    def step(self, s: int):
+        """Decode step s: the self cache grows to length s + 1."""
+        kb = self.kb
+        L = s + 1
+        for l in range(LAYERS):
+            kb.kv_append(self.self_c[l], self.k_new[l][s], self.v_new[l][s], s)
+            kb.decode_attn_self(self.q_self[l][s], self.self_c[l], L, self.scale,
+                                out=self.out_self[l], ws=self.ws)
+            kb.decode_attn_cross(self.q_cross[l][s], self.cross_c[l], FRAMES, self.scale,
+                                 out=self.out_cross[l], ws=self.ws)
+
+    def cross(self, l: int, s: int):
+        self.kb.decode_attn_cross(self.q_cross[l][s], self.cross_c[l], FRAMES, self.scale,
+                                  out=self.out_cross[l], ws=self.ws)
+
+
+def capture_graphs(torch, eng: Engine):
+    graphs = []
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for s in range(S_MAX):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                eng.step(s)
+            graphs.append(g)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def time_cross_kernel(torch, eng: Engine, reps: int = 4):
+    """Average duration of one cross-attention launch, HIP events recorded
+    around each launch on the stream it runs on."""
+    stream = torch.cuda.current_stream()
+    times = []
+    for r in range(reps):
+        for l in range(LAYERS):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            eng.cross(l, (r * 37 + l) % S_MAX)
+            b.record(stream)
+            times.append((a, b))
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in times]
+    return float(np.mean(ms)) * 1e-3, float(np.median(ms)) * 1e-3
+
+
+def cpu_baseline(target_s: float = 15.0):
+    """The CPU oracle (numpy, float64) on a bounded sample of the same steps:
+    full 32-layer steps at lengths spread over 1..448, BLAS pinned to one
+    thread."""
+    import oracle as O
+    from kv_cached_decode_amd import inputs as I
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:  # noqa: BLE001
+        limiter = None
+    w = I.WHISPER_GREEDY
+    xcs = []
+    for l in range(LAYERS):
+        xk, xv = I.cross_kv(w, l)
+        c = O.ConcatCache(1, H, D, "f16")
+        c.set_once(xk, xv)
+        xcs.append(c)
+    kv = [I.self_kv(w, l) for l in range(LAYERS)]
+    lengths = [1, 112, 224, 336, 448, 56, 168, 280, 392, 28, 140, 252, 364, 420]
+    spent, times, used = 0.0, [], []
+    for L in lengths:
+        caches = []
+        for l in range(LAYERS):
+            c = O.ConcatCache(1, H, D, "f16")
+            c.append(kv[l][0][:, :, :L - 1], kv[l][1][:, :, :L - 1])
+            caches.append(c)
+        q = [I.queries(w, l, L) for l in range(LAYERS)]
+        qx = [I.queries(w, l, L, cross=True) for l in range(LAYERS)]
+        kn = [kv[l][0][:, :, L - 1:L] for l in range(LAYERS)]
+        vn = [kv[l][1][:, :, L - 1:L] for l in range(LAYERS)]
+        t0 = time.perf_counter()
+        O.decode_step(q, qx, kn, vn, caches, xcs, w.attn_scale)
+        dt = time.perf_counter() - t0
+        times.append(dt)
+        used.append(L)
+        spent += dt
+        if spent > target_s:
+            break
+    if limiter is not None:
+        limiter.unregister()
+    mean = float(np.mean(times))
+    return {"value": 1.0 / mean, "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(times)} full 32-layer decode steps at self lengths {used} "
+                      f"(oracle: numpy float64, BLAS limited to 1 thread), {spent:.1f} s total"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=448)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--eager", action="store_true", help="also time eager (no graph) launches")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode step has no multi-GPU path in this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from kv_cached_decode_amd import binding as kb
+    from kv_cached_decode_amd import inputs as I
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    kb.lib()
+    print("bench: building device state", file=sys.stderr, flush=True)
+    eng = Engine(torch, kb, I)
+    print("bench: capturing graphs", file=sys.stderr, flush=True)
+    graphs = capture_graphs(torch, eng)
+
+    # warmup
+    for i in range(args.warmup):
+        graphs[i % S_MAX].replay()
+    torch.cuda.synchronize()
+
+    # timed region: steps continue from where warmup stopped (wrapping at 448)
+    start = args.warmup
+    seq = [(start + i) % S_MAX for i in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in seq:
+        graphs[s].replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kv_bytes = sum(kv_bytes_per_step(s + 1) for s in seq)
+
+    eager = None
+    if args.eager:
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for s in seq:
+            eng.step(s)
+        torch.cuda.synchronize()
+        eager = args.steps / (time.perf_counter() - t1)
+
+    k_avg, k_med = time_cross_kernel(torch, eng)
+    achieved = CROSS_BYTES / k_avg / 1e9
+    traffic = measured_traffic()
+
+    cpu = None if args.no_cpu else cpu_baseline()
+
+    steps_per_s = args.steps / elapsed
+    gbps = kv_bytes / elapsed / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(steps_per_s, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "layers": LAYERS, "batch": 1, "heads": H,
+                   "head_dim": D, "self_len": "1..448 (steps wrap)", "cross_frames": FRAMES,
+                   "launch": "one hipGraph per step, 96 kernels"},
+        "effective_kv_gbps": round(gbps, 1),
+        "hbm_peak_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "kernel": "decode_attn_cross (attn_kernel<f16, 1>)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "bytes_per_launch": CROSS_BYTES,
+                     "avg_launch_us": round(k_avg * 1e6, 3),
+                     "median_launch_us": round(k_med * 1e6, 3)},
+        "cpu_baseline": cpu,
+    }
+    if eager is not None:
+        line["eager_steps_per_s"] = round(eager, 2)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,173 @@
+/*
+ * kvdecode.h - C ABI of the KV-cached decoder-step library for AMD MI355X
+ * (gfx950). Plain C types only; every pointer named "device" is HIP device
+ * memory, every other pointer is host memory.
+ *
+ * Sources the operations follow (page title, section):
+ *   [W] "Whisper のデコーダー内部：Beam Search、Logit フィルター、KV キャッシュ"
+ *       (readoss.com): section "Inference 抽象と KV キャッシュ" - the
+ *       save_to_cache hook (self-attention K/V concatenated onto the cache,
+ *       cross-attention K/V stored once from the encoder output and reused),
+ *       the greedy decoder (argmax at temperature 0) and step 4 of the beam
+ *       search update (reorder the cache to the new beam order).
+ *   [N] "nanoVLM における KV キャッシュ実装" (agentlenshq.com): sections
+ *       "KV キャッシュが推論を最適化する方法" (per-layer key/value tensors of
+ *       shape (batch, heads, seq_cached, head_dim); new K/V appended, then the
+ *       current query attends over the cache) and "nanoVLM における技術的実装"
+ *       (grouped-query attention; start_pos keeps rotary positions absolute;
+ *       prefill then decode).
+ *   [S] "추측 디코딩으로 Whisper 추론 속도 2배 향상" (agentlenshq.com), section
+ *       "추측 디코딩이란?", and the aitime.ge translation of the same post
+ *       (its worked example): the main model scores the drafts in one pass,
+ *       drafts are kept up to the first mismatch, the main model's token
+ *       replaces the mismatch and the rest is dropped.
+ *
+ * Conventions shared by every call
+ *   - Element types: KVD_F32, KVD_F16 (IEEE binary16), KVD_BF16. Attention
+ *     accumulates in fp32 and writes fp32 output.
+ *   - Head dimension D must be 64.
+ *   - All device buffers are contiguous, row-major in the order written, and
+ *     16-byte aligned. The caller owns every buffer; the library allocates
+ *     nothing and keeps no state between calls.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
+ *     default stream). Calls are thread-safe; two calls that share a
+ *     workspace must be ordered (same stream).
+ *   - Return value: KVD_OK, or a negative status. Every status except
+ *     KVD_ERR_LAUNCH is decided on the host before any HIP call, so nothing is
+ *     enqueued when a call fails.
+ *   - Results are deterministic: split counts depend only on the shape and
+ *     every reduction runs in a fixed order.
+ */
+#ifndef KVDECODE_H
+#define KVDECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum kvd_dtype { KVD_F32 = 0, KVD_F16 = 1, KVD_BF16 = 2 };
+
+enum kvd_status {
+  KVD_OK = 0,
+  KVD_ERR_NULL = -1,       /* a required pointer is NULL */
+  KVD_ERR_SHAPE = -2,      /* a size is out of range or two sizes disagree */
+  KVD_ERR_DTYPE = -3,      /* unknown element type */
+  KVD_ERR_CAPACITY = -4,   /* rows beyond the cache capacity S_max */
+  KVD_ERR_ROWS = -5,       /* verify: logits rows R is neither N nor N + 1 */
+  KVD_ERR_WORKSPACE = -6,  /* workspace NULL or smaller than required */
+  KVD_ERR_ALIGN = -7,      /* a device pointer is not 16-byte aligned */
+  KVD_ERR_LAUNCH = -8      /* the HIP launch reported an error */
+};
+
+/* One layer's K/V cache ([N] per-layer key/value tensors).
+ * k, v: device, [B][H][S_max][D] elements of `dtype`. Rows [0, len) of every
+ * (b, h) are valid; the library never reads past the `len` it is given. */
+typedef struct kvd_cache {
+  void *k;
+  void *v;
+  int32_t B;      /* batch rows (beams count as rows); 1 for a shared cross cache */
+  int32_t H;      /* K/V heads */
+  int32_t S_max;  /* capacity in positions */
+  int32_t D;      /* head dimension (64) */
+  int32_t dtype;  /* enum kvd_dtype */
+} kvd_cache;
+
+/* kv_append - write T new K/V rows per (b, h) at positions [pos, pos + T).
+ * [W] save_to_cache (self attention: concatenation along the sequence;
+ * cross attention: the encoder-derived K/V written once, here T = frames at
+ * pos = 0); [N] workflow steps 2-3 and the prefill phase (T = prompt length).
+ *   k_new, v_new: device, [B][H][T][D] in cache->dtype.
+ *   rope_base > 0: each key row is first rotated at its absolute position
+ *     pos + t (pairs (i, i + D/2) turn by (pos + t) * rope_base^(-2i/D)),
+ *     computed in fp32 and rounded to nearest-even into the cache; values
+ *     are copied as they are. rope_base == 0: a bit-exact copy of both.
+ * Errors: KVD_ERR_NULL, KVD_ERR_SHAPE (T < 1, pos < 0, D != 64, B/H < 1),
+ *   KVD_ERR_DTYPE, KVD_ERR_CAPACITY (pos + T > S_max), KVD_ERR_ALIGN. */
+int kv_append(const kvd_cache *cache, const void *k_new, const void *v_new,
+              int32_t pos, int32_t T, float rope_base, void *stream);
+
+/* kv_reorder - beam reorder in place: rows [0, len) of beam b, K and V of
+ * every head, become the rows beam parent[b] held before the call.
+ * [W] beam search update, step 4 (rearrange_kv_cache).
+ *   parent: device int32[cache->B]; repeats allowed (several beams may take
+ *     the same parent); parent[b] == b leaves beam b untouched.
+ *   dev_status: device int32 or NULL. A parent outside [0, B) leaves that
+ *     beam unchanged and stores KVD_ERR_SHAPE there (never faults).
+ * Errors: KVD_ERR_NULL, KVD_ERR_SHAPE (len < 0, B > 16, D != 64),
+ *   KVD_ERR_DTYPE, KVD_ERR_CAPACITY (len > S_max), KVD_ERR_ALIGN. */
+int kv_reorder(const kvd_cache *cache, const int32_t *parent, int32_t len,
+               int32_t *dev_status, void *stream);
+
+/* decode_attn_self - attention of N new queries over a self-attention cache
+ * that already holds them ([W]: attention sees the whole concatenated
+ * sequence; [N] workflow step 4; [S]: the N drafts scored in one pass).
+ *   q: device, [B][Hq][N][D] in cache->dtype, B = cache->B. Query i sits at
+ *     position len - N + i and sees keys 0 .. len - N + i (causal among the
+ *     N new rows). Query head h reads K/V head h / (Hq / cache->H).
+ *   len: valid cache rows after the append, N <= len <= S_max.
+ *   scale: multiplies q.k (1/sqrt(D) for the usual attention).
+ *   rope_base > 0: query i is rotated at position len - N + i first (same
+ *     rotation as kv_append); 0: no rotation.
+ *   out: device fp32 [B][Hq][N][D] = softmax(scale q K^T) V.
+ *   ws: device workspace of ws_bytes >= kvd_attn_workspace_bytes(B, Hq, N,
+ *     len); it must be zero-filled before its first use and is left that way.
+ * Errors: KVD_ERR_NULL, KVD_ERR_SHAPE (N < 1, Hq % H != 0, D != 64),
+ *   KVD_ERR_DTYPE, KVD_ERR_CAPACITY (len > S_max or len < N),
+ *   KVD_ERR_WORKSPACE, KVD_ERR_ALIGN. */
+int decode_attn_self(const void *q, int32_t Hq, int32_t N, const kvd_cache *cache,
+                     int32_t len, float scale, float rope_base, float *out,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/* decode_attn_cross - attention of N queries per row over all `frames`
+ * rows of a cross-attention cache, with no mask ([W]: cross-attention K/V
+ * computed once from the encoder and reused every step).
+ *   q: device, [B][Hq][N][D] in xcache->dtype.
+ *   xcache->B == 1: one cache shared by all B rows (beams of one audio);
+ *     xcache->B == B: one cache per row.
+ *   frames: 1 <= frames <= xcache->S_max.
+ *   out: device fp32 [B][Hq][N][D]; ws as for decode_attn_self
+ *     (kvd_attn_workspace_bytes(B, Hq, N, frames)).
+ * Errors: as decode_attn_self; KVD_ERR_SHAPE also when xcache->B is
+ *   neither 1 nor B. */
+int decode_attn_cross(const void *q, int32_t B, int32_t Hq, int32_t N,
+                      const kvd_cache *xcache, int32_t frames, float scale,
+                      float *out, void *ws, size_t ws_bytes, void *stream);
+
+/* verify_accept - speculative verification epilogue ([S]; [W] greedy
+ * argmax). For each batch row b:
+ *   argmax[r] = lowest index of the largest logit of row r (-inf is an
+ *     ordinary value; a row of only -inf gives 0; NaN is outside the
+ *     contract),
+ *   accept_len[b] = n = first i < N with draft[b][i] != argmax[i], else N,
+ *   next_token[b] = argmax[n] if n < R, else -1 (all N drafts kept and no
+ *     bonus row).
+ *   logits: device, [B][R][V] of logits_dtype; R = N (row i scores draft i)
+ *     or N + 1 (a bonus row after the last draft).
+ *   draft: device int32 [B][N] (any value; one outside [0, V) never matches).
+ *   argmax_out: device int32 [B][R] or NULL.
+ *   accept_len, next_token: device int32 [B].
+ *   ws: device workspace, ws_bytes >= kvd_verify_workspace_bytes(B, R, V),
+ *     zero-filled before its first use and left that way.
+ * Errors: KVD_ERR_NULL, KVD_ERR_SHAPE (B, N, V < 1), KVD_ERR_ROWS,
+ *   KVD_ERR_DTYPE, KVD_ERR_WORKSPACE, KVD_ERR_ALIGN (logits only). */
+int verify_accept(const void *logits, int32_t logits_dtype, int32_t B, int32_t R,
+                  int32_t V, const int32_t *draft, int32_t N, int32_t *argmax_out,
+                  int32_t *accept_len, int32_t *next_token, void *ws,
+                  size_t ws_bytes, void *stream);
+
+/* Workspace sizes (bytes) for the calls above; 0 for invalid sizes. A
+ * workspace sized for the largest len (or frames) serves every smaller one. */
+size_t kvd_attn_workspace_bytes(int32_t B, int32_t Hq, int32_t N, int32_t len_max);
+size_t kvd_verify_workspace_bytes(int32_t B, int32_t R, int32_t V);
+
+/* Static text for a status code (never NULL). */
+const char *kvd_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVDECODE_H */

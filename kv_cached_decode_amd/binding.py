@@ -1,0 +1,251 @@
+"""Thin ctypes binding over libkvdecode.so (the C ABI in include/kvdecode.h).
+
+Argument marshalling only: every function checks that the torch tensors it is
+given are on the ROCm device, contiguous and of the expected dtype, then
+passes their data pointers, the sizes and torch's current HIP stream to the C
+entry point of the same name. Nothing here computes any step of the path, and
+there is no fallback: when the library is missing every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from ctypes import c_float, c_int, c_int32, c_size_t, c_void_p
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvdecode.so")
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "kvdecode.h")
+
+F32, F16, BF16 = 0, 1, 2
+DTYPE_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+CODE_DTYPE = {v: k for k, v in DTYPE_CODE.items()}
+HEAD_DIM = 64
+
+
+class KvdCache(ctypes.Structure):
+    _fields_ = [("k", c_void_p), ("v", c_void_p), ("B", c_int32), ("H", c_int32),
+                ("S_max", c_int32), ("D", c_int32), ("dtype", c_int32)]
+
+
+class KVDError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: status {status} ({status_string(status)})")
+        self.status = status
+
+
+_lib = None
+
+_SIGNATURES = {
+    "kv_append": (c_int, [ctypes.POINTER(KvdCache), c_void_p, c_void_p, c_int32, c_int32,
+                          c_float, c_void_p]),
+    "kv_reorder": (c_int, [ctypes.POINTER(KvdCache), c_void_p, c_int32, c_void_p, c_void_p]),
+    "decode_attn_self": (c_int, [c_void_p, c_int32, c_int32, ctypes.POINTER(KvdCache), c_int32,
+                                 c_float, c_float, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "decode_attn_cross": (c_int, [c_void_p, c_int32, c_int32, c_int32, ctypes.POINTER(KvdCache),
+                                  c_int32, c_float, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "verify_accept": (c_int, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_int32,
+                              c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "kvd_attn_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32]),
+    "kvd_verify_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
+    "kvd_status_string": (ctypes.c_char_p, [c_int]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Open libkvdecode.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m kv_cached_decode_amd.build` (no fallback exists)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def declared_functions() -> list[str]:
+    """Names of the functions include/kvdecode.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+
+
+def status_string(status: int) -> str:
+    return lib().kvd_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise KVDError(fn, status)
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the ROCm device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+class Cache:
+    """One layer's K/V cache preallocated to capacity: k, v [B, H, S_max, D]."""
+
+    def __init__(self, B: int, H: int, S_max: int, dtype=torch.float16, device="cuda",
+                 D: int = HEAD_DIM):
+        self.k = torch.zeros((B, H, S_max, D), dtype=dtype, device=device)
+        self.v = torch.zeros((B, H, S_max, D), dtype=dtype, device=device)
+        self._desc = None
+
+    @classmethod
+    def wrap(cls, k: torch.Tensor, v: torch.Tensor) -> "Cache":
+        c = cls.__new__(cls)
+        c.k, c.v, c._desc = k, v, None
+        return c
+
+    @property
+    def B(self):
+        return self.k.shape[0]
+
+    @property
+    def H(self):
+        return self.k.shape[1]
+
+    @property
+    def S_max(self):
+        return self.k.shape[2]
+
+    @property
+    def dtype(self):
+        return self.k.dtype
+
+    def desc(self) -> KvdCache:
+        if self._desc is None:
+            if self.k.dim() != 4 or self.k.shape != self.v.shape or self.k.dtype != self.v.dtype:
+                raise ValueError("k and v must be [B, H, S_max, D] tensors of one dtype")
+            if self.k.dtype not in DTYPE_CODE:
+                raise ValueError(f"unsupported cache dtype {self.k.dtype}")
+            B, H, S, D = self.k.shape
+            self._desc = KvdCache(_dev(self.k, "cache.k"), _dev(self.v, "cache.v"),
+                                  B, H, S, D, DTYPE_CODE[self.k.dtype])
+        return self._desc
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A zero-filled device workspace (the counters at its start must be zero
+    before first use; the kernels leave them that way)."""
+    return torch.zeros(max(int(nbytes), 16384), dtype=torch.uint8, device=device)
+
+
+def attn_workspace_bytes(B: int, Hq: int, N: int, len_max: int) -> int:
+    return int(lib().kvd_attn_workspace_bytes(B, Hq, N, len_max))
+
+
+def verify_workspace_bytes(B: int, R: int, V: int) -> int:
+    return int(lib().kvd_verify_workspace_bytes(B, R, V))
+
+
+def kv_append(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor, pos: int,
+              rope_base: float = 0.0):
+    d = cache.desc()
+    if k_new.dim() != 4 or k_new.shape != v_new.shape:
+        raise ValueError("k_new and v_new must be [B, H, T, D] of one shape")
+    T = k_new.shape[2]
+    if (k_new.shape[0], k_new.shape[1], k_new.shape[3]) != (d.B, d.H, d.D):
+        raise ValueError(f"k_new shape {tuple(k_new.shape)} does not match the cache")
+    _check("kv_append", lib().kv_append(
+        ctypes.byref(d), _dev(k_new, "k_new", cache.dtype), _dev(v_new, "v_new", cache.dtype),
+        pos, T, rope_base, _stream()))
+
+
+def kv_reorder(cache: Cache, parent: torch.Tensor, length: int,
+               dev_status: torch.Tensor | None = None):
+    d = cache.desc()
+    if parent.numel() != d.B:
+        raise ValueError("parent must hold one index per beam")
+    st = _dev(dev_status, "dev_status", torch.int32) if dev_status is not None else None
+    _check("kv_reorder", lib().kv_reorder(ctypes.byref(d), _dev(parent, "parent", torch.int32),
+                                          length, st, _stream()))
+
+
+def _attn_out(q: torch.Tensor, out):
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    return out
+
+
+def decode_attn_self(q: torch.Tensor, cache: Cache, length: int, scale: float,
+                     rope_base: float = 0.0, out: torch.Tensor | None = None,
+                     ws: torch.Tensor | None = None) -> torch.Tensor:
+    d = cache.desc()
+    if q.dim() != 4 or q.shape[0] != d.B or q.shape[3] != d.D:
+        raise ValueError(f"q must be [B={d.B}, Hq, N, {d.D}], got {tuple(q.shape)}")
+    Hq, N = q.shape[1], q.shape[2]
+    out = _attn_out(q, out)
+    if ws is None:
+        ws = workspace(attn_workspace_bytes(d.B, Hq, N, length), q.device)
+    _check("decode_attn_self", lib().decode_attn_self(
+        _dev(q, "q", cache.dtype), Hq, N, ctypes.byref(d), length, scale, rope_base,
+        _dev(out, "out", torch.float32), _dev(ws, "ws"), ws.numel() * ws.element_size(),
+        _stream()))
+    return out
+
+
+def decode_attn_cross(q: torch.Tensor, xcache: Cache, frames: int, scale: float,
+                      out: torch.Tensor | None = None,
+                      ws: torch.Tensor | None = None) -> torch.Tensor:
+    d = xcache.desc()
+    if q.dim() != 4 or q.shape[3] != d.D:
+        raise ValueError(f"q must be [B, Hq, N, {d.D}], got {tuple(q.shape)}")
+    B, Hq, N = q.shape[0], q.shape[1], q.shape[2]
+    out = _attn_out(q, out)
+    if ws is None:
+        ws = workspace(attn_workspace_bytes(B, Hq, N, frames), q.device)
+    _check("decode_attn_cross", lib().decode_attn_cross(
+        _dev(q, "q", xcache.dtype), B, Hq, N, ctypes.byref(d), frames, scale,
+        _dev(out, "out", torch.float32), _dev(ws, "ws"), ws.numel() * ws.element_size(),
+        _stream()))
+    return out
+
+
+def verify_accept(logits: torch.Tensor, draft: torch.Tensor,
+                  argmax_out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                  accept_len: torch.Tensor | None = None,
+                  next_token: torch.Tensor | None = None):
+    """Returns (accept_len int32[B], next_token int32[B], argmax int32[B, R] or None)."""
+    if logits.dim() != 3 or draft.dim() != 2 or draft.shape[0] != logits.shape[0]:
+        raise ValueError("logits must be [B, R, V] and draft [B, N]")
+    if logits.dtype not in DTYPE_CODE:
+        raise ValueError(f"unsupported logits dtype {logits.dtype}")
+    B, R, V = logits.shape
+    N = draft.shape[1]
+    dev = logits.device
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if next_token is None:
+        next_token = torch.empty(B, dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = workspace(verify_workspace_bytes(B, R, V), dev)
+    am = _dev(argmax_out, "argmax_out", torch.int32) if argmax_out is not None else None
+    _check("verify_accept", lib().verify_accept(
+        _dev(logits, "logits"), DTYPE_CODE[logits.dtype], B, R, V,
+        _dev(draft, "draft", torch.int32), N, am, _dev(accept_len, "accept_len", torch.int32),
+        _dev(next_token, "next_token", torch.int32), _dev(ws, "ws"),
+        ws.numel() * ws.element_size(), _stream()))
+    return accept_len, next_token, argmax_out

@@ -1,0 +1,60 @@
+"""Build the C-ABI library libkvdecode.so in-tree with hipcc for gfx950.
+
+    python -m kv_cached_decode_amd.build
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libkvdecode.so")
+SOURCES = ["kvd_kernels.hip", "kvd_api.cpp"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the HIP toolchain is required to build libkvdecode.so")
+
+
+def compile_flags() -> list[str]:
+    return [
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+        # packed fp32 VALU forms stay off: hipcc -O3 would otherwise form them
+        # from plain float code
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wall", "-Wno-unused-function",
+        f"-I{INCLUDE}", f"-I{CSRC}",
+    ]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libkvdecode.so; returns its path."""
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *compile_flags(), "-shared", "-o", tmp,
+           *[os.path.join(CSRC, s) for s in SOURCES]]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed with status {res.returncode}")
+    if verbose and res.stderr.strip():
+        # the host pass does not know the packed-fp32 feature and says so
+        msgs = [ln for ln in res.stderr.splitlines() if "packed-fp32-ops" not in ln]
+        if msgs:
+            sys.stderr.write("\n".join(msgs) + "\n")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,261 @@
+// C-ABI entry points: argument validation (all of it before any HIP call),
+// launch planning, and status codes. The operations are defined in
+// include/kvdecode.h.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "kvd_internal.hpp"
+#include "kvdecode.h"
+
+using kvd::AttnArgs;
+using kvd::AttnPlan;
+
+namespace {
+
+bool dtype_ok(int dt) { return dt == KVD_F32 || dt == KVD_F16 || dt == KVD_BF16; }
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Shared checks of a cache descriptor.
+int check_cache(const kvd_cache *c) {
+  if (!c) return KVD_ERR_NULL;
+  if (!c->k || !c->v) return KVD_ERR_NULL;
+  if (!dtype_ok(c->dtype)) return KVD_ERR_DTYPE;
+  if (c->B < 1 || c->H < 1 || c->S_max < 1 || c->D != kvd::kHeadDim) return KVD_ERR_SHAPE;
+  if (!aligned16(c->k) || !aligned16(c->v)) return KVD_ERR_ALIGN;
+  return KVD_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? KVD_OK : KVD_ERR_LAUNCH; }
+
+// Every workspace starts with a fixed block of arrival counters, zero at rest
+// (each kernel that counts arrivals sets its counters back to zero), so one
+// workspace can serve calls with different plans: partial results of one call
+// never land where another call keeps a counter.
+constexpr size_t kCounterBytes = kvd::kMaxCounters * sizeof(uint32_t);
+
+size_t attn_bytes(const AttnPlan &p) { return kCounterBytes + p.part_floats * sizeof(float); }
+
+// Fill the plan-dependent fields and the workspace pointers.
+int prepare_attn(AttnArgs &a, int dtype, void *ws, size_t ws_bytes) {
+  const int units = a.Bkv * a.Hkv;
+  const AttnPlan p = kvd::plan_attn(dtype, units, a.G, a.L);
+  if (p.row_tiles > 65535 || units > 65535) return KVD_ERR_SHAPE;  // grid limits
+  a.chunk = p.chunk;
+  a.splits = p.splits;
+  a.row_tiles = p.row_tiles;
+  a.waves = p.waves;
+  a.gm = p.gm;
+  if (p.splits > 1) {
+    const size_t need = attn_bytes(p);
+    if (!ws) return KVD_ERR_WORKSPACE;
+    if (ws_bytes < need) return KVD_ERR_WORKSPACE;
+    if (!aligned16(ws)) return KVD_ERR_ALIGN;
+    a.ws_count = static_cast<uint32_t *>(ws);
+    a.ws_part = reinterpret_cast<float *>(static_cast<char *>(ws) + kCounterBytes);
+  } else {
+    a.ws_count = nullptr;
+    a.ws_part = nullptr;
+  }
+  return KVD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kvd_status_string(int status) {
+  switch (status) {
+    case KVD_OK: return "ok";
+    case KVD_ERR_NULL: return "a required pointer is NULL";
+    case KVD_ERR_SHAPE: return "a size is out of range or two sizes disagree";
+    case KVD_ERR_DTYPE: return "unknown element type";
+    case KVD_ERR_CAPACITY: return "rows beyond the cache capacity";
+    case KVD_ERR_ROWS: return "logits rows must be N or N + 1";
+    case KVD_ERR_WORKSPACE: return "workspace missing or too small";
+    case KVD_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case KVD_ERR_LAUNCH: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int kv_append(const kvd_cache *cache, const void *k_new, const void *v_new, int32_t pos,
+              int32_t T, float rope_base, void *stream) {
+  int st = check_cache(cache);
+  if (st) return st;
+  if (!k_new || !v_new) return KVD_ERR_NULL;
+  if (T < 1 || pos < 0 || !(rope_base >= 0.f) || isinf(rope_base)) return KVD_ERR_SHAPE;
+  if ((int64_t)pos + T > cache->S_max) return KVD_ERR_CAPACITY;
+  if (!aligned16(k_new) || !aligned16(v_new)) return KVD_ERR_ALIGN;
+  kvd::AppendArgs a;
+  a.k_cache = cache->k;
+  a.v_cache = cache->v;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.B = cache->B;
+  a.H = cache->H;
+  a.S_max = cache->S_max;
+  a.T = T;
+  a.pos = pos;
+  a.rope_base = rope_base;
+  return status_of(kvd::launch_append(cache->dtype, a, static_cast<hipStream_t>(stream)));
+}
+
+int kv_reorder(const kvd_cache *cache, const int32_t *parent, int32_t len, int32_t *dev_status,
+               void *stream) {
+  int st = check_cache(cache);
+  if (st) return st;
+  if (!parent) return KVD_ERR_NULL;
+  if (len < 0 || cache->B > 16) return KVD_ERR_SHAPE;
+  if (len > cache->S_max) return KVD_ERR_CAPACITY;
+  if (!aligned4(parent) || (dev_status && !aligned4(dev_status))) return KVD_ERR_ALIGN;
+  kvd::ReorderArgs a;
+  a.k_cache = cache->k;
+  a.v_cache = cache->v;
+  a.parent = parent;
+  a.dev_status = dev_status;
+  a.B = cache->B;
+  a.H = cache->H;
+  a.S_max = cache->S_max;
+  a.len = len;
+  return status_of(kvd::launch_reorder(cache->dtype, a, static_cast<hipStream_t>(stream)));
+}
+
+int decode_attn_self(const void *q, int32_t Hq, int32_t N, const kvd_cache *cache, int32_t len,
+                     float scale, float rope_base, float *out, void *ws, size_t ws_bytes,
+                     void *stream) {
+  int st = check_cache(cache);
+  if (st) return st;
+  if (!q || !out) return KVD_ERR_NULL;
+  if (N < 1 || Hq < 1 || Hq % cache->H != 0 || !isfinite(scale) || !(rope_base >= 0.f) ||
+      isinf(rope_base))
+    return KVD_ERR_SHAPE;
+  if (len > cache->S_max || len < N) return KVD_ERR_CAPACITY;
+  if (!aligned16(q) || !aligned16(out)) return KVD_ERR_ALIGN;
+  AttnArgs a{};
+  a.q = q;
+  a.k = cache->k;
+  a.v = cache->v;
+  a.out = out;
+  a.B = cache->B;
+  a.Hq = Hq;
+  a.N = N;
+  a.Bkv = cache->B;
+  a.Hkv = cache->H;
+  a.group = Hq / cache->H;
+  a.S_max = cache->S_max;
+  a.G = a.group * N;
+  a.L = len;
+  a.causal_base = len - N;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.rope_base = rope_base;
+  st = prepare_attn(a, cache->dtype, ws, ws_bytes);
+  if (st) return st;
+  return status_of(kvd::launch_attn(cache->dtype, a, static_cast<hipStream_t>(stream)));
+}
+
+int decode_attn_cross(const void *q, int32_t B, int32_t Hq, int32_t N, const kvd_cache *xcache,
+                      int32_t frames, float scale, float *out, void *ws, size_t ws_bytes,
+                      void *stream) {
+  int st = check_cache(xcache);
+  if (st) return st;
+  if (!q || !out) return KVD_ERR_NULL;
+  if (B < 1 || N < 1 || Hq < 1 || Hq % xcache->H != 0 || !isfinite(scale) || frames < 1 ||
+      (xcache->B != 1 && xcache->B != B))
+    return KVD_ERR_SHAPE;
+  if (frames > xcache->S_max) return KVD_ERR_CAPACITY;
+  if (!aligned16(q) || !aligned16(out)) return KVD_ERR_ALIGN;
+  AttnArgs a{};
+  a.q = q;
+  a.k = xcache->k;
+  a.v = xcache->v;
+  a.out = out;
+  a.B = B;
+  a.Hq = Hq;
+  a.N = N;
+  a.Bkv = xcache->B;
+  a.Hkv = xcache->H;
+  a.group = Hq / xcache->H;
+  a.S_max = xcache->S_max;
+  a.G = (xcache->B == 1 ? B : 1) * a.group * N;
+  a.L = frames;
+  a.causal_base = -1;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.rope_base = 0.f;
+  st = prepare_attn(a, xcache->dtype, ws, ws_bytes);
+  if (st) return st;
+  return status_of(kvd::launch_attn(xcache->dtype, a, static_cast<hipStream_t>(stream)));
+}
+
+size_t kvd_attn_workspace_bytes(int32_t B, int32_t Hq, int32_t N, int32_t len_max) {
+  if (B < 1 || Hq < 1 || N < 1 || len_max < 1) return 0;
+  // The largest plan over every grouping the calls can use (Hkv divides Hq,
+  // cache per row or shared), every dtype and every length up to len_max.
+  size_t best = 0;
+  for (int hkv = 1; hkv <= Hq; ++hkv) {
+    if (Hq % hkv) continue;
+    const int group = Hq / hkv;
+    for (int shared = 0; shared < 2; ++shared) {
+      if (shared && B == 1) continue;
+      const int units = shared ? hkv : B * hkv;
+      const int G = (shared ? B : 1) * group * N;
+      for (int dt = 0; dt < 2; ++dt) {
+        for (int L = 1; L <= len_max; ++L) {
+          const AttnPlan p = kvd::plan_attn(dt == 0 ? kvd::F32 : kvd::F16, units, G, L);
+          if (p.splits > 1) {
+            const size_t b = attn_bytes(p);
+            if (b > best) best = b;
+          }
+        }
+      }
+    }
+  }
+  return best;
+}
+
+int verify_accept(const void *logits, int32_t logits_dtype, int32_t B, int32_t R, int32_t V,
+                  const int32_t *draft, int32_t N, int32_t *argmax_out, int32_t *accept_len,
+                  int32_t *next_token, void *ws, size_t ws_bytes, void *stream) {
+  if (!logits || !draft || !accept_len || !next_token) return KVD_ERR_NULL;
+  if (!dtype_ok(logits_dtype)) return KVD_ERR_DTYPE;
+  if (B < 1 || N < 1 || V < 1 || N > 63 || B > kvd::kMaxCounters) return KVD_ERR_SHAPE;
+  if (R != N && R != N + 1) return KVD_ERR_ROWS;
+  if (!aligned16(logits)) return KVD_ERR_ALIGN;
+  if (!aligned4(draft) || !aligned4(accept_len) || !aligned4(next_token) ||
+      (argmax_out && !aligned4(argmax_out)))
+    return KVD_ERR_ALIGN;
+  const size_t need = kvd_verify_workspace_bytes(B, R, V);
+  if (!ws || ws_bytes < need) return KVD_ERR_WORKSPACE;
+  if (!aligned16(ws)) return KVD_ERR_ALIGN;
+  kvd::VerifyArgs a;
+  a.logits = logits;
+  a.dtype = logits_dtype;
+  a.draft = draft;
+  a.argmax_out = argmax_out;
+  a.accept_len = accept_len;
+  a.next_token = next_token;
+  a.B = B;
+  a.R = R;
+  a.V = V;
+  a.N = N;
+  kvd::plan_verify(B, R, V, a.chunk, a.chunks);
+  const size_t slots = (size_t)B * R * a.chunks;
+  const size_t val_bytes = ((slots * sizeof(float) + 255) / 256) * 256;
+  a.ws_count = static_cast<uint32_t *>(ws);
+  a.ws_val = reinterpret_cast<float *>(static_cast<char *>(ws) + kCounterBytes);
+  a.ws_idx = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + kCounterBytes + val_bytes);
+  return status_of(kvd::launch_verify(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t kvd_verify_workspace_bytes(int32_t B, int32_t R, int32_t V) {
+  if (B < 1 || R < 1 || V < 1) return 0;
+  int chunk = 0, chunks = 0;
+  kvd::plan_verify(B, R, V, chunk, chunks);
+  const size_t slots = (size_t)B * R * chunks;
+  return kCounterBytes + ((slots * sizeof(float) + 255) / 256) * 256 + slots * sizeof(int32_t);
+}
+
+}  // extern "C"

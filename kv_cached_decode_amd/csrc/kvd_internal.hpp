@@ -1,0 +1,83 @@
+// Internal interface between the C-ABI entry points (validation, planning)
+// and the kernel launchers. Nothing here is exported.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvd {
+
+enum DType { F32 = 0, F16 = 1, BF16 = 2 };  // same values as enum kvd_dtype
+
+constexpr int kHeadDim = 64;
+
+// Arrival counters at the start of every workspace (one per merged tile).
+constexpr int kMaxCounters = 4096;
+
+struct AppendArgs {
+  void *k_cache, *v_cache;       // [B][H][S_max][D]
+  const void *k_new, *v_new;     // [B][H][T][D]
+  int B, H, S_max, T, pos;
+  float rope_base;               // > 0: rotate keys at pos + t
+};
+
+struct ReorderArgs {
+  void *k_cache, *v_cache;       // [B][H][S_max][D]
+  const int32_t *parent;         // [B]
+  int32_t *dev_status;           // nullable
+  int B, H, S_max, len;
+};
+
+// One attention launch. A "unit" is one (cache row, kv head) pair; its query
+// rows are every (b, h, i) that reads it, numbered g = (bl * group + j) * N + i
+// with bl the batch row within the unit (0 unless the cache is shared),
+// j the head within the group and i the query.
+struct AttnArgs {
+  const void *q;                 // [B][Hq][N][D]
+  const void *k, *v;             // [Bkv][Hkv][S_max][D]
+  float *out;                    // [B][Hq][N][D]
+  float *ws_part;                // partial (m, l, o) per split
+  uint32_t *ws_count;            // arrival counters, one per (unit, row tile)
+  int B, Hq, N, Bkv, Hkv, group, S_max;
+  int G;                         // query rows per unit
+  int L;                         // keys: len (self) or frames (cross)
+  int causal_base;               // self: len - N; cross: -1 (no mask)
+  float scale_log2;              // scale * log2(e)
+  float rope_base;               // > 0: rotate q at causal_base + i
+  // plan
+  int chunk;                     // keys per workgroup
+  int splits;                    // workgroups per (unit, row tile)
+  int row_tiles;                 // ceil(G / rows per tile)
+  int waves;                     // waves per workgroup
+  int gm;                        // rows per tile (template bucket)
+};
+
+struct VerifyArgs {
+  const void *logits;            // [B][R][V]
+  int dtype;
+  const int32_t *draft;          // [B][N]
+  int32_t *argmax_out;           // [B][R] or null
+  int32_t *accept_len, *next_token;
+  float *ws_val;                 // [B][R][chunks]
+  int32_t *ws_idx;               // [B][R][chunks]
+  uint32_t *ws_count;            // [B]
+  int B, R, V, N;
+  int chunk, chunks;
+};
+
+// Attention planning shared by the entry points and the workspace-size query.
+struct AttnPlan {
+  int gm, row_tiles, chunk, splits, waves;
+  size_t part_floats, counters;
+};
+AttnPlan plan_attn(int dtype, int units, int G, int L);
+
+void plan_verify(int B, int R, int V, int &chunk, int &chunks);
+
+hipError_t launch_append(int dtype, const AppendArgs &a, hipStream_t s);
+hipError_t launch_reorder(int dtype, const ReorderArgs &a, hipStream_t s);
+hipError_t launch_attn(int dtype, const AttnArgs &a, hipStream_t s);
+hipError_t launch_verify(const VerifyArgs &a, hipStream_t s);
+
+}  // namespace kvd

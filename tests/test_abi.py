@@ -1,0 +1,113 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+the header declares, sizes workspaces, and rejects bad arguments on the host
+before any HIP call (each call below fails validation, so nothing launches)."""
+import ctypes
+
+import pytest
+
+from kv_cached_decode_amd import binding as kb
+
+FAKE = 0x10000        # 16-byte aligned non-null stand-in; never dereferenced
+MIS = 0x10008         # misaligned stand-in
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return kb.lib()
+
+
+def test_header_declares_the_five_calls_and_helpers():
+    names = kb.declared_functions()
+    for n in ("kv_append", "kv_reorder", "decode_attn_self", "decode_attn_cross",
+              "verify_accept", "kvd_attn_workspace_bytes", "kvd_verify_workspace_bytes",
+              "kvd_status_string"):
+        assert n in names
+    assert len(names) == len(set(names))
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in kb.declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(-8, 1):
+        s = kb.status_string(code)
+        assert s and s != "unknown status"
+    assert kb.status_string(-99) == "unknown status"
+
+
+def _cache(B=1, H=20, S=448, D=64, dtype=kb.F16, k=FAKE, v=FAKE):
+    return kb.KvdCache(k, v, B, H, S, D, dtype)
+
+
+def test_kv_append_validation(lib):
+    c = _cache()
+    f = lib.kv_append
+    assert f(None, FAKE, FAKE, 0, 1, 0.0, None) == -1
+    assert f(ctypes.byref(_cache(k=None)), FAKE, FAKE, 0, 1, 0.0, None) == -1
+    assert f(ctypes.byref(c), None, FAKE, 0, 1, 0.0, None) == -1
+    assert f(ctypes.byref(_cache(dtype=7)), FAKE, FAKE, 0, 1, 0.0, None) == -3
+    assert f(ctypes.byref(_cache(D=128)), FAKE, FAKE, 0, 1, 0.0, None) == -2
+    assert f(ctypes.byref(c), FAKE, FAKE, 0, 0, 0.0, None) == -2          # T < 1
+    assert f(ctypes.byref(c), FAKE, FAKE, -1, 1, 0.0, None) == -2         # pos < 0
+    assert f(ctypes.byref(c), FAKE, FAKE, 0, 1, -1.0, None) == -2         # rope base < 0
+    assert f(ctypes.byref(c), FAKE, FAKE, 448, 1, 0.0, None) == -4        # capacity
+    assert f(ctypes.byref(c), FAKE, FAKE, 440, 9, 0.0, None) == -4
+    assert f(ctypes.byref(c), MIS, FAKE, 0, 1, 0.0, None) == -7
+    assert f(ctypes.byref(_cache(k=MIS)), FAKE, FAKE, 0, 1, 0.0, None) == -7
+
+
+def test_kv_reorder_validation(lib):
+    f = lib.kv_reorder
+    assert f(ctypes.byref(_cache(B=5)), None, 10, None, None) == -1
+    assert f(ctypes.byref(_cache(B=17)), FAKE, 10, None, None) == -2      # too many beams
+    assert f(ctypes.byref(_cache(B=5)), FAKE, -1, None, None) == -2
+    assert f(ctypes.byref(_cache(B=5)), FAKE, 449, None, None) == -4
+    assert f(ctypes.byref(_cache(B=5)), FAKE + 2, 10, None, None) == -7
+
+
+def test_decode_attn_validation(lib):
+    c = _cache()
+    ws = FAKE
+    s = lib.decode_attn_self
+    assert s(None, 20, 1, ctypes.byref(c), 10, 0.125, 0.0, FAKE, ws, 1 << 30, None) == -1
+    assert s(FAKE, 20, 1, ctypes.byref(c), 10, 0.125, 0.0, None, ws, 1 << 30, None) == -1
+    assert s(FAKE, 20, 0, ctypes.byref(c), 10, 0.125, 0.0, FAKE, ws, 1 << 30, None) == -2
+    assert s(FAKE, 30, 1, ctypes.byref(c), 10, 0.125, 0.0, FAKE, ws, 1 << 30, None) == -2  # Hq % H
+    assert s(FAKE, 20, 1, ctypes.byref(c), 449, 0.125, 0.0, FAKE, ws, 1 << 30, None) == -4
+    assert s(FAKE, 20, 5, ctypes.byref(c), 4, 0.125, 0.0, FAKE, ws, 1 << 30, None) == -4   # len < N
+    assert s(FAKE, 20, 1, ctypes.byref(c), 10, float("nan"), 0.0, FAKE, ws, 1 << 30, None) == -2
+    assert s(MIS, 20, 1, ctypes.byref(c), 10, 0.125, 0.0, FAKE, ws, 1 << 30, None) == -7
+    # a long cache needs split partials: no or too small a workspace is refused
+    assert s(FAKE, 20, 1, ctypes.byref(c), 448, 0.125, 0.0, FAKE, None, 0, None) == -6
+    assert s(FAKE, 20, 1, ctypes.byref(c), 448, 0.125, 0.0, FAKE, ws, 64, None) == -6
+    x = lib.decode_attn_cross
+    xc = _cache(B=1, S=1500)
+    assert x(FAKE, 5, 20, 1, ctypes.byref(xc), 1501, 0.125, FAKE, ws, 1 << 30, None) == -4
+    assert x(FAKE, 5, 20, 1, ctypes.byref(_cache(B=2, S=1500)), 1500, 0.125, FAKE, ws, 1 << 30, None) == -2
+    assert x(FAKE, 5, 20, 1, ctypes.byref(xc), 0, 0.125, FAKE, ws, 1 << 30, None) == -2
+    assert x(FAKE, 1, 20, 1, ctypes.byref(xc), 1500, 0.125, FAKE, None, 0, None) == -6
+
+
+def test_verify_accept_validation(lib):
+    f = lib.verify_accept
+    big = 1 << 30
+    assert f(None, 0, 1, 5, 51865, FAKE, 5, None, FAKE, FAKE, FAKE, big, None) == -1
+    assert f(FAKE, 0, 1, 5, 51865, None, 5, None, FAKE, FAKE, FAKE, big, None) == -1
+    assert f(FAKE, 9, 1, 5, 51865, FAKE, 5, None, FAKE, FAKE, FAKE, big, None) == -3
+    assert f(FAKE, 0, 1, 7, 51865, FAKE, 5, None, FAKE, FAKE, FAKE, big, None) == -5
+    assert f(FAKE, 0, 1, 4, 51865, FAKE, 5, None, FAKE, FAKE, FAKE, big, None) == -5
+    assert f(FAKE, 0, 1, 5, 0, FAKE, 5, None, FAKE, FAKE, FAKE, big, None) == -2
+    assert f(FAKE, 0, 1, 5, 51865, FAKE, 5, None, FAKE, FAKE, None, 0, None) == -6
+    assert f(FAKE, 0, 1, 5, 51865, FAKE, 5, None, FAKE, FAKE, FAKE, 100, None) == -6
+    assert f(MIS, 0, 1, 5, 51865, FAKE, 5, None, FAKE, FAKE, FAKE, big, None) == -7
+
+
+def test_workspace_sizes(lib):
+    # short caches need no split partials beyond the counter block
+    assert kb.attn_workspace_bytes(1, 20, 1, 448) > 16384
+    assert kb.attn_workspace_bytes(1, 20, 1, 1500) >= kb.attn_workspace_bytes(1, 20, 1, 448)
+    assert kb.attn_workspace_bytes(0, 20, 1, 448) == 0
+    assert kb.verify_workspace_bytes(1, 5, 51865) > 16384
+    assert kb.verify_workspace_bytes(1, 0, 10) == 0

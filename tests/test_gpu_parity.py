@@ -1,0 +1,402 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bit-exact: cache append (plain copy), beam reorder, argmax, accepted length and
+corrected token. Attention outputs: max |err| <= 1e-5 with fp32 storage and
+<= 2e-3 with fp16/bf16 storage (fp32 accumulation on the GPU, fp64 in the
+oracle, both reading the same stored bits). Rotary keys: within one bf16 ulp
+of the oracle's once-rounded fp64 value (the kernel rounds an fp32 rotation).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from kv_cached_decode_amd import binding as kb
+from kv_cached_decode_amd import inputs as I
+from _util import TOL, TORCH_DTYPE, bits, from_dev, max_err, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    kb.lib()
+
+
+def _ws(nbytes=64 << 20):
+    return kb.workspace(nbytes)
+
+
+# ------------------------------------------------------------ tiny step ----
+
+def test_tiny_step_fp32_against_recompute():
+    w = I.TINY
+    say("case: tiny fp32 step, self 32+1, cross 1500")
+    k_all, v_all = I.self_kv(w, 0)                     # [1, 6, 33, 64]
+    xk, xv = I.cross_kv(w, 0)
+    q = I.queries(w, 0, 32)
+    qx = I.queries(w, 0, 32, cross=True)
+    cache = kb.Cache(1, 6, 33, torch.float32)
+    xc = kb.Cache(1, 6, 1500, torch.float32)
+    kb.kv_append(cache, to_dev(k_all[:, :, :32], "f32"), to_dev(v_all[:, :, :32], "f32"), 0)
+    kb.kv_append(cache, to_dev(k_all[:, :, 32:], "f32"), to_dev(v_all[:, :, 32:], "f32"), 32)
+    kb.kv_append(xc, to_dev(xk, "f32"), to_dev(xv, "f32"), 0)
+    ws = _ws()
+    o_self = kb.decode_attn_self(to_dev(q, "f32"), cache, 33, w.attn_scale, ws=ws)
+    o_cross = kb.decode_attn_cross(to_dev(qx, "f32"), xc, 1500, w.attn_scale, ws=ws)
+    torch.cuda.synchronize()
+
+    oc = O.ConcatCache(1, 6, 64, "f32")
+    oc.append(k_all[:, :, :32], v_all[:, :, :32])
+    oc.append(k_all[:, :, 32:], v_all[:, :, 32:])
+    ox = O.ConcatCache(1, 6, 64, "f32")
+    ox.set_once(xk, xv)
+    assert np.array_equal(bits(from_dev(cache.k, "f32")), bits(oc.k))
+    assert np.array_equal(bits(from_dev(cache.v, "f32")), bits(oc.v))
+    assert np.array_equal(bits(from_dev(xc.k, "f32")), bits(xk))
+    ref_self = O.attend_self(q, oc, w.attn_scale)
+    # the last row of a full causal recomputation over all 33 tokens
+    full = O.full_causal_attention(np.concatenate([np.zeros((6, 32, 64)), O.widen(q, "f32")[0]], 1),
+                                   O.widen(k_all, "f32")[0], O.widen(v_all, "f32")[0],
+                                   w.attn_scale)[:, 32]
+    assert np.max(np.abs(ref_self[0, :, 0] - full)) < 1e-12
+    e_self = max_err(o_self, ref_self)
+    e_cross = max_err(o_cross, O.attend_cross(qx, ox, w.attn_scale))
+    say(f"tiny: self max|err| {e_self:.2e}, cross {e_cross:.2e}")
+    assert e_self <= TOL["f32"] and e_cross <= TOL["f32"]
+
+
+# ------------------------------------------------- whisper greedy shape ----
+
+@pytest.mark.parametrize("layer", [0, 31])
+def test_whisper_greedy_sweep_lengths(layer):
+    """Full large-v2 layer shape (20 heads, 1500 frames, self cache to 448):
+    tokens appended one per step, attention checked at sampled lengths that
+    include split boundaries."""
+    w = I.WHISPER_GREEDY
+    say(f"case: whisper greedy layer {layer}")
+    k_all, v_all = I.self_kv(w, layer)
+    xk, xv = I.cross_kv(w, layer)
+    cache = kb.Cache(1, 20, 448, torch.float16)
+    xc = kb.Cache(1, 20, 1500, torch.float16)
+    kb.kv_append(xc, to_dev(xk, "f16"), to_dev(xv, "f16"), 0)
+    ox = O.ConcatCache(1, 20, 64, "f16")
+    ox.set_once(xk, xv)
+    oc = O.ConcatCache(1, 20, 64, "f16")
+    kd, vd = to_dev(k_all, "f16"), to_dev(v_all, "f16")
+    ws = _ws()
+    check = {1, 2, 31, 32, 33, 127, 128, 129, 255, 256, 257, 384, 447, 448}
+    worst = 0.0
+    for L in range(1, 449):
+        kb.kv_append(cache, kd[:, :, L - 1:L].contiguous(), vd[:, :, L - 1:L].contiguous(), L - 1)
+        oc.append(k_all[:, :, L - 1:L], v_all[:, :, L - 1:L])
+        if L not in check:
+            continue
+        q = I.queries(w, layer, L)
+        qx = I.queries(w, layer, L, cross=True)
+        o_self = kb.decode_attn_self(to_dev(q, "f16"), cache, L, w.attn_scale, ws=ws)
+        o_cross = kb.decode_attn_cross(to_dev(qx, "f16"), xc, 1500, w.attn_scale, ws=ws)
+        e1 = max_err(o_self, O.attend_self(q, oc, w.attn_scale))
+        e2 = max_err(o_cross, O.attend_cross(qx, ox, w.attn_scale))
+        worst = max(worst, e1, e2)
+        assert e1 <= TOL["f16"] and e2 <= TOL["f16"], (L, e1, e2)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(from_dev(cache.k, "f16")), bits(oc.k))
+    assert np.array_equal(bits(from_dev(cache.v, "f16")), bits(oc.v))
+    say(f"whisper layer {layer}: worst max|err| {worst:.2e}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("N", [1, 5])
+@pytest.mark.parametrize("L", [5, 64, 129, 130, 133, 257, 448])
+def test_sentinel_mask(dtype, N, L):
+    """Query i's own key and the next key (one it must not see) both align
+    with it; one-hot values name every key that got weight."""
+    if L < N:
+        pytest.skip("len < N")
+    say(f"case: sentinel dtype={dtype} N={N} L={L}")
+    g = np.random.default_rng(100 + L + N)
+    H, D = 4, 64
+    k = g.standard_normal((1, H, L, D)) * 0.05
+    v = np.zeros((1, H, L, D))
+    v[0, :, np.arange(L), np.arange(L) % D] = 1.0
+    q = np.zeros((1, H, N, D))
+    for i in range(N):
+        q[0, :, i, 40 + i] = 1.0
+        p = L - N + i
+        k[0, :, p, 40 + i] = 120.0
+        if p + 1 < L:
+            k[0, :, p + 1, 40 + i] = 120.0
+    ks, vs, qs = (O.narrow(a, dtype) for a in (k, v, q))
+    cache = kb.Cache.wrap(to_dev(ks, dtype), to_dev(vs, dtype))
+    out = kb.decode_attn_self(to_dev(qs, dtype), cache, L, 0.125, ws=_ws())
+    oc = O.ConcatCache(1, H, D, dtype)
+    oc.append(ks, vs)
+    ref = O.attend_self(qs, oc, 0.125)
+    got = out.cpu().numpy()
+    for i in range(N):
+        own = (L - N + i) % D
+        assert np.all(got[0, :, i, own] > 0.99)
+    assert max_err(out, ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_large_scores_online_rescale(dtype):
+    """Scores with sd ~ 16: the running max changes often inside a split."""
+    say(f"case: large scores {dtype}")
+    g = np.random.default_rng(5)
+    B, H, L, N = 2, 8, 700, 3
+    k = O.narrow(g.standard_normal((B, H, L, 64)) * 4, dtype)
+    v = O.narrow(g.standard_normal((B, H, L, 64)), dtype)
+    q = O.narrow(g.standard_normal((B, H, N, 64)) * 4, dtype)
+    cache = kb.Cache.wrap(to_dev(k, dtype), to_dev(v, dtype))
+    out = kb.decode_attn_self(to_dev(q, dtype), cache, L, 0.125, ws=_ws())
+    oc = O.ConcatCache(B, H, 64, dtype)
+    oc.append(k, v)
+    e = max_err(out, O.attend_self(q, oc, 0.125))
+    say(f"large scores {dtype}: {e:.2e}")
+    assert e <= TOL[dtype]
+
+
+# ------------------------------------------------------ speculative verify ----
+
+@pytest.mark.parametrize("L_before", [64, 128, 443])
+def test_verify_attention_n5(L_before):
+    """Five draft rows appended at once, causal among themselves, over the
+    self cache and the cross cache (large-v2 layer shape)."""
+    w = I.WHISPER_VERIFY
+    say(f"case: verify attention L_before={L_before}")
+    layer = 3
+    L = L_before + 5
+    k_all, v_all = I.self_kv(w, layer)
+    xk, xv = I.cross_kv(w, layer)
+    cache = kb.Cache(1, 20, 448, torch.float16)
+    kb.kv_append(cache, to_dev(k_all[:, :, :L_before], "f16"), to_dev(v_all[:, :, :L_before], "f16"), 0)
+    kb.kv_append(cache, to_dev(k_all[:, :, L_before:L], "f16"), to_dev(v_all[:, :, L_before:L], "f16"),
+                 L_before)
+    xc = kb.Cache(1, 20, 1500, torch.float16)
+    kb.kv_append(xc, to_dev(xk, "f16"), to_dev(xv, "f16"), 0)
+    q = I.queries(w, layer, L, N=5)
+    qx = I.queries(w, layer, L, N=5, cross=True)
+    ws = _ws()
+    o_self = kb.decode_attn_self(to_dev(q, "f16"), cache, L, w.attn_scale, ws=ws)
+    o_cross = kb.decode_attn_cross(to_dev(qx, "f16"), xc, 1500, w.attn_scale, ws=ws)
+    oc = O.ConcatCache(1, 20, 64, "f16")
+    oc.append(k_all[:, :, :L_before], v_all[:, :, :L_before])
+    oc.append(k_all[:, :, L_before:L], v_all[:, :, L_before:L])
+    ox = O.ConcatCache(1, 20, 64, "f16")
+    ox.set_once(xk, xv)
+    e1 = max_err(o_self, O.attend_self(q, oc, w.attn_scale))
+    e2 = max_err(o_cross, O.attend_cross(qx, ox, w.attn_scale))
+    say(f"verify L={L}: self {e1:.2e} cross {e2:.2e}")
+    assert e1 <= TOL["f16"] and e2 <= TOL["f16"]
+
+
+def _verify_gpu(logits, draft, dtype="f32"):
+    lt = to_dev(logits if dtype == "f32" else O.narrow(logits.astype(np.float64), dtype), dtype)
+    dt = torch.from_numpy(draft).to("cuda")
+    B, R, _ = logits.shape
+    am = torch.empty((B, R), dtype=torch.int32, device="cuda")
+    acc, nxt, _ = kb.verify_accept(lt, dt, argmax_out=am)
+    return acc.cpu().numpy(), nxt.cpu().numpy(), am.cpu().numpy()
+
+
+def test_verify_accept_random_trials_bit_exact():
+    w = I.WHISPER_VERIFY
+    say("case: verify_accept 400 trials V=51865")
+    hist = np.zeros(6, dtype=int)
+    for t in range(400):
+        logits, draft = I.verify_logits(w, t, plant=(t % 8 != 0))
+        acc, nxt, am = _verify_gpu(logits, draft)
+        ram, racc, rnxt = O.verify_accept(logits, draft)
+        assert np.array_equal(am, ram), t
+        assert np.array_equal(acc, racc) and np.array_equal(nxt, rnxt), t
+        hist[racc[0]] += 1
+    say(f"accept histogram {hist.tolist()}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_verify_accept_edges(dtype):
+    say(f"case: verify edges {dtype}")
+    g = np.random.default_rng(21)
+    B, N, V = 4, 5, 51865
+    for R in (N, N + 1):
+        logits = g.standard_normal((B, R, V)).astype(np.float32) * 2
+        logits[0, 0, [4095, 4096, 9000]] = 30.0          # tie across workgroup slices
+        logits[0, 1, :] = -np.inf                          # all -inf -> 0
+        logits[0, 2, :5000] = -np.inf
+        logits[1, 0, V - 1] = 31.0                         # last element
+        logits[1, 1, :] = 0.5                              # all equal -> 0
+        logits[2, 3, [17, 40000]] = 33.0
+        ref_am = O.argmax_rows(O.widen(O.narrow(logits.astype(np.float64), dtype), dtype)
+                               if dtype != "f32" else logits)
+        draft = ref_am[:, :N].copy().astype(np.int32)
+        draft[1, 2] = -5                                   # out of range never matches
+        draft[2, 0] = V + 7
+        draft[3, 4] = (draft[3, 4] + 1) % V                # mismatch at the last draft
+        acc, nxt, am = _verify_gpu(logits, draft, dtype)
+        racc = np.zeros(B, np.int32)
+        rnxt = np.zeros(B, np.int32)
+        for b in range(B):
+            racc[b], rnxt[b] = O.accept(ref_am[b], draft[b])
+        assert np.array_equal(am, ref_am)
+        assert np.array_equal(acc, racc) and np.array_equal(nxt, rnxt)
+        assert acc[0] == N and nxt[0] == (ref_am[0, N] if R == N + 1 else -1)
+
+
+@pytest.mark.parametrize("V", [1, 7, 4096, 4097, 12289])
+def test_verify_accept_small_vocab(V):
+    say(f"case: verify V={V}")
+    g = np.random.default_rng(V)
+    logits = np.round(g.standard_normal((2, 3, V)) * 2).astype(np.float32)  # many ties
+    draft = g.integers(0, V, (2, 3)).astype(np.int32)
+    acc, nxt, am = _verify_gpu(logits, draft)
+    ram, racc, rnxt = O.verify_accept(logits, draft)
+    assert np.array_equal(am, ram) and np.array_equal(acc, racc) and np.array_equal(nxt, rnxt)
+
+
+# ------------------------------------------------------------------ beam ----
+
+def test_beam_reorder_and_attention():
+    w = I.WHISPER_BEAM
+    say("case: beam 5, 224 steps, two layers")
+    layers = [0, 1]
+    steps = 224
+    ws = _ws()
+    xcs, oxs, caches, ocs, kvs = [], [], [], [], []
+    for l in layers:
+        xk, xv = I.cross_kv(w, l)
+        xc = kb.Cache(1, 20, 1500, torch.float16)
+        kb.kv_append(xc, to_dev(xk, "f16"), to_dev(xv, "f16"), 0)
+        ox = O.ConcatCache(1, 20, 64, "f16"); ox.set_once(xk, xv)
+        xcs.append(xc); oxs.append(ox)
+        caches.append(kb.Cache(5, 20, 448, torch.float16))
+        ocs.append(O.ConcatCache(5, 20, 64, "f16"))
+        k_all, v_all = I.self_kv(w, l)
+        kvs.append((k_all, v_all, to_dev(k_all, "f16"), to_dev(v_all, "f16")))
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    worst = 0.0
+    for s in range(steps):
+        par = I.parents(w, s)
+        pd = torch.from_numpy(par).to("cuda")
+        L = s + 1
+        for li, l in enumerate(layers):
+            k_all, v_all, kd, vd = kvs[li]
+            if s > 0:
+                kb.kv_reorder(caches[li], pd, s, status)
+                ocs[li].reorder(par)
+            kb.kv_append(caches[li], kd[:, :, s:s + 1].contiguous(), vd[:, :, s:s + 1].contiguous(), s)
+            ocs[li].append(k_all[:, :, s:s + 1], v_all[:, :, s:s + 1])
+            if s % 16 == 15 or s == steps - 1:
+                q = I.queries(w, l, s)
+                qx = I.queries(w, l, s, cross=True)
+                o1 = kb.decode_attn_self(to_dev(q, "f16"), caches[li], L, w.attn_scale, ws=ws)
+                o2 = kb.decode_attn_cross(to_dev(qx, "f16"), xcs[li], 1500, w.attn_scale, ws=ws)
+                e1 = max_err(o1, O.attend_self(q, ocs[li], w.attn_scale))
+                e2 = max_err(o2, O.attend_cross(qx, oxs[li], w.attn_scale))
+                worst = max(worst, e1, e2)
+                assert e1 <= TOL["f16"] and e2 <= TOL["f16"]
+                kc = from_dev(caches[li].k, "f16")[:, :, :L]
+                vc = from_dev(caches[li].v, "f16")[:, :, :L]
+                assert np.array_equal(bits(kc), bits(ocs[li].k))
+                assert np.array_equal(bits(vc), bits(ocs[li].v))
+    assert int(status.item()) == 0
+    say(f"beam: worst attention max|err| {worst:.2e}")
+
+
+def test_reorder_duplicate_parents_and_bad_parent():
+    say("case: reorder duplicates / invalid parent")
+    g = np.random.default_rng(3)
+    for dtype in ("f32", "f16", "bf16"):
+        B, H, S, L = 7, 3, 40, 33
+        k = O.narrow(g.standard_normal((B, H, S, 64)), dtype)
+        v = O.narrow(g.standard_normal((B, H, S, 64)), dtype)
+        cache = kb.Cache.wrap(to_dev(k, dtype), to_dev(v, dtype))
+        par = np.array([3, 3, 0, 6, 6, 6, 1], dtype=np.int32)
+        kb.kv_reorder(cache, torch.from_numpy(par).cuda(), L)
+        ek = k.copy(); ek[:, :, :L] = O.reorder(k[:, :, :L], par)
+        ev = v.copy(); ev[:, :, :L] = O.reorder(v[:, :, :L], par)
+        assert np.array_equal(bits(from_dev(cache.k, dtype)), bits(ek))
+        assert np.array_equal(bits(from_dev(cache.v, dtype)), bits(ev))
+        # an invalid parent leaves its beam unchanged and is reported
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        before_k = from_dev(cache.k, dtype)
+        bad = np.array([1, 0, 9, 3, -1, 5, 6], dtype=np.int32)
+        kb.kv_reorder(cache, torch.from_numpy(bad).cuda(), L, status)
+        after_k = from_dev(cache.k, dtype)
+        assert int(status.item()) == -2
+        assert np.array_equal(bits(after_k[2]), bits(before_k[2]))
+        assert np.array_equal(bits(after_k[4]), bits(before_k[4]))
+        assert np.array_equal(bits(after_k[0]), bits(before_k[1]))
+
+
+# ---------------------------------------------------------- GQA + RoPE ----
+
+def _bf16_ulp_diff(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    """Distance in representable bf16 steps (same-sign finite values)."""
+    def ordered(x):
+        x = x.astype(np.int32)
+        return np.where(x & 0x8000, -(x & 0x7FFF), x)
+    return np.abs(ordered(a_bits) - ordered(b_bits))
+
+
+@pytest.mark.parametrize("layer", [0, 29])
+def test_gqa_prefill_then_decode_with_rope(layer):
+    """B=8, 9 query / 3 KV heads, bf16, RoPE base 10000: prefill 512 tokens
+    (one append, 512 causal queries), then decode to 1024 one token at a time."""
+    w = I.GQA_PREFILL_DECODE
+    say(f"case: gqa prefill+decode layer {layer}")
+    P, S = 512, 1024
+    k_all, v_all = I.self_kv(w, layer)                  # [8, 3, 1024, 64] bf16
+    kd, vd = to_dev(k_all, "bf16"), to_dev(v_all, "bf16")
+    cache = kb.Cache(8, 3, S, torch.bfloat16)
+    oc = O.ConcatCache(8, 3, 64, "bf16")
+    ws = _ws()
+    # prefill
+    kb.kv_append(cache, kd[:, :, :P].contiguous(), vd[:, :, :P].contiguous(), 0, rope_base=w.rope_base)
+    oc.append(k_all[:, :, :P], v_all[:, :, :P], rope_base=w.rope_base)
+    qp = I.queries(w, layer, 0, N=P)
+    out = kb.decode_attn_self(to_dev(qp, "bf16"), cache, P, w.attn_scale, rope_base=w.rope_base, ws=ws)
+    gk = from_dev(cache.k, "bf16")[:, :, :P]
+    d = _bf16_ulp_diff(gk, oc.k)
+    say(f"rope keys: max ulp {d.max()}, share off by one {np.mean(d > 0):.2e}")
+    assert d.max() <= 1 and np.mean(d > 0) < 0.01
+    assert np.array_equal(from_dev(cache.v, "bf16")[:, :, :P], oc.v)
+    # the oracle attends over its own rotated keys; the kernel over its own
+    e = max_err(out, O.attend_self(qp, oc, w.attn_scale, rope_base=w.rope_base))
+    say(f"prefill max|err| {e:.2e}")
+    assert e <= TOL["bf16"]
+    # decode
+    check = {P + 1, 700, S}
+    for L in range(P + 1, S + 1):
+        kb.kv_append(cache, kd[:, :, L - 1:L].contiguous(), vd[:, :, L - 1:L].contiguous(), L - 1,
+                     rope_base=w.rope_base)
+        oc.append(k_all[:, :, L - 1:L], v_all[:, :, L - 1:L], rope_base=w.rope_base)
+        if L in check:
+            q = I.queries(w, layer, L)
+            o = kb.decode_attn_self(to_dev(q, "bf16"), cache, L, w.attn_scale, rope_base=w.rope_base, ws=ws)
+            e = max_err(o, O.attend_self(q, oc, w.attn_scale, rope_base=w.rope_base))
+            say(f"decode L={L} max|err| {e:.2e}")
+            assert e <= TOL["bf16"]
+    d = _bf16_ulp_diff(from_dev(cache.k, "bf16"), oc.k)
+    assert d.max() <= 1
+
+
+def test_cross_cache_per_row_and_shared_agree():
+    """A cross cache shared by 3 rows gives what 3 identical per-row copies give."""
+    say("case: cross shared vs per-row")
+    g = np.random.default_rng(8)
+    F = 1500
+    xk = O.narrow(g.standard_normal((1, 6, F, 64)) / 8, "f16")
+    xv = O.narrow(g.standard_normal((1, 6, F, 64)) / 8, "f16")
+    q = O.narrow(g.standard_normal((3, 6, 2, 64)) / 8, "f16")
+    shared = kb.Cache.wrap(to_dev(xk, "f16"), to_dev(xv, "f16"))
+    per_row = kb.Cache.wrap(to_dev(np.repeat(xk, 3, 0), "f16"), to_dev(np.repeat(xv, 3, 0), "f16"))
+    ws = _ws()
+    a = kb.decode_attn_cross(to_dev(q, "f16"), shared, F, 0.125, ws=ws)
+    b = kb.decode_attn_cross(to_dev(q, "f16"), per_row, F, 0.125, ws=ws)
+    ox = O.ConcatCache(1, 6, 64, "f16"); ox.set_once(xk, xv)
+    ref = O.attend_cross(q, ox, 0.125)
+    assert max_err(a, ref) <= TOL["f16"] and max_err(b, ref) <= TOL["f16"]
