@@ -44,11 +44,19 @@ template <> __device__ __forceinline__ void unpack2<BF16>(uint32_t w, float &lo,
 // A 16-byte vector -> vec_elems<DT>() floats.
 template <int DT> __device__ __forceinline__ void unpack16(u32x4 v, float *out) {
   if constexpr (DT == F32) {
+    // copy each element out first: bit-casting a vector element lvalue
+    // directly reads element 0 with this compiler
 #pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] = __builtin_bit_cast(float, v[i]);
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = v[i];
+      out[i] = __builtin_bit_cast(float, w);
+    }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) unpack2<DT>(v[i], out[2 * i], out[2 * i + 1]);
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = v[i];
+      unpack2<DT>(w, out[2 * i], out[2 * i + 1]);
+    }
   }
 }
 

@@ -329,17 +329,25 @@ def test_reorder_duplicate_parents_and_bad_parent():
         assert int(status.item()) == -2
         assert np.array_equal(bits(after_k[2]), bits(before_k[2]))
         assert np.array_equal(bits(after_k[4]), bits(before_k[4]))
-        assert np.array_equal(bits(after_k[0]), bits(before_k[1]))
+        assert np.array_equal(bits(after_k[0, :, :L]), bits(before_k[1, :, :L]))
+        assert np.array_equal(bits(after_k[0, :, L:]), bits(before_k[0, :, L:]))
 
 
 # ---------------------------------------------------------- GQA + RoPE ----
 
-def _bf16_ulp_diff(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
-    """Distance in representable bf16 steps (same-sign finite values)."""
-    def ordered(x):
-        x = x.astype(np.int32)
-        return np.where(x & 0x8000, -(x & 0x7FFF), x)
-    return np.abs(ordered(a_bits) - ordered(b_bits))
+def _rope_key_check(gpu_bits, ref_bits, raw_bits):
+    """Rotated keys: the kernel rounds an fp32 rotation to bf16, the oracle an
+    fp64 one. They may differ by one bf16 step, plus the fp32 rounding error
+    of lo*c - hi*s (about 2^-22 of |lo| + |hi|) where the two terms cancel.
+    Returns (worst ratio to that bound, share of elements that differ)."""
+    g = O.widen(gpu_bits, "bf16")
+    r = O.widen(ref_bits, "bf16")
+    x = np.abs(O.widen(raw_bits, "bf16"))
+    half = x.shape[-1] // 2
+    pair = np.concatenate([x[..., :half] + x[..., half:]] * 2, axis=-1)
+    ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(r), 1e-38))[1] - 8)
+    bound = ulp + pair * 2.0 ** -20
+    return float(np.max(np.abs(g - r) / bound)), float(np.mean(g != r))
 
 
 @pytest.mark.parametrize("layer", [0, 29])
@@ -360,9 +368,9 @@ def test_gqa_prefill_then_decode_with_rope(layer):
     qp = I.queries(w, layer, 0, N=P)
     out = kb.decode_attn_self(to_dev(qp, "bf16"), cache, P, w.attn_scale, rope_base=w.rope_base, ws=ws)
     gk = from_dev(cache.k, "bf16")[:, :, :P]
-    d = _bf16_ulp_diff(gk, oc.k)
-    say(f"rope keys: max ulp {d.max()}, share off by one {np.mean(d > 0):.2e}")
-    assert d.max() <= 1 and np.mean(d > 0) < 0.01
+    worst, share = _rope_key_check(gk, oc.k, k_all[:, :, :P])
+    say(f"rope keys: worst/bound {worst:.3f}, share differing {share:.2e}")
+    assert worst <= 1.0 and share < 0.01
     assert np.array_equal(from_dev(cache.v, "bf16")[:, :, :P], oc.v)
     # the oracle attends over its own rotated keys; the kernel over its own
     e = max_err(out, O.attend_self(qp, oc, w.attn_scale, rope_base=w.rope_base))
@@ -380,8 +388,8 @@ def test_gqa_prefill_then_decode_with_rope(layer):
             e = max_err(o, O.attend_self(q, oc, w.attn_scale, rope_base=w.rope_base))
             say(f"decode L={L} max|err| {e:.2e}")
             assert e <= TOL["bf16"]
-    d = _bf16_ulp_diff(from_dev(cache.k, "bf16"), oc.k)
-    assert d.max() <= 1
+    worst, share = _rope_key_check(from_dev(cache.k, "bf16"), oc.k, k_all)
+    assert worst <= 1.0 and share < 0.01
 
 
 def test_cross_cache_per_row_and_shared_agree():
