@@ -1,10 +1,11 @@
 """Decode-step benchmark: Whisper-large-v2-shaped greedy decoding on one GPU.
 
 One step = for each of the 32 decoder layers: append the new token's K/V to
-the self cache (kv_append, T=1), self attention of the token's query over the
-cache (decode_attn_self, N=1), cross attention over the 1500-frame cache built
-once before timing (decode_attn_cross). B=1, 20 heads of 64, fp16 storage,
-fp32 accumulation. Steps walk the self cache from length 1 to 448 and wrap.
+the self cache and attend the token's query over it (decode_step_self: the
+append and the self attention in one launch; --unfused: kv_append then
+decode_attn_self), then cross attention over the 1500-frame cache built once
+before timing (decode_attn_cross). B=1, 20 heads of 64, fp16 storage, fp32
+accumulation. Steps walk the self cache from length 1 to 448 and wrap.
 
 Prints one JSON line. `value` is decode steps/s over the timed steps (hipGraph
 replay of one captured graph per step, inputs resident in HBM). Also reported:
@@ -33,10 +34,10 @@ LAYERS, H, D, S_MAX, FRAMES = 32, 20, 64, 448, 1500
 ROW_BYTES = H * D * 2                      # one position of one layer, K or V, fp16
 CROSS_BYTES = 2 * FRAMES * ROW_BYTES       # K+V read by one cross-attention launch
 METRIC = "decode-attn steps/s + effective KV GB/s (% HBM peak), large-v2 shape, 1 GPU"
-WORKLOAD = ("whisper-large-v2 greedy decode step: 32 layers x [kv_append T=1, self attention "
+WORKLOAD = ("whisper-large-v2 greedy decode step: 32 layers x [append T=1 + self attention "
             "N=1 over len 1..448, cross attention over 1500 frames], B1, 20 heads x 64, fp16 "
             "storage / fp32 accumulate")
-KERNEL_SOURCES = ["kv_cached_decode_amd/csrc/kvd_kernels.hip",
+KERNEL_SOURCES = ["kv_cached_decode_amd/csrc/kvd_attn.hip",
                   "kv_cached_decode_amd/csrc/kvd_device.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_cross_attention.json")
 
@@ -100,14 +101,20 @@ class Engine:
                                    kb.attn_workspace_bytes(1, H, 1, FRAMES)), dev)
         torch.cuda.synchronize()
 
-    def step(self, s: int):
-        """Decode step s: the self cache grows to length s + 1."""
+    def step(self, s: int, fused: bool = True):
+        """Decode step s: the self cache grows to length s + 1. Fused: the
+        append runs inside the self-attention launch (decode_step_self);
+        otherwise kv_append then decode_attn_self."""
         kb = self.kb
         L = s + 1
         for l in range(LAYERS):
-            kb.kv_append(self.self_c[l], self.k_new[l][s], self.v_new[l][s], s)
-            kb.decode_attn_self(self.q_self[l][s], self.self_c[l], L, self.scale,
-                                out=self.out_self[l], ws=self.ws)
+            if fused:
+                kb.decode_step_self(self.q_self[l][s], self.k_new[l][s], self.v_new[l][s],
+                                    self.self_c[l], L, self.scale, out=self.out_self[l], ws=self.ws)
+            else:
+                kb.kv_append(self.self_c[l], self.k_new[l][s], self.v_new[l][s], s)
+                kb.decode_attn_self(self.q_self[l][s], self.self_c[l], L, self.scale,
+                                    out=self.out_self[l], ws=self.ws)
             kb.decode_attn_cross(self.q_cross[l][s], self.cross_c[l], FRAMES, self.scale,
                                  out=self.out_cross[l], ws=self.ws)
 
@@ -116,7 +123,7 @@ class Engine:
                                   out=self.out_cross[l], ws=self.ws)
 
 
-def capture_graphs(torch, eng: Engine):
+def capture_graphs(torch, eng: Engine, fused: bool):
     graphs = []
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
@@ -124,29 +131,40 @@ def capture_graphs(torch, eng: Engine):
         for s in range(S_MAX):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=stream):
-                eng.step(s)
+                eng.step(s, fused)
             graphs.append(g)
     torch.cuda.current_stream().wait_stream(stream)
     torch.cuda.synchronize()
     return graphs
 
 
-def time_cross_kernel(torch, eng: Engine, reps: int = 4):
-    """Average duration of one cross-attention launch, HIP events recorded
-    around each launch on the stream it runs on."""
+def time_cross_kernel(torch, eng: Engine, reps: int = 8):
+    """Average duration of one cross-attention launch: HIP events on the
+    launch stream around back-to-back batches of 32 launches (one per layer,
+    so no launch re-reads the previous one's cache), divided by the count.
+    Also the per-launch figure with events around every single launch, which
+    adds the event overhead."""
     stream = torch.cuda.current_stream()
-    times = []
+    batches, singles = [], []
     for r in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
         for l in range(LAYERS):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
             eng.cross(l, (r * 37 + l) % S_MAX)
-            b.record(stream)
-            times.append((a, b))
+        b.record(stream)
+        batches.append((a, b))
+    for l in range(LAYERS):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        eng.cross(l, l)
+        b.record(stream)
+        singles.append((a, b))
     torch.cuda.synchronize()
-    ms = [a.elapsed_time(b) for a, b in times]
-    return float(np.mean(ms)) * 1e-3, float(np.median(ms)) * 1e-3
+    per_launch = [a.elapsed_time(b) / LAYERS for a, b in batches]
+    single = [a.elapsed_time(b) for a, b in singles]
+    return float(np.mean(per_launch)) * 1e-3, float(np.median(single)) * 1e-3
 
 
 def cpu_baseline(target_s: float = 15.0):
@@ -203,6 +221,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--eager", action="store_true", help="also time eager (no graph) launches")
+    ap.add_argument("--unfused", action="store_true",
+                    help="separate kv_append and decode_attn_self launches (96 per step)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -220,7 +240,8 @@ def main():
     print("bench: building device state", file=sys.stderr, flush=True)
     eng = Engine(torch, kb, I)
     print("bench: capturing graphs", file=sys.stderr, flush=True)
-    graphs = capture_graphs(torch, eng)
+    fused = not args.unfused
+    graphs = capture_graphs(torch, eng, fused)
 
     # warmup
     for i in range(args.warmup):
@@ -243,11 +264,11 @@ def main():
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         for s in seq:
-            eng.step(s)
+            eng.step(s, fused)
         torch.cuda.synchronize()
         eager = args.steps / (time.perf_counter() - t1)
 
-    k_avg, k_med = time_cross_kernel(torch, eng)
+    k_avg, k_single = time_cross_kernel(torch, eng)
     achieved = CROSS_BYTES / k_avg / 1e9
     traffic = measured_traffic()
 
@@ -270,7 +291,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD, "layers": LAYERS, "batch": 1, "heads": H,
                    "head_dim": D, "self_len": "1..448 (steps wrap)", "cross_frames": FRAMES,
-                   "launch": "one hipGraph per step, 96 kernels"},
+                   "launch": ("one hipGraph per step, 64 kernels (append fused into self "
+                              "attention)") if fused else "one hipGraph per step, 96 kernels"},
         "effective_kv_gbps": round(gbps, 1),
         "hbm_peak_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "kernel": "decode_attn_cross (attn_kernel<f16, 1>)",
@@ -279,7 +301,8 @@ def main():
                      "traffic": traffic,
                      "bytes_per_launch": CROSS_BYTES,
                      "avg_launch_us": round(k_avg * 1e6, 3),
-                     "median_launch_us": round(k_med * 1e6, 3)},
+                     "single_launch_event_us": round(k_single * 1e6, 3),
+                     "timing": "HIP events around back-to-back batches of 32 launches"},
         "cpu_baseline": cpu,
     }
     if eager is not None:

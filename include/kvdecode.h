@@ -121,6 +121,22 @@ int decode_attn_self(const void *q, int32_t Hq, int32_t N, const kvd_cache *cach
                      int32_t len, float scale, float rope_base, float *out,
                      void *ws, size_t ws_bytes, void *stream);
 
+/* decode_step_self - kv_append followed by decode_attn_self, in one launch
+ * for N <= 16 (two launches on `stream` for longer blocks such as a prefill):
+ * the N new K/V rows are written at positions [len - N, len) (keys rotated
+ * exactly as kv_append rotates them when rope_base > 0) and the N queries
+ * attend over the cache including them ([W] the hook returns the cache with
+ * the new rows concatenated, and attention consumes that; [N] attention
+ * block: concatenate K_new/V_new onto the cache, then attend).
+ *   k_new, v_new: device, [B][H][N][D] in cache->dtype (B, H of the cache).
+ *   Other arguments, results and errors as decode_attn_self. After the call
+ *   the cache holds exactly what kv_append(cache, k_new, v_new, len - N, N,
+ *   rope_base) would have written, and `out` equals what decode_attn_self
+ *   would have returned. */
+int decode_step_self(const void *q, const void *k_new, const void *v_new, int32_t Hq, int32_t N,
+                     const kvd_cache *cache, int32_t len, float scale, float rope_base,
+                     float *out, void *ws, size_t ws_bytes, void *stream);
+
 /* decode_attn_cross - attention of N queries per row over all `frames`
  * rows of a cross-attention cache, with no mask ([W]: cross-attention K/V
  * computed once from the encoder and reused every step).
@@ -151,7 +167,8 @@ int decode_attn_cross(const void *q, int32_t B, int32_t Hq, int32_t N,
  *   accept_len, next_token: device int32 [B].
  *   ws: device workspace, ws_bytes >= kvd_verify_workspace_bytes(B, R, V),
  *     zero-filled before its first use and left that way.
- * Errors: KVD_ERR_NULL, KVD_ERR_SHAPE (B, N, V < 1), KVD_ERR_ROWS,
+ * Errors: KVD_ERR_NULL, KVD_ERR_SHAPE (B, N, V < 1; N > 63; B > 4096;
+ *   R * ceil(V / 4096) > 2048), KVD_ERR_ROWS,
  *   KVD_ERR_DTYPE, KVD_ERR_WORKSPACE, KVD_ERR_ALIGN (logits only). */
 int verify_accept(const void *logits, int32_t logits_dtype, int32_t B, int32_t R,
                   int32_t V, const int32_t *draft, int32_t N, int32_t *argmax_out,

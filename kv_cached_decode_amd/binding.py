@@ -44,6 +44,9 @@ _SIGNATURES = {
     "kv_reorder": (c_int, [ctypes.POINTER(KvdCache), c_void_p, c_int32, c_void_p, c_void_p]),
     "decode_attn_self": (c_int, [c_void_p, c_int32, c_int32, ctypes.POINTER(KvdCache), c_int32,
                                  c_float, c_float, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "decode_step_self": (c_int, [c_void_p, c_void_p, c_void_p, c_int32, c_int32,
+                                 ctypes.POINTER(KvdCache), c_int32, c_float, c_float, c_void_p,
+                                 c_void_p, c_size_t, c_void_p]),
     "decode_attn_cross": (c_int, [c_void_p, c_int32, c_int32, c_int32, ctypes.POINTER(KvdCache),
                                   c_int32, c_float, c_void_p, c_void_p, c_size_t, c_void_p]),
     "verify_accept": (c_int, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_int32,
@@ -202,6 +205,29 @@ def decode_attn_self(q: torch.Tensor, cache: Cache, length: int, scale: float,
         ws = workspace(attn_workspace_bytes(d.B, Hq, N, length), q.device)
     _check("decode_attn_self", lib().decode_attn_self(
         _dev(q, "q", cache.dtype), Hq, N, ctypes.byref(d), length, scale, rope_base,
+        _dev(out, "out", torch.float32), _dev(ws, "ws"), ws.numel() * ws.element_size(),
+        _stream()))
+    return out
+
+
+def decode_step_self(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, cache: Cache,
+                     length: int, scale: float, rope_base: float = 0.0,
+                     out: torch.Tensor | None = None,
+                     ws: torch.Tensor | None = None) -> torch.Tensor:
+    """kv_append of the N new rows at [length - N, length) plus decode_attn_self,
+    one launch for N <= 16."""
+    d = cache.desc()
+    if q.dim() != 4 or q.shape[0] != d.B or q.shape[3] != d.D:
+        raise ValueError(f"q must be [B={d.B}, Hq, N, {d.D}], got {tuple(q.shape)}")
+    Hq, N = q.shape[1], q.shape[2]
+    if tuple(k_new.shape) != (d.B, d.H, N, d.D) or k_new.shape != v_new.shape:
+        raise ValueError(f"k_new/v_new must be [{d.B}, {d.H}, {N}, {d.D}]")
+    out = _attn_out(q, out)
+    if ws is None:
+        ws = workspace(attn_workspace_bytes(d.B, Hq, N, length), q.device)
+    _check("decode_step_self", lib().decode_step_self(
+        _dev(q, "q", cache.dtype), _dev(k_new, "k_new", cache.dtype),
+        _dev(v_new, "v_new", cache.dtype), Hq, N, ctypes.byref(d), length, scale, rope_base,
         _dev(out, "out", torch.float32), _dev(ws, "ws"), ws.numel() * ws.element_size(),
         _stream()))
     return out

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvdecode.so")
-SOURCES = ["kvd_kernels.hip", "kvd_api.cpp"]
+SOURCES = ["kvd_copy.hip", "kvd_attn.hip", "kvd_verify.hip", "kvd_api.cpp"]
 ARCH = "gfx950"
 
 
@@ -31,6 +31,9 @@ def compile_flags() -> list[str]:
         # packed fp32 VALU forms stay off: hipcc -O3 would otherwise form them
         # from plain float code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # no implicit fma contraction: every fused multiply-add is explicit,
+        # so the same expression rounds the same way at every call site
+        "-ffp-contract=off",
         "-Wall", "-Wno-unused-function",
         f"-I{INCLUDE}", f"-I{CSRC}",
     ]

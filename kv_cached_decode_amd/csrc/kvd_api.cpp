@@ -1,6 +1,7 @@
 // C-ABI entry points: argument validation (all of it before any HIP call),
 // launch planning, and status codes. The operations are defined in
 // include/kvdecode.h.
+#include <limits.h>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -42,7 +43,7 @@ size_t attn_bytes(const AttnPlan &p) { return kCounterBytes + p.part_floats * si
 // Fill the plan-dependent fields and the workspace pointers.
 int prepare_attn(AttnArgs &a, int dtype, void *ws, size_t ws_bytes) {
   const int units = a.Bkv * a.Hkv;
-  const AttnPlan p = kvd::plan_attn(dtype, units, a.G, a.L);
+  const AttnPlan p = kvd::plan_attn(dtype, units, a.G, a.L, a.rope_base > 0.f);
   if (p.row_tiles > 65535 || units > 65535) return KVD_ERR_SHAPE;  // grid limits
   a.chunk = p.chunk;
   a.splits = p.splits;
@@ -124,9 +125,13 @@ int kv_reorder(const kvd_cache *cache, const int32_t *parent, int32_t len, int32
   return status_of(kvd::launch_reorder(cache->dtype, a, static_cast<hipStream_t>(stream)));
 }
 
-int decode_attn_self(const void *q, int32_t Hq, int32_t N, const kvd_cache *cache, int32_t len,
-                     float scale, float rope_base, float *out, void *ws, size_t ws_bytes,
-                     void *stream) {
+namespace {
+
+// Shared by decode_attn_self and decode_step_self: validate and plan (no HIP
+// call). k_new/v_new non-null: the N new rows are appended in the same launch.
+int prepare_self(AttnArgs &a, const void *q, const void *k_new, const void *v_new, int32_t Hq,
+                 int32_t N, const kvd_cache *cache, int32_t len, float scale, float rope_base,
+                 float *out, void *ws, size_t ws_bytes) {
   int st = check_cache(cache);
   if (st) return st;
   if (!q || !out) return KVD_ERR_NULL;
@@ -135,10 +140,13 @@ int decode_attn_self(const void *q, int32_t Hq, int32_t N, const kvd_cache *cach
     return KVD_ERR_SHAPE;
   if (len > cache->S_max || len < N) return KVD_ERR_CAPACITY;
   if (!aligned16(q) || !aligned16(out)) return KVD_ERR_ALIGN;
-  AttnArgs a{};
+  if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return KVD_ERR_ALIGN;
+  a = AttnArgs{};
   a.q = q;
   a.k = cache->k;
   a.v = cache->v;
+  a.k_new = k_new;
+  a.v_new = v_new;
   a.out = out;
   a.B = cache->B;
   a.Hq = Hq;
@@ -150,11 +158,53 @@ int decode_attn_self(const void *q, int32_t Hq, int32_t N, const kvd_cache *cach
   a.G = a.group * N;
   a.L = len;
   a.causal_base = len - N;
+  a.new_base = k_new ? len - N : INT_MAX;
+  a.T_new = k_new ? N : 0;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.rope_base = rope_base;
-  st = prepare_attn(a, cache->dtype, ws, ws_bytes);
+  return prepare_attn(a, cache->dtype, ws, ws_bytes);
+}
+
+}  // namespace
+
+int decode_attn_self(const void *q, int32_t Hq, int32_t N, const kvd_cache *cache, int32_t len,
+                     float scale, float rope_base, float *out, void *ws, size_t ws_bytes,
+                     void *stream) {
+  AttnArgs a;
+  const int st = prepare_self(a, q, nullptr, nullptr, Hq, N, cache, len, scale, rope_base, out,
+                              ws, ws_bytes);
   if (st) return st;
   return status_of(kvd::launch_attn(cache->dtype, a, static_cast<hipStream_t>(stream)));
+}
+
+int decode_step_self(const void *q, const void *k_new, const void *v_new, int32_t Hq, int32_t N,
+                     const kvd_cache *cache, int32_t len, float scale, float rope_base,
+                     float *out, void *ws, size_t ws_bytes, void *stream) {
+  if (!k_new || !v_new) return KVD_ERR_NULL;
+  const bool fused = N <= kvd::kMaxFusedRows;
+  AttnArgs a;
+  const int st = prepare_self(a, q, fused ? k_new : nullptr, fused ? v_new : nullptr, Hq, N, cache,
+                              len, scale, rope_base, out, ws, ws_bytes);
+  if (st) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!fused) {
+    // a long block of new rows (prefill): append first, then attend
+    if (!aligned16(k_new) || !aligned16(v_new)) return KVD_ERR_ALIGN;
+    kvd::AppendArgs ap;
+    ap.k_cache = cache->k;
+    ap.v_cache = cache->v;
+    ap.k_new = k_new;
+    ap.v_new = v_new;
+    ap.B = cache->B;
+    ap.H = cache->H;
+    ap.S_max = cache->S_max;
+    ap.T = N;
+    ap.pos = len - N;
+    ap.rope_base = rope_base;
+    const int sa = status_of(kvd::launch_append(cache->dtype, ap, s));
+    if (sa) return sa;
+  }
+  return status_of(kvd::launch_attn(cache->dtype, a, s));
 }
 
 int decode_attn_cross(const void *q, int32_t B, int32_t Hq, int32_t N, const kvd_cache *xcache,
@@ -183,6 +233,7 @@ int decode_attn_cross(const void *q, int32_t B, int32_t Hq, int32_t N, const kvd
   a.G = (xcache->B == 1 ? B : 1) * a.group * N;
   a.L = frames;
   a.causal_base = -1;
+  a.new_base = INT_MAX;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.rope_base = 0.f;
   st = prepare_attn(a, xcache->dtype, ws, ws_bytes);
@@ -204,7 +255,7 @@ size_t kvd_attn_workspace_bytes(int32_t B, int32_t Hq, int32_t N, int32_t len_ma
       const int G = (shared ? B : 1) * group * N;
       for (int dt = 0; dt < 2; ++dt) {
         for (int L = 1; L <= len_max; ++L) {
-          const AttnPlan p = kvd::plan_attn(dt == 0 ? kvd::F32 : kvd::F16, units, G, L);
+          const AttnPlan p = kvd::plan_attn(dt == 0 ? kvd::F32 : kvd::F16, units, G, L, false);
           if (p.splits > 1) {
             const size_t b = attn_bytes(p);
             if (b > best) best = b;
@@ -242,6 +293,7 @@ int verify_accept(const void *logits, int32_t logits_dtype, int32_t B, int32_t R
   a.V = V;
   a.N = N;
   kvd::plan_verify(B, R, V, a.chunk, a.chunks);
+  if ((int64_t)R * a.chunks > kvd::kMaxVerifyPartials) return KVD_ERR_SHAPE;
   const size_t slots = (size_t)B * R * a.chunks;
   const size_t val_bytes = ((slots * sizeof(float) + 255) / 256) * 256;
   a.ws_count = static_cast<uint32_t *>(ws);

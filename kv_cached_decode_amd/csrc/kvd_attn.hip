@@ -1,0 +1,461 @@
+// Decode attention on gfx950, split over keys (the streaming kernel used for
+// one query per head and for small query groups).
+//
+// Workgroup (split, row tile, unit) takes keys [split*chunk, +chunk) of one
+// (cache row, kv head) "unit" for up to GM query rows. A wavefront loads
+// TILE keys per iteration with 16-byte loads: LPR lanes share a key row, so
+// one wave load covers RPL whole rows and is fully coalesced. Scores are
+// reduced across the LPR lanes with DPP. Each group of LPR lanes keeps its
+// own online-softmax state (running max m, sum l, unnormalised o, in the log2
+// domain), so the key loop has no cross-group traffic; groups are merged once
+// per wave, waves once per workgroup in LDS. Splits are merged by the last
+// workgroup of the unit to arrive: it stages every split's partial in LDS
+// with all loads in flight at once and combines them in split order, so the
+// result does not depend on arrival order.
+//
+// With new rows (k_new/v_new, at most kMaxFusedRows of them), the kernel also
+// performs the cache append of the step: each workgroup rotates and rounds
+// the new rows of its key range once into LDS, exactly as kv_append would
+// store them, and reads them from there; the workgroups of row tile 0 write
+// them into the cache. No workgroup reads those cache rows, so the writes
+// need no ordering within the launch.
+#include <stdlib.h>
+
+#include "kvd_device.hpp"
+#include "kvd_internal.hpp"
+
+namespace kvd {
+
+namespace {
+
+constexpr int kMaxWaves = 16;     // the wide variant: one workgroup of 1024 per unit
+constexpr int kSteps = 4;
+constexpr int kPStride = kHeadDim + 4;  // o[D], m, l, 2 pad floats: 16-byte rows
+constexpr int kMergeRows = 128;         // splits * rows per tile staged by the merge
+// staged floats per thread in the final merge, for 4- and 16-wave workgroups
+template <int NWMAX>
+constexpr int stage_iters() { return (kMergeRows * kPStride + 64 * NWMAX - 1) / (64 * NWMAX); }
+
+template <int DT>
+struct AttnGeom {
+  static constexpr int VE = vec_elems<DT>();      // elements per lane load
+  static constexpr int LPR = kHeadDim / VE;       // lanes per key row
+  static constexpr int RPL = 64 / LPR;            // key rows per wave load
+  static constexpr int TILE = RPL * kSteps;       // keys per wave iteration
+  static constexpr int ROWB = kHeadDim * Storage<DT>::bytes;
+};
+
+struct RowId {
+  int b, h, i;
+};
+
+// Query row gg of unit (bkv, hk): numbered (bl * group + j) * N + i.
+__device__ __forceinline__ RowId row_id(const AttnArgs &a, int bkv, int hk, int gg) {
+  RowId r;
+  r.i = gg % a.N;
+  const int j = (gg / a.N) % a.group;
+  const int bl = gg / (a.N * a.group);
+  r.b = (a.Bkv == 1) ? bl : bkv;
+  r.h = hk * a.group + j;
+  return r;
+}
+
+template <int DT, int GM, bool FUSED, int NWMAX, bool ROPE>
+__global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
+  using Geo = AttnGeom<DT>;
+  constexpr int D = kHeadDim;
+  constexpr int VE = Geo::VE, LPR = Geo::LPR, RPL = Geo::RPL, TILE = Geo::TILE;
+  constexpr int ROWB = Geo::ROWB;
+  constexpr int VPR = ROWB / 16;  // 16-byte vectors per row
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const int kr = lane / LPR;  // key row within a wave load
+  const int ds = lane % LPR;  // dims [ds*VE, ds*VE + VE)
+
+  // every kernel argument the first loads depend on, fetched in one go (the
+  // empty asm keeps the compiler from sinking a fetch into a later branch,
+  // which would add a serial round trip before the first key load)
+  {
+    const int f0 = a.Hkv, f1 = a.S_max, f2 = a.G, f3 = a.L, f4 = a.N, f5 = a.group, f6 = a.Bkv,
+              f7 = a.causal_base, f8 = a.new_base, f9 = a.chunk, f10 = a.Hq, f11 = a.T_new;
+    asm volatile("" ::"s"(f0), "s"(f1), "s"(f2), "s"(f3), "s"(f4), "s"(f5), "s"(f6), "s"(f7),
+                 "s"(f8), "s"(f9), "s"(f10), "s"(f11), "s"(a.k), "s"(a.v), "s"(a.q));
+  }
+  const int split = blockIdx.x, rt = blockIdx.y, unit = blockIdx.z;
+  const int bkv = unit / a.Hkv, hk = unit % a.Hkv;
+  const int g0 = rt * GM;
+  const int gcount = min(GM, a.G - g0);
+  const int k0 = split * a.chunk;
+  const int kspan = min(k0 + a.chunk, a.L);
+
+  const size_t head = (size_t)bkv * a.Hkv + hk;
+  char *kc = static_cast<char *>(a.k) + head * a.S_max * ROWB;
+  char *vc = static_cast<char *>(a.v) + head * a.S_max * ROWB;
+  const int nb0 = max(k0, a.new_base);  // first new row of this key range
+
+  // ---- which keys each query row sees (indices only, no memory access)
+  int lim[GM];
+  int kvis = 0;
+#pragma unroll
+  for (int g = 0; g < GM; ++g) {
+    lim[g] = 0;
+    if (g < gcount) {
+      const RowId r = row_id(a, bkv, hk, g0 + g);
+      lim[g] = (a.causal_base < 0) ? a.L : a.causal_base + r.i + 1;
+      kvis = max(kvis, lim[g]);
+    }
+  }
+  const int kend = min(kspan, kvis);
+
+  // ---- first tile of cached keys: in flight before anything else waits
+  u32x4 kv[kSteps], vv[kSteps];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      const int key = t + s * RPL + kr;
+      kv[s] = u32x4{0, 0, 0, 0};
+      vv[s] = u32x4{0, 0, 0, 0};
+      if (key < kend && (!FUSED || key < nb0)) {
+        kv[s] = load16(kc + (size_t)key * ROWB + ds * 16);
+        vv[s] = load16(vc + (size_t)key * ROWB + ds * 16);
+      }
+    }
+  };
+  int t0 = k0 + wave * TILE;
+  if (t0 < kend) load_tile(t0);
+
+  // ---- query rows: their loads go out before anything waits
+  u32x4 qraw[GM], qpart[GM];
+#pragma unroll
+  for (int g = 0; g < GM; ++g) {
+    qraw[g] = u32x4{0, 0, 0, 0};
+    qpart[g] = u32x4{0, 0, 0, 0};
+    if (g < gcount) {
+      const RowId r = row_id(a, bkv, hk, g0 + g);
+      const char *qrow =
+          static_cast<const char *>(a.q) + ((size_t)(r.b * a.Hq + r.h) * a.N + r.i) * ROWB;
+      qraw[g] = load16(qrow + ds * 16);
+      if (ROPE) qpart[g] = load16(qrow + (ds ^ (LPR / 2)) * 16);
+    }
+  }
+
+  // ---- fused append: the new rows of this key range are rotated and
+  // rounded once into LDS (the loop reads them there); row tile 0 also writes
+  // them into the cache
+  __shared__ u32x4 s_new[FUSED ? 2 * kMaxFusedRows * VPR : 1];
+  if constexpr (FUSED) {
+    constexpr int HALF_VECS = kHeadDim / 2 / VE;
+    const char *kn = static_cast<const char *>(a.k_new) + head * a.T_new * ROWB;
+    const char *vn = static_cast<const char *>(a.v_new) + head * a.T_new * ROWB;
+    const int n = (kspan - nb0) * HALF_VECS;
+    for (int t = threadIdx.x; t < n; t += blockDim.x) {
+      const int r = t / HALF_VECS, j = t % HALF_VECS;
+      const int pos = nb0 + r;
+      const size_t src = (size_t)(pos - a.new_base) * ROWB;
+      const PairChunks c = load_pair<DT>(kn + src, vn + src, j, pos, ROPE ? a.rope_base : 0.f);
+      s_new[r * VPR + j] = c.klo;
+      s_new[r * VPR + j + VPR / 2] = c.khi;
+      s_new[(kMaxFusedRows + r) * VPR + j] = c.vlo;
+      s_new[(kMaxFusedRows + r) * VPR + j + VPR / 2] = c.vhi;
+      if (rt == 0) store_pair<DT>(kc + (size_t)pos * ROWB, vc + (size_t)pos * ROWB, j, c);
+    }
+    __syncthreads();
+  }
+
+  // ---- query rows: rotate (fp32), fold in scale*log2(e)
+  float qf[GM][VE];
+#pragma unroll
+  for (int g = 0; g < GM; ++g) {
+#pragma unroll
+    for (int e = 0; e < VE; ++e) qf[g][e] = 0.f;
+    if (g < gcount) {
+      if constexpr (ROPE) {
+        const RowId r = row_id(a, bkv, hk, g0 + g);
+        rope_slice_f32<DT>(qraw[g], qpart[g], ds, a.causal_base + r.i, a.rope_base, qf[g]);
+      } else {
+        unpack16<DT>(qraw[g], qf[g]);
+      }
+#pragma unroll
+      for (int e = 0; e < VE; ++e) qf[g][e] *= a.scale_log2;
+    }
+  }
+
+  float m[GM], l[GM], o[GM][VE];
+#pragma unroll
+  for (int g = 0; g < GM; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) o[g][e] = 0.f;
+  }
+
+  while (t0 < kend) {
+    if constexpr (FUSED) {  // new rows of this tile come from LDS
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) {
+        const int key = t0 + s * RPL + kr;
+        if (key < kend && key >= nb0) {
+          kv[s] = s_new[(key - nb0) * VPR + ds];
+          vv[s] = s_new[(kMaxFusedRows + key - nb0) * VPR + ds];
+        }
+      }
+    }
+    float sc[kSteps][GM];
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      float kf[VE];
+      unpack16<DT>(kv[s], kf);
+      const int key = t0 + s * RPL + kr;
+#pragma unroll
+      for (int g = 0; g < GM; ++g) {
+        sc[s][g] = -INFINITY;
+        if (g < gcount) {  // uniform: every lane takes part in the DPP sum
+          float d = 0.f;
+#pragma unroll
+          for (int e = 0; e < VE; ++e) d = fmaf(qf[g][e], kf[e], d);
+          d = group_sum<LPR>(d);
+          if (key < lim[g] && key < kend) sc[s][g] = d;
+        }
+      }
+    }
+    float vf[kSteps][VE];
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) unpack16<DT>(vv[s], vf[s]);
+    t0 += nw * TILE;
+    if (t0 < kend) load_tile(t0);  // next tile in flight during this one's math
+#pragma unroll
+    for (int g = 0; g < GM; ++g) {
+      float mt = sc[0][g];
+#pragma unroll
+      for (int s = 1; s < kSteps; ++s) mt = fmaxf(mt, sc[s][g]);
+      const float mn = fmaxf(m[g], mt);
+      if (mn != -INFINITY) {
+        const float alpha = exp2f(m[g] - mn);
+        float ls = l[g] * alpha;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) o[g][e] *= alpha;
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+          const float p = exp2f(sc[s][g] - mn);
+          ls += p;
+#pragma unroll
+          for (int e = 0; e < VE; ++e) o[g][e] = fmaf(p, vf[s][e], o[g][e]);
+        }
+        l[g] = ls;
+        m[g] = mn;
+      }
+    }
+  }
+
+  // ---- merge the key-row groups of the wave
+#pragma unroll
+  for (int g = 0; g < GM; ++g) {
+    if (g < gcount) {
+      const float M = groups_max<LPR>(m[g]);
+      const float f = (M == -INFINITY) ? 0.f : exp2f(m[g] - M);
+      l[g] = groups_sum<LPR>(l[g] * f);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) o[g][e] = groups_sum<LPR>(o[g][e] * f);
+      m[g] = M;
+    }
+  }
+
+  // ---- merge the waves of the workgroup in LDS; the same buffer later
+  // stages the split partials
+  constexpr int kWaveFloats = NWMAX * GM * (D + 2);
+  constexpr int kStageFloats = kMergeRows * kPStride;
+  constexpr int kSmem = kWaveFloats > kStageFloats ? kWaveFloats : kStageFloats;
+  __shared__ __attribute__((aligned(16))) float smem[kSmem];
+  __shared__ int s_last;
+  float *sm_o = smem;                       // [nw][GM][D]
+  float *sm_m = smem + NWMAX * GM * D;  // [nw][GM]
+  float *sm_l = sm_m + NWMAX * GM;      // [nw][GM]
+  if (kr == 0) {
+#pragma unroll
+    for (int g = 0; g < GM; ++g) {
+      if (g < gcount) {
+#pragma unroll
+        for (int e = 0; e < VE; ++e) sm_o[(wave * GM + g) * D + ds * VE + e] = o[g][e];
+        if (ds == 0) {
+          sm_m[wave * GM + g] = m[g];
+          sm_l[wave * GM + g] = l[g];
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  const size_t tile_id = (size_t)unit * a.row_tiles + rt;
+  float *part = a.ws_part + (tile_id * a.splits + split) * GM * kPStride;
+  for (int idx = threadIdx.x; idx < GM * D; idx += blockDim.x) {
+    const int g = idx / D, d = idx % D;
+    if (g >= gcount) continue;
+    float mw[NWMAX];
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NWMAX; ++w) {
+      mw[w] = (w < nw) ? sm_m[w * GM + g] : -INFINITY;
+      M = fmaxf(M, mw[w]);
+    }
+    float Ls = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWMAX; ++w) {
+      if (w < nw && mw[w] != -INFINITY) {
+        const float f = exp2f(mw[w] - M);
+        Ls = fmaf(sm_l[w * GM + g], f, Ls);
+        O = fmaf(sm_o[(w * GM + g) * D + d], f, O);
+      }
+    }
+    if (a.splits == 1) {
+      const RowId r = row_id(a, bkv, hk, g0 + g);
+      a.out[((size_t)(r.b * a.Hq + r.h) * a.N + r.i) * D + d] = O / Ls;
+    } else {
+      publish(part + g * kPStride + d, O);
+      if (d == 0) {
+        publish(part + g * kPStride + D, M);
+        publish(part + g * kPStride + D + 1, Ls);
+      }
+    }
+  }
+  if (a.splits == 1) return;
+
+  // ---- arrival: the last workgroup of this (unit, row tile) merges
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = (arrive(&a.ws_count[tile_id]) == (uint32_t)(a.splits - 1)) ? 1 : 0;
+  __syncthreads();
+  if (!s_last) return;
+
+  // ---- last workgroup: stage every partial of the tile in LDS, all loads
+  // in flight at once, then combine in split order
+  const int n = a.splits * GM * kPStride;
+  const float *src = a.ws_part + tile_id * a.splits * GM * kPStride;
+  constexpr int kStageIters = stage_iters<NWMAX>();
+  uint32_t stage[kStageIters];
+#pragma unroll
+  for (int j = 0; j < kStageIters; ++j) {
+    const int i = threadIdx.x + j * blockDim.x;
+    if (i < n) stage[j] = fetch_u32(src + i);
+  }
+#pragma unroll
+  for (int j = 0; j < kStageIters; ++j) {
+    const int i = threadIdx.x + j * blockDim.x;
+    if (i < n) smem[i] = __builtin_bit_cast(float, stage[j]);
+  }
+  __syncthreads();
+  // wave 0: lane sp holds split sp's (m, l) of row g; the split weights and
+  // the row's normaliser go to LDS (splits <= 64 by the plan)
+  __shared__ float s_w[kMergeRows], s_inv[GM];
+  if (wave == 0) {
+    for (int g = 0; g < gcount; ++g) {
+      const bool on = lane < a.splits;
+      const float ms = on ? smem[(lane * GM + g) * kPStride + D] : -INFINITY;
+      const float ls = on ? smem[(lane * GM + g) * kPStride + D + 1] : 0.f;
+      const float M = groups_max<1>(ms);
+      const float w = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+      const float L = groups_sum<1>(ls * w);
+      if (on) s_w[lane * GM + g] = w;
+      if (lane == 0) s_inv[g] = 1.f / L;
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < GM * D; idx += blockDim.x) {
+    const int g = idx / D, d = idx % D;
+    if (g >= gcount) continue;
+    float O = 0.f;
+#pragma unroll 8
+    for (int sp = 0; sp < a.splits; ++sp)
+      O = fmaf(smem[(sp * GM + g) * kPStride + d], s_w[sp * GM + g], O);
+    const RowId r = row_id(a, bkv, hk, g0 + g);
+    a.out[((size_t)(r.b * a.Hq + r.h) * a.N + r.i) * D + d] = O * s_inv[g];
+  }
+  if (threadIdx.x == 0) reset_counter(&a.ws_count[tile_id]);
+}
+
+template <int DT, bool FUSED, bool ROPE>
+void launch_gm(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
+  switch (a.gm) {
+    case 1: hipLaunchKernelGGL((attn_kernel<DT, 1, FUSED, 4, ROPE>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((attn_kernel<DT, 2, FUSED, 4, ROPE>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((attn_kernel<DT, 4, FUSED, 4, ROPE>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((attn_kernel<DT, 8, FUSED, 4, ROPE>), grid, block, 0, s, a); break;
+  }
+}
+
+// The 16-wave variant (one wide workgroup per unit): at most 2 query rows and
+// no rotary work, so that it fits 128 registers without spilling.
+template <int DT, bool FUSED>
+void launch_wide(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
+  if (a.gm == 1) hipLaunchKernelGGL((attn_kernel<DT, 1, FUSED, kMaxWaves, false>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((attn_kernel<DT, 2, FUSED, kMaxWaves, false>), grid, block, 0, s, a);
+}
+
+template <int DT, bool FUSED>
+void launch_dt(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
+  if (a.waves > 4) launch_wide<DT, FUSED>(a, grid, block, s);
+  else if (a.rope_base > 0.f) launch_gm<DT, FUSED, true>(a, grid, block, s);
+  else launch_gm<DT, FUSED, false>(a, grid, block, s);
+}
+
+int env_int(const char *name, int dflt) {
+  const char *v = getenv(name);
+  return (v && *v) ? atoi(v) : dflt;
+}
+
+}  // namespace
+
+hipError_t launch_attn(int dtype, const AttnArgs &a, hipStream_t s) {
+  const dim3 grid(a.splits, a.row_tiles, a.Bkv * a.Hkv);
+  const dim3 block(64 * a.waves);
+  const bool fused = a.k_new != nullptr;
+  switch (dtype) {
+    case F32: fused ? launch_dt<F32, true>(a, grid, block, s) : launch_dt<F32, false>(a, grid, block, s); break;
+    case F16: fused ? launch_dt<F16, true>(a, grid, block, s) : launch_dt<F16, false>(a, grid, block, s); break;
+    default: fused ? launch_dt<BF16, true>(a, grid, block, s) : launch_dt<BF16, false>(a, grid, block, s); break;
+  }
+  return hipGetLastError();
+}
+
+// Split plan: a pure function of the shape (and of the tuning variables
+// KVD_ATTN_WAVES / KVD_ATTN_TARGET_WGS / KVD_ATTN_CHUNK when set), so results
+// are reproducible run to run.
+AttnPlan plan_attn(int dtype, int units, int G, int L, bool rope) {
+  AttnPlan p{};
+  p.gm = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
+  p.row_tiles = (G + p.gm - 1) / p.gm;
+  p.waves = env_int("KVD_ATTN_WAVES", 4);
+  if (p.waves != 1 && p.waves != 2 && p.waves != 4 && p.waves != kMaxWaves) p.waves = 4;
+  if (p.waves > 4 && (p.gm > 2 || rope)) p.waves = 4;  // what the wide variant supports
+  const int tile = (dtype == F32) ? AttnGeom<F32>::TILE : AttnGeom<F16>::TILE;
+  const int min_chunk = tile * p.waves;
+  const int max_splits = kMergeRows / p.gm < 64 ? kMergeRows / p.gm : 64;
+  const int per_split = units * p.row_tiles;
+  int target_wgs = env_int("KVD_ATTN_TARGET_WGS", 512);
+  if (target_wgs < 1 || target_wgs > kMaxCounters) target_wgs = 512;
+  int want = (target_wgs + per_split - 1) / per_split;
+  want = want < 1 ? 1 : (want > max_splits ? max_splits : want);
+  int chunk = (L + want - 1) / want;
+  const int forced = env_int("KVD_ATTN_CHUNK", 0);
+  if (forced > 0) chunk = forced;
+  chunk = ((chunk + min_chunk - 1) / min_chunk) * min_chunk;
+  if (chunk < min_chunk) chunk = min_chunk;
+  p.chunk = chunk;
+  p.splits = (L + chunk - 1) / chunk;
+  const size_t tiles = (size_t)units * p.row_tiles;
+  if (p.splits > max_splits || (p.splits > 1 && tiles > (size_t)kMaxCounters)) {
+    // too many partials to merge or count: fall back to the widest chunks
+    p.chunk = (((L + max_splits - 1) / max_splits + min_chunk - 1) / min_chunk) * min_chunk;
+    p.splits = (L + p.chunk - 1) / p.chunk;
+    if (tiles > (size_t)kMaxCounters) {
+      p.chunk = ((L + min_chunk - 1) / min_chunk) * min_chunk;
+      p.splits = 1;
+    }
+  }
+  p.part_floats = (p.splits > 1) ? tiles * p.splits * p.gm * kPStride : 0;
+  p.counters = tiles;
+  return p;
+}
+
+}  // namespace kvd

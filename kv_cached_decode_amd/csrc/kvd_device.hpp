@@ -109,4 +109,167 @@ __device__ __forceinline__ void rope_rotate(float &lo, float &hi, float c, float
   hi = fmaf(h, c, l * s);
 }
 
+// ---------------------------------------------------------------------------
+// Cross-lane sums with DPP (no LDS round trip). Every lane of an aligned group
+// ends with the same bits: each step adds a value and its partner's value,
+// and IEEE addition is commutative.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRowMirror = 0x140;   // lane i <- lane 15-i within 16 lanes
+constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7-i within 8 lanes
+
+constexpr int kDppRowRor8 = 0x128;     // lane i <- lane (i + 8) mod 16 within 16 lanes
+constexpr int kSwizzleSwap16 = 0x401F; // ds_swizzle bit mode: lane i <- lane i ^ 16
+
+// Value of lane (this lane ^ 8), (^ 16), (^ 32) in a 64-lane wavefront.
+__device__ __forceinline__ float lane_xor8(float x) { return dpp_mov<kDppRowRor8>(x); }
+__device__ __forceinline__ float lane_xor16(float x) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), kSwizzleSwap16));
+}
+__device__ __forceinline__ float lane_xor32(float x) {
+  // v_permlane32_swap with both operands x: the first result holds x's upper
+  // half in lanes 32..63's place of the lower half and vice versa
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (threadIdx.x & 32) ? (unsigned)r[0] : (unsigned)r[1]);
+}
+
+// Reduce over the 64 / FROM aligned groups of FROM lanes (lanes that differ
+// only in the bits >= FROM): max or sum, every lane ends with the result.
+// (FROM = 1: the whole wavefront.)
+template <int FROM>
+__device__ __forceinline__ float groups_max(float x) {
+  if constexpr (FROM <= 1) x = fmaxf(x, dpp_mov<kDppQuadXor1>(x));
+  if constexpr (FROM <= 2) x = fmaxf(x, dpp_mov<kDppQuadXor2>(x));
+  if constexpr (FROM <= 4) x = fmaxf(x, dpp_mov<kDppHalfMirror>(x));
+  if constexpr (FROM <= 8) x = fmaxf(x, lane_xor8(x));
+  if constexpr (FROM <= 16) x = fmaxf(x, lane_xor16(x));
+  return fmaxf(x, lane_xor32(x));
+}
+template <int FROM>
+__device__ __forceinline__ float groups_sum(float x) {
+  if constexpr (FROM <= 1) x += dpp_mov<kDppQuadXor1>(x);
+  if constexpr (FROM <= 2) x += dpp_mov<kDppQuadXor2>(x);
+  if constexpr (FROM <= 4) x += dpp_mov<kDppHalfMirror>(x);
+  if constexpr (FROM <= 8) x += lane_xor8(x);
+  if constexpr (FROM <= 16) x += lane_xor16(x);
+  return x + lane_xor32(x);
+}
+
+template <int LANES> __device__ __forceinline__ float group_sum(float x);
+template <> __device__ __forceinline__ float group_sum<8>(float x) {
+  x += dpp_mov<kDppQuadXor1>(x);
+  x += dpp_mov<kDppQuadXor2>(x);
+  x += dpp_mov<kDppHalfMirror>(x);
+  return x;
+}
+template <> __device__ __forceinline__ float group_sum<16>(float x) {
+  x = group_sum<8>(x);
+  x += dpp_mov<kDppRowMirror>(x);
+  return x;
+}
+
+// The 16-byte slice `ds` of a query row rotated at position pos, in fp32
+// (queries are not stored, so they are not rounded): `partner` is slice
+// ds ^ (LPR/2) of the same row, the other half of every rotary pair.
+template <int DT>
+__device__ __forceinline__ void rope_slice_f32(u32x4 mine, u32x4 partner, int ds, int pos,
+                                               float base, float *x) {
+  constexpr int VE = vec_elems<DT>();
+  constexpr int LPR = kHeadDim / VE;
+  float p[VE];
+  unpack16<DT>(mine, x);
+  unpack16<DT>(partner, p);
+  const bool is_lo = ds < LPR / 2;
+#pragma unroll
+  for (int e = 0; e < VE; ++e) {
+    float c, s;
+    rope_cos_sin(pos, (ds % (LPR / 2)) * VE + e, base, c, s);
+    float lo = is_lo ? x[e] : p[e];
+    float hi = is_lo ? p[e] : x[e];
+    rope_rotate(lo, hi, c, s);
+    x[e] = is_lo ? lo : hi;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Handing small partial results from many workgroups to the last one to
+// arrive. The partials are written with agent-scope atomic stores, which go
+// through the caches that other XCDs cannot see; each thread waits for its
+// stores to complete before the workgroup barrier, and one thread then counts
+// the arrival with an agent-scope atomic. The last arriver reads the partials
+// back with agent-scope atomic loads, which bypass those caches too, and only
+// after its own count has returned. No L2 write-back or invalidate is needed
+// because the handed-over data never sits in a non-coherent cache.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void publish(float *p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t *>(p), __builtin_bit_cast(uint32_t, v),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void publish(int32_t *p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t fetch_u32(const void *p) {
+  return __hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Returns the arrival count before this one (call from one thread).
+__device__ __forceinline__ uint32_t arrive(uint32_t *counter) {
+  return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void reset_counter(uint32_t *counter) {
+  __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One rotary pair of 16-byte chunks of a new K/V row (chunk j in the first
+// half of the row, j + D/2 in the second), the key rotated at position pos
+// when base > 0, rounded to the storage type.
+struct PairChunks {
+  u32x4 klo, khi, vlo, vhi;
+};
+template <int DT>
+__device__ __forceinline__ PairChunks load_pair(const char *k_src, const char *v_src, int j,
+                                                int pos, float base) {
+  constexpr int VE = vec_elems<DT>();
+  constexpr int EB = Storage<DT>::bytes;
+  const int lo_off = j * VE * EB, hi_off = (kHeadDim / 2 + j * VE) * EB;
+  PairChunks c;
+  c.klo = load16(k_src + lo_off);
+  c.khi = load16(k_src + hi_off);
+  c.vlo = load16(v_src + lo_off);
+  c.vhi = load16(v_src + hi_off);
+  if (base > 0.f) {
+    float lo[VE], hi[VE];
+    unpack16<DT>(c.klo, lo);
+    unpack16<DT>(c.khi, hi);
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+      float cs, sn;
+      rope_cos_sin(pos, j * VE + e, base, cs, sn);
+      rope_rotate(lo[e], hi[e], cs, sn);
+    }
+    c.klo = pack16<DT>(lo);
+    c.khi = pack16<DT>(hi);
+  }
+  return c;
+}
+template <int DT>
+__device__ __forceinline__ void store_pair(char *k_dst, char *v_dst, int j, const PairChunks &c) {
+  constexpr int VE = vec_elems<DT>();
+  constexpr int EB = Storage<DT>::bytes;
+  const int lo_off = j * VE * EB, hi_off = (kHeadDim / 2 + j * VE) * EB;
+  store16(k_dst + lo_off, c.klo);
+  store16(k_dst + hi_off, c.khi);
+  store16(v_dst + lo_off, c.vlo);
+  store16(v_dst + hi_off, c.vhi);
+}
+
 }  // namespace kvd

@@ -14,6 +14,11 @@ constexpr int kHeadDim = 64;
 
 // Arrival counters at the start of every workspace (one per merged tile).
 constexpr int kMaxCounters = 4096;
+// decode_step_self: new rows appended inside the attention launch (more are
+// appended by a separate kv_append launch first).
+constexpr int kMaxFusedRows = 16;
+// verify_accept: (value, index) pairs one batch row may stage for its merge.
+constexpr int kMaxVerifyPartials = 2048;
 
 struct AppendArgs {
   void *k_cache, *v_cache;       // [B][H][S_max][D]
@@ -35,16 +40,18 @@ struct ReorderArgs {
 // j the head within the group and i the query.
 struct AttnArgs {
   const void *q;                 // [B][Hq][N][D]
-  const void *k, *v;             // [Bkv][Hkv][S_max][D]
+  void *k, *v;                   // [Bkv][Hkv][S_max][D]
+  const void *k_new, *v_new;     // [Bkv][Hkv][T_new][D] rows appended in this launch, or null
   float *out;                    // [B][Hq][N][D]
-  float *ws_part;                // partial (m, l, o) per split
+  float *ws_part;                // partial (o, m, l) per split
   uint32_t *ws_count;            // arrival counters, one per (unit, row tile)
   int B, Hq, N, Bkv, Hkv, group, S_max;
   int G;                         // query rows per unit
   int L;                         // keys: len (self) or frames (cross)
   int causal_base;               // self: len - N; cross: -1 (no mask)
+  int new_base, T_new;           // new rows sit at [new_base, new_base + T_new); INT_MAX: none
   float scale_log2;              // scale * log2(e)
-  float rope_base;               // > 0: rotate q at causal_base + i
+  float rope_base;               // > 0: rotate q at causal_base + i (and new keys)
   // plan
   int chunk;                     // keys per workgroup
   int splits;                    // workgroups per (unit, row tile)
@@ -71,7 +78,7 @@ struct AttnPlan {
   int gm, row_tiles, chunk, splits, waves;
   size_t part_floats, counters;
 };
-AttnPlan plan_attn(int dtype, int units, int G, int L);
+AttnPlan plan_attn(int dtype, int units, int G, int L, bool rope);
 
 void plan_verify(int B, int R, int V, int &chunk, int &chunks);
 

@@ -18,7 +18,7 @@ def lib():
 
 def test_header_declares_the_five_calls_and_helpers():
     names = kb.declared_functions()
-    for n in ("kv_append", "kv_reorder", "decode_attn_self", "decode_attn_cross",
+    for n in ("kv_append", "kv_reorder", "decode_attn_self", "decode_step_self", "decode_attn_cross",
               "verify_accept", "kvd_attn_workspace_bytes", "kvd_verify_workspace_bytes",
               "kvd_status_string"):
         assert n in names
@@ -82,6 +82,11 @@ def test_decode_attn_validation(lib):
     # a long cache needs split partials: no or too small a workspace is refused
     assert s(FAKE, 20, 1, ctypes.byref(c), 448, 0.125, 0.0, FAKE, None, 0, None) == -6
     assert s(FAKE, 20, 1, ctypes.byref(c), 448, 0.125, 0.0, FAKE, ws, 64, None) == -6
+    st = lib.decode_step_self
+    assert st(FAKE, None, FAKE, 20, 1, ctypes.byref(c), 10, 0.125, 0.0, FAKE, ws, 1 << 30, None) == -1
+    assert st(FAKE, FAKE, FAKE, 20, 1, ctypes.byref(c), 449, 0.125, 0.0, FAKE, ws, 1 << 30, None) == -4
+    assert st(FAKE, FAKE, MIS, 20, 1, ctypes.byref(c), 10, 0.125, 0.0, FAKE, ws, 1 << 30, None) == -7
+    assert st(FAKE, FAKE, MIS, 20, 40, ctypes.byref(c), 100, 0.125, 0.0, FAKE, ws, 1 << 30, None) == -7
     x = lib.decode_attn_cross
     xc = _cache(B=1, S=1500)
     assert x(FAKE, 5, 20, 1, ctypes.byref(xc), 1501, 0.125, FAKE, ws, 1 << 30, None) == -4

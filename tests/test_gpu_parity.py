@@ -408,3 +408,45 @@ def test_cross_cache_per_row_and_shared_agree():
     ox = O.ConcatCache(1, 6, 64, "f16"); ox.set_once(xk, xv)
     ref = O.attend_cross(q, ox, 0.125)
     assert max_err(a, ref) <= TOL["f16"] and max_err(b, ref) <= TOL["f16"]
+
+
+# --------------------------------------------------- fused append + attend ----
+
+@pytest.mark.parametrize("dtype,B,Hq,Hkv,N,L,rope", [
+    ("f16", 1, 20, 20, 1, 1, 0.0),          # first token
+    ("f16", 1, 20, 20, 1, 300, 0.0),        # whisper decode step
+    ("f16", 1, 20, 20, 5, 133, 0.0),        # verify block across a split boundary
+    ("bf16", 8, 9, 3, 1, 700, 10000.0),     # GQA decode with rotary keys
+    ("bf16", 8, 9, 3, 16, 530, 10000.0),    # largest fused block
+    ("bf16", 2, 9, 3, 40, 100, 10000.0),    # long block: append then attend
+    ("f32", 2, 4, 4, 3, 70, 10000.0),
+])
+def test_step_self_equals_append_then_attend(dtype, B, Hq, Hkv, N, L, rope):
+    """decode_step_self leaves the cache exactly as kv_append does and returns
+    decode_attn_self's output, and both match the oracle."""
+    say(f"case: step_self {dtype} B={B} Hq={Hq} Hkv={Hkv} N={N} L={L} rope={rope}")
+    g = np.random.default_rng(L * 7 + N)
+    S = L + 3
+    k_all = O.narrow(g.standard_normal((B, Hkv, L, 64)), dtype)
+    v_all = O.narrow(g.standard_normal((B, Hkv, L, 64)), dtype)
+    q = O.narrow(g.standard_normal((B, Hq, N, 64)), dtype)
+    old, new = slice(0, L - N), slice(L - N, L)
+    ws = _ws()
+    c1 = kb.Cache(B, Hkv, S, TORCH_DTYPE[dtype])
+    c2 = kb.Cache(B, Hkv, S, TORCH_DTYPE[dtype])
+    if L > N:
+        for c in (c1, c2):
+            kb.kv_append(c, to_dev(k_all[:, :, old], dtype), to_dev(v_all[:, :, old], dtype), 0, rope)
+    kb.kv_append(c1, to_dev(k_all[:, :, new], dtype), to_dev(v_all[:, :, new], dtype), L - N, rope)
+    o1 = kb.decode_attn_self(to_dev(q, dtype), c1, L, 0.125, rope_base=rope, ws=ws)
+    o2 = kb.decode_step_self(to_dev(q, dtype), to_dev(k_all[:, :, new], dtype),
+                             to_dev(v_all[:, :, new], dtype), c2, L, 0.125, rope_base=rope, ws=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(from_dev(c1.k, dtype)), bits(from_dev(c2.k, dtype)))
+    assert np.array_equal(bits(from_dev(c1.v, dtype)), bits(from_dev(c2.v, dtype)))
+    assert torch.equal(o1, o2)
+    oc = O.ConcatCache(B, Hkv, 64, dtype)
+    if L > N:
+        oc.append(k_all[:, :, old], v_all[:, :, old], rope)
+    oc.append(k_all[:, :, new], v_all[:, :, new], rope)
+    assert max_err(o2, O.attend_self(q, oc, 0.125, rope_base=rope)) <= TOL[dtype]
