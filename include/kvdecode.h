@@ -175,8 +175,10 @@ int verify_accept(const void *logits, int32_t logits_dtype, int32_t B, int32_t R
                   int32_t *accept_len, int32_t *next_token, void *ws,
                   size_t ws_bytes, void *stream);
 
-/* Workspace sizes (bytes) for the calls above; 0 for invalid sizes. A
- * workspace sized for the largest len (or frames) serves every smaller one. */
+/* Workspace sizes (bytes) for the calls above: 0 for invalid sizes, and 0
+ * when no call of that shape merges split partials (a NULL workspace is then
+ * accepted). A workspace sized for the largest len (or frames) serves every
+ * smaller one. */
 size_t kvd_attn_workspace_bytes(int32_t B, int32_t Hq, int32_t N, int32_t len_max);
 size_t kvd_verify_workspace_bytes(int32_t B, int32_t R, int32_t V);
 

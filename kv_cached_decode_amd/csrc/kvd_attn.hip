@@ -419,40 +419,51 @@ hipError_t launch_attn(int dtype, const AttnArgs &a, hipStream_t s) {
 }
 
 // Split plan: a pure function of the shape (and of the tuning variables
-// KVD_ATTN_WAVES / KVD_ATTN_TARGET_WGS / KVD_ATTN_CHUNK when set), so results
-// are reproducible run to run.
+// KVD_ATTN_WAVES / KVD_ATTN_CHUNK when set), so results are reproducible run
+// to run. The numbers come from timing the kernel on MI355X: a CU keeps about
+// 55 KB of loads in flight, so a unit's keys are split when they exceed about
+// 128 KB (each workgroup then takes about 64 KB, one round of loads); below
+// that, one workgroup per unit avoids the cross-workgroup merge, which costs
+// three memory round trips.
 AttnPlan plan_attn(int dtype, int units, int G, int L, bool rope) {
   AttnPlan p{};
   p.gm = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
   p.row_tiles = (G + p.gm - 1) / p.gm;
-  p.waves = env_int("KVD_ATTN_WAVES", 4);
-  if (p.waves != 1 && p.waves != 2 && p.waves != 4 && p.waves != kMaxWaves) p.waves = 4;
-  if (p.waves > 4 && (p.gm > 2 || rope)) p.waves = 4;  // what the wide variant supports
   const int tile = (dtype == F32) ? AttnGeom<F32>::TILE : AttnGeom<F16>::TILE;
-  const int min_chunk = tile * p.waves;
-  const int max_splits = kMergeRows / p.gm < 64 ? kMergeRows / p.gm : 64;
-  const int per_split = units * p.row_tiles;
-  int target_wgs = env_int("KVD_ATTN_TARGET_WGS", 512);
-  if (target_wgs < 1 || target_wgs > kMaxCounters) target_wgs = 512;
-  int want = (target_wgs + per_split - 1) / per_split;
-  want = want < 1 ? 1 : (want > max_splits ? max_splits : want);
-  int chunk = (L + want - 1) / want;
+  const int key_bytes = 2 * kHeadDim * ((dtype == F32) ? 4 : 2);  // K + V row
+  const long unit_bytes = (long)L * key_bytes;
+  const size_t tiles = (size_t)units * p.row_tiles;
+  const bool wide_ok = p.gm <= 2 && !rope;
+
+  int waves = 4, chunk;
+  if (tiles >= 256 || unit_bytes <= 128 * 1024) {
+    chunk = L;  // one workgroup per (unit, row tile)
+    if (tiles < 256 && unit_bytes > 64 * 1024 && wide_ok) waves = kMaxWaves;
+  } else {
+    chunk = (64 * 1024) / key_bytes;
+  }
+  const int env_waves = env_int("KVD_ATTN_WAVES", 0);
+  if (env_waves == 1 || env_waves == 2 || env_waves == 4 || (env_waves == kMaxWaves && wide_ok))
+    waves = env_waves;
   const int forced = env_int("KVD_ATTN_CHUNK", 0);
   if (forced > 0) chunk = forced;
+  p.waves = waves;
+
+  const int min_chunk = tile * waves;
+  const int max_splits = kMergeRows / p.gm < 64 ? kMergeRows / p.gm : 64;
   chunk = ((chunk + min_chunk - 1) / min_chunk) * min_chunk;
   if (chunk < min_chunk) chunk = min_chunk;
-  p.chunk = chunk;
-  p.splits = (L + chunk - 1) / chunk;
-  const size_t tiles = (size_t)units * p.row_tiles;
-  if (p.splits > max_splits || (p.splits > 1 && tiles > (size_t)kMaxCounters)) {
-    // too many partials to merge or count: fall back to the widest chunks
-    p.chunk = (((L + max_splits - 1) / max_splits + min_chunk - 1) / min_chunk) * min_chunk;
-    p.splits = (L + p.chunk - 1) / p.chunk;
-    if (tiles > (size_t)kMaxCounters) {
-      p.chunk = ((L + min_chunk - 1) / min_chunk) * min_chunk;
-      p.splits = 1;
-    }
+  int splits = (L + chunk - 1) / chunk;
+  if (splits > max_splits) {  // too many partials to stage: widen the chunks
+    chunk = (((L + max_splits - 1) / max_splits + min_chunk - 1) / min_chunk) * min_chunk;
+    splits = (L + chunk - 1) / chunk;
   }
+  if (splits > 1 && tiles > (size_t)kMaxCounters) {  // one counter per tile
+    chunk = ((L + min_chunk - 1) / min_chunk) * min_chunk;
+    splits = 1;
+  }
+  p.chunk = chunk;
+  p.splits = splits;
   p.part_floats = (p.splits > 1) ? tiles * p.splits * p.gm * kPStride : 0;
   p.counters = tiles;
   return p;

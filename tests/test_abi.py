@@ -80,8 +80,9 @@ def test_decode_attn_validation(lib):
     assert s(FAKE, 20, 1, ctypes.byref(c), 10, float("nan"), 0.0, FAKE, ws, 1 << 30, None) == -2
     assert s(MIS, 20, 1, ctypes.byref(c), 10, 0.125, 0.0, FAKE, ws, 1 << 30, None) == -7
     # a long cache needs split partials: no or too small a workspace is refused
-    assert s(FAKE, 20, 1, ctypes.byref(c), 448, 0.125, 0.0, FAKE, None, 0, None) == -6
-    assert s(FAKE, 20, 1, ctypes.byref(c), 448, 0.125, 0.0, FAKE, ws, 64, None) == -6
+    long_c = _cache(S=1500)
+    assert s(FAKE, 20, 1, ctypes.byref(long_c), 1500, 0.125, 0.0, FAKE, None, 0, None) == -6
+    assert s(FAKE, 20, 1, ctypes.byref(long_c), 1500, 0.125, 0.0, FAKE, ws, 64, None) == -6
     st = lib.decode_step_self
     assert st(FAKE, None, FAKE, 20, 1, ctypes.byref(c), 10, 0.125, 0.0, FAKE, ws, 1 << 30, None) == -1
     assert st(FAKE, FAKE, FAKE, 20, 1, ctypes.byref(c), 449, 0.125, 0.0, FAKE, ws, 1 << 30, None) == -4
@@ -110,8 +111,9 @@ def test_verify_accept_validation(lib):
 
 
 def test_workspace_sizes(lib):
-    # short caches need no split partials beyond the counter block
-    assert kb.attn_workspace_bytes(1, 20, 1, 448) > 16384
+    # a 1500-key cache is split, a 40-key one is not (the counter block only)
+    assert kb.attn_workspace_bytes(1, 20, 1, 1500) > 16384
+    assert kb.attn_workspace_bytes(1, 20, 1, 40) == 0
     assert kb.attn_workspace_bytes(1, 20, 1, 1500) >= kb.attn_workspace_bytes(1, 20, 1, 448)
     assert kb.attn_workspace_bytes(0, 20, 1, 448) == 0
     assert kb.verify_workspace_bytes(1, 5, 51865) > 16384

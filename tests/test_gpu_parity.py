@@ -108,15 +108,28 @@ def test_whisper_greedy_sweep_lengths(layer):
     say(f"whisper layer {layer}: worst max|err| {worst:.2e}")
 
 
+# Plans forced through the tuning variables, so that split boundaries and the
+# wide (16-wave) variant are covered at lengths the default plan runs unsplit.
+PLANS = {"default": {}, "chunk128": {"KVD_ATTN_CHUNK": "128"},
+         "wide": {"KVD_ATTN_WAVES": "16"}, "wide_chunk512": {"KVD_ATTN_WAVES": "16", "KVD_ATTN_CHUNK": "512"}}
+
+
+@pytest.fixture(params=list(PLANS))
+def plan(request, monkeypatch):
+    for k, v in PLANS[request.param].items():
+        monkeypatch.setenv(k, v)
+    return request.param
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("N", [1, 5])
-@pytest.mark.parametrize("L", [5, 64, 129, 130, 133, 257, 448])
-def test_sentinel_mask(dtype, N, L):
+@pytest.mark.parametrize("L", [5, 64, 129, 130, 133, 257, 448, 1100])
+def test_sentinel_mask(dtype, N, L, plan):
     """Query i's own key and the next key (one it must not see) both align
     with it; one-hot values name every key that got weight."""
     if L < N:
         pytest.skip("len < N")
-    say(f"case: sentinel dtype={dtype} N={N} L={L}")
+    say(f"case: sentinel dtype={dtype} N={N} L={L} plan={plan}")
     g = np.random.default_rng(100 + L + N)
     H, D = 4, 64
     k = g.standard_normal((1, H, L, D)) * 0.05
@@ -143,9 +156,9 @@ def test_sentinel_mask(dtype, N, L):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_large_scores_online_rescale(dtype):
+def test_large_scores_online_rescale(dtype, plan):
     """Scores with sd ~ 16: the running max changes often inside a split."""
-    say(f"case: large scores {dtype}")
+    say(f"case: large scores {dtype} plan={plan}")
     g = np.random.default_rng(5)
     B, H, L, N = 2, 8, 700, 3
     k = O.narrow(g.standard_normal((B, H, L, 64)) * 4, dtype)
