@@ -182,6 +182,12 @@ int verify_accept(const void *logits, int32_t logits_dtype, int32_t B, int32_t R
 size_t kvd_attn_workspace_bytes(int32_t B, int32_t Hq, int32_t N, int32_t len_max);
 size_t kvd_verify_workspace_bytes(int32_t B, int32_t R, int32_t V);
 
+/* Profiling aid: the next kernel launch made by the calling thread records
+ * `start_event` when the kernel begins and `stop_event` when it ends (created
+ * hipEvent_t handles, or NULL), so hipEventElapsedTime gives the kernel's own
+ * duration without launch gaps. The request is consumed by that one launch. */
+int kvd_time_next_launch(void *start_event, void *stop_event);
+
 /* Static text for a status code (never NULL). */
 const char *kvd_status_string(int status);
 

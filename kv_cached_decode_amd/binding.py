@@ -54,6 +54,7 @@ _SIGNATURES = {
     "kvd_attn_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32]),
     "kvd_verify_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
     "kvd_status_string": (ctypes.c_char_p, [c_int]),
+    "kvd_time_next_launch": (c_int, [c_void_p, c_void_p]),
 }
 
 
@@ -146,6 +147,13 @@ class Cache:
             self._desc = KvdCache(_dev(self.k, "cache.k"), _dev(self.v, "cache.v"),
                                   B, H, S, D, DTYPE_CODE[self.k.dtype])
         return self._desc
+
+
+def time_next_launch(start: "torch.cuda.Event", stop: "torch.cuda.Event"):
+    """The next kernel launch of this thread records `start` at kernel begin
+    and `stop` at kernel end (both events must have been recorded once, which
+    creates them)."""
+    _check("kvd_time_next_launch", lib().kvd_time_next_launch(start.cuda_event, stop.cuda_event))
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:

@@ -64,9 +64,23 @@ int prepare_attn(AttnArgs &a, int dtype, void *ws, size_t ws_bytes) {
   return KVD_OK;
 }
 
+thread_local kvd::LaunchTiming g_next_timing;
+
 }  // namespace
 
+kvd::LaunchTiming kvd::take_launch_timing() {
+  const LaunchTiming t = g_next_timing;
+  g_next_timing = LaunchTiming{};
+  return t;
+}
+
 extern "C" {
+
+int kvd_time_next_launch(void *start_event, void *stop_event) {
+  g_next_timing.start = static_cast<hipEvent_t>(start_event);
+  g_next_timing.stop = static_cast<hipEvent_t>(stop_event);
+  return KVD_OK;
+}
 
 const char *kvd_status_string(int status) {
   switch (status) {

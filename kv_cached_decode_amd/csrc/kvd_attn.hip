@@ -377,10 +377,10 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
 template <int DT, bool FUSED, bool ROPE>
 void launch_gm(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
   switch (a.gm) {
-    case 1: hipLaunchKernelGGL((attn_kernel<DT, 1, FUSED, 4, ROPE>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((attn_kernel<DT, 2, FUSED, 4, ROPE>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((attn_kernel<DT, 4, FUSED, 4, ROPE>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((attn_kernel<DT, 8, FUSED, 4, ROPE>), grid, block, 0, s, a); break;
+    case 1: launch_kernel(attn_kernel<DT, 1, FUSED, 4, ROPE>, grid, block, s, a); break;
+    case 2: launch_kernel(attn_kernel<DT, 2, FUSED, 4, ROPE>, grid, block, s, a); break;
+    case 4: launch_kernel(attn_kernel<DT, 4, FUSED, 4, ROPE>, grid, block, s, a); break;
+    default: launch_kernel(attn_kernel<DT, 8, FUSED, 4, ROPE>, grid, block, s, a); break;
   }
 }
 
@@ -388,8 +388,8 @@ void launch_gm(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
 // no rotary work, so that it fits 128 registers without spilling.
 template <int DT, bool FUSED>
 void launch_wide(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
-  if (a.gm == 1) hipLaunchKernelGGL((attn_kernel<DT, 1, FUSED, kMaxWaves, false>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((attn_kernel<DT, 2, FUSED, kMaxWaves, false>), grid, block, 0, s, a);
+  if (a.gm == 1) launch_kernel(attn_kernel<DT, 1, FUSED, kMaxWaves, false>, grid, block, s, a);
+  else launch_kernel(attn_kernel<DT, 2, FUSED, kMaxWaves, false>, grid, block, s, a);
 }
 
 template <int DT, bool FUSED>

@@ -89,9 +89,9 @@ hipError_t launch_append(int dtype, const AppendArgs &a, hipStream_t s) {
   const long total = (long)a.B * a.H * a.T * (kHeadDim / 2 / ve);
   const dim3 grid((unsigned)((total + kThreads - 1) / kThreads));
   switch (dtype) {
-    case F32: hipLaunchKernelGGL((append_kernel<F32>), grid, dim3(kThreads), 0, s, a); break;
-    case F16: hipLaunchKernelGGL((append_kernel<F16>), grid, dim3(kThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL((append_kernel<BF16>), grid, dim3(kThreads), 0, s, a); break;
+    case F32: launch_kernel(append_kernel<F32>, grid, dim3(kThreads), s, a); break;
+    case F16: launch_kernel(append_kernel<F16>, grid, dim3(kThreads), s, a); break;
+    default: launch_kernel(append_kernel<BF16>, grid, dim3(kThreads), s, a); break;
   }
   return hipGetLastError();
 }
@@ -102,9 +102,9 @@ hipError_t launch_reorder(int dtype, const ReorderArgs &a, hipStream_t s) {
   const long total = (long)a.H * a.len * vpr;
   const dim3 grid((unsigned)((total + kThreads - 1) / kThreads));
   switch (dtype) {
-    case F32: hipLaunchKernelGGL((reorder_kernel<F32>), grid, dim3(kThreads), 0, s, a); break;
-    case F16: hipLaunchKernelGGL((reorder_kernel<F16>), grid, dim3(kThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL((reorder_kernel<BF16>), grid, dim3(kThreads), 0, s, a); break;
+    case F32: launch_kernel(reorder_kernel<F32>, grid, dim3(kThreads), s, a); break;
+    case F16: launch_kernel(reorder_kernel<F16>, grid, dim3(kThreads), s, a); break;
+    default: launch_kernel(reorder_kernel<BF16>, grid, dim3(kThreads), s, a); break;
   }
   return hipGetLastError();
 }

@@ -2,6 +2,7 @@
 // and the kernel launchers. Nothing here is exported.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -81,6 +82,26 @@ struct AttnPlan {
 AttnPlan plan_attn(int dtype, int units, int G, int L, bool rope);
 
 void plan_verify(int B, int R, int V, int &chunk, int &chunks);
+
+// Events a caller asked the next launch of this thread to record (kernel
+// begin / end); taken and cleared by that launch.
+struct LaunchTiming {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchTiming take_launch_timing();
+
+// Every kernel of the library is launched through here.
+template <typename... Args>
+inline void launch_kernel(void (*kernel)(Args...), dim3 grid, dim3 block, hipStream_t s,
+                          Args... args) {
+  void *argv[] = {static_cast<void *>(&args)...};
+  const LaunchTiming t = take_launch_timing();
+  if (t.start || t.stop)
+    (void)hipExtLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, argv, 0, s,
+                             t.start, t.stop, 0);
+  else
+    (void)hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, argv, 0, s);
+}
 
 hipError_t launch_append(int dtype, const AppendArgs &a, hipStream_t s);
 hipError_t launch_reorder(int dtype, const ReorderArgs &a, hipStream_t s);

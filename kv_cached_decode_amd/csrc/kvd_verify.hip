@@ -153,9 +153,9 @@ void plan_verify(int B, int R, int V, int &chunk, int &chunks) {
 hipError_t launch_verify(const VerifyArgs &a, hipStream_t s) {
   const dim3 grid(a.chunks, a.R, a.B);
   switch (a.dtype) {
-    case F32: hipLaunchKernelGGL((verify_kernel<F32>), grid, dim3(kThreads), 0, s, a); break;
-    case F16: hipLaunchKernelGGL((verify_kernel<F16>), grid, dim3(kThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL((verify_kernel<BF16>), grid, dim3(kThreads), 0, s, a); break;
+    case F32: launch_kernel(verify_kernel<F32>, grid, dim3(kThreads), s, a); break;
+    case F16: launch_kernel(verify_kernel<F16>, grid, dim3(kThreads), s, a); break;
+    default: launch_kernel(verify_kernel<BF16>, grid, dim3(kThreads), s, a); break;
   }
   return hipGetLastError();
 }
