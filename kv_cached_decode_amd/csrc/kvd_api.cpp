@@ -43,13 +43,15 @@ size_t attn_bytes(const AttnPlan &p) { return kCounterBytes + p.part_floats * si
 // Fill the plan-dependent fields and the workspace pointers.
 int prepare_attn(AttnArgs &a, int dtype, void *ws, size_t ws_bytes) {
   const int units = a.Bkv * a.Hkv;
-  const AttnPlan p = kvd::plan_attn(dtype, units, a.G, a.L, a.rope_base > 0.f);
+  const AttnPlan p = kvd::plan_attn(dtype, units, a.G, a.N, a.L, a.rope_base > 0.f);
   if (p.row_tiles > 65535 || units > 65535) return KVD_ERR_SHAPE;  // grid limits
   a.chunk = p.chunk;
   a.splits = p.splits;
   a.row_tiles = p.row_tiles;
   a.waves = p.waves;
   a.gm = p.gm;
+  a.mfma = p.mfma;
+  a.rw = p.rw;
   if (p.splits > 1) {
     const size_t need = attn_bytes(p);
     if (!ws) return KVD_ERR_WORKSPACE;
@@ -269,7 +271,7 @@ size_t kvd_attn_workspace_bytes(int32_t B, int32_t Hq, int32_t N, int32_t len_ma
       const int G = (shared ? B : 1) * group * N;
       for (int dt = 0; dt < 2; ++dt) {
         for (int L = 1; L <= len_max; ++L) {
-          const AttnPlan p = kvd::plan_attn(dt == 0 ? kvd::F32 : kvd::F16, units, G, L, false);
+          const AttnPlan p = kvd::plan_attn(dt == 0 ? kvd::F32 : kvd::F16, units, G, N, L, false);
           if (p.splits > 1) {
             const size_t b = attn_bytes(p);
             if (b > best) best = b;

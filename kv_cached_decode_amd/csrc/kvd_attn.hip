@@ -21,6 +21,7 @@
 // need no ordering within the launch.
 #include <stdlib.h>
 
+#include "kvd_attn_common.hpp"
 #include "kvd_device.hpp"
 #include "kvd_internal.hpp"
 
@@ -28,14 +29,7 @@ namespace kvd {
 
 namespace {
 
-constexpr int kMaxWaves = 16;     // the wide variant: one workgroup of 1024 per unit
 constexpr int kSteps = 4;
-constexpr int kPStride = kHeadDim + 4;  // o[D], m, l, 2 pad floats: 16-byte rows
-constexpr int kMergeRows = 128;         // splits * rows per tile staged by the merge
-// staged floats per thread in the final merge, for 4- and 16-wave workgroups
-template <int NWMAX>
-constexpr int stage_iters() { return (kMergeRows * kPStride + 64 * NWMAX - 1) / (64 * NWMAX); }
-
 template <int DT>
 struct AttnGeom {
   static constexpr int VE = vec_elems<DT>();      // elements per lane load
@@ -44,21 +38,6 @@ struct AttnGeom {
   static constexpr int TILE = RPL * kSteps;       // keys per wave iteration
   static constexpr int ROWB = kHeadDim * Storage<DT>::bytes;
 };
-
-struct RowId {
-  int b, h, i;
-};
-
-// Query row gg of unit (bkv, hk): numbered (bl * group + j) * N + i.
-__device__ __forceinline__ RowId row_id(const AttnArgs &a, int bkv, int hk, int gg) {
-  RowId r;
-  r.i = gg % a.N;
-  const int j = (gg / a.N) % a.group;
-  const int bl = gg / (a.N * a.group);
-  r.b = (a.Bkv == 1) ? bl : bkv;
-  r.h = hk * a.group + j;
-  return r;
-}
 
 template <int DT, int GM, bool FUSED, int NWMAX, bool ROPE>
 __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
@@ -74,15 +53,7 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
   const int kr = lane / LPR;  // key row within a wave load
   const int ds = lane % LPR;  // dims [ds*VE, ds*VE + VE)
 
-  // every kernel argument the first loads depend on, fetched in one go (the
-  // empty asm keeps the compiler from sinking a fetch into a later branch,
-  // which would add a serial round trip before the first key load)
-  {
-    const int f0 = a.Hkv, f1 = a.S_max, f2 = a.G, f3 = a.L, f4 = a.N, f5 = a.group, f6 = a.Bkv,
-              f7 = a.causal_base, f8 = a.new_base, f9 = a.chunk, f10 = a.Hq, f11 = a.T_new;
-    asm volatile("" ::"s"(f0), "s"(f1), "s"(f2), "s"(f3), "s"(f4), "s"(f5), "s"(f6), "s"(f7),
-                 "s"(f8), "s"(f9), "s"(f10), "s"(f11), "s"(a.k), "s"(a.v), "s"(a.q));
-  }
+  hoist_args(a);
   const int split = blockIdx.x, rt = blockIdx.y, unit = blockIdx.z;
   const int bkv = unit / a.Hkv, hk = unit % a.Hkv;
   const int g0 = rt * GM;
@@ -268,7 +239,6 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
   constexpr int kStageFloats = kMergeRows * kPStride;
   constexpr int kSmem = kWaveFloats > kStageFloats ? kWaveFloats : kStageFloats;
   __shared__ __attribute__((aligned(16))) float smem[kSmem];
-  __shared__ int s_last;
   float *sm_o = smem;                       // [nw][GM][D]
   float *sm_m = smem + NWMAX * GM * D;  // [nw][GM]
   float *sm_l = sm_m + NWMAX * GM;      // [nw][GM]
@@ -321,57 +291,7 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
   }
   if (a.splits == 1) return;
 
-  // ---- arrival: the last workgroup of this (unit, row tile) merges
-  wait_stores();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = (arrive(&a.ws_count[tile_id]) == (uint32_t)(a.splits - 1)) ? 1 : 0;
-  __syncthreads();
-  if (!s_last) return;
-
-  // ---- last workgroup: stage every partial of the tile in LDS, all loads
-  // in flight at once, then combine in split order
-  const int n = a.splits * GM * kPStride;
-  const float *src = a.ws_part + tile_id * a.splits * GM * kPStride;
-  constexpr int kStageIters = stage_iters<NWMAX>();
-  uint32_t stage[kStageIters];
-#pragma unroll
-  for (int j = 0; j < kStageIters; ++j) {
-    const int i = threadIdx.x + j * blockDim.x;
-    if (i < n) stage[j] = fetch_u32(src + i);
-  }
-#pragma unroll
-  for (int j = 0; j < kStageIters; ++j) {
-    const int i = threadIdx.x + j * blockDim.x;
-    if (i < n) smem[i] = __builtin_bit_cast(float, stage[j]);
-  }
-  __syncthreads();
-  // wave 0: lane sp holds split sp's (m, l) of row g; the split weights and
-  // the row's normaliser go to LDS (splits <= 64 by the plan)
-  __shared__ float s_w[kMergeRows], s_inv[GM];
-  if (wave == 0) {
-    for (int g = 0; g < gcount; ++g) {
-      const bool on = lane < a.splits;
-      const float ms = on ? smem[(lane * GM + g) * kPStride + D] : -INFINITY;
-      const float ls = on ? smem[(lane * GM + g) * kPStride + D + 1] : 0.f;
-      const float M = groups_max<1>(ms);
-      const float w = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-      const float L = groups_sum<1>(ls * w);
-      if (on) s_w[lane * GM + g] = w;
-      if (lane == 0) s_inv[g] = 1.f / L;
-    }
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < GM * D; idx += blockDim.x) {
-    const int g = idx / D, d = idx % D;
-    if (g >= gcount) continue;
-    float O = 0.f;
-#pragma unroll 8
-    for (int sp = 0; sp < a.splits; ++sp)
-      O = fmaf(smem[(sp * GM + g) * kPStride + d], s_w[sp * GM + g], O);
-    const RowId r = row_id(a, bkv, hk, g0 + g);
-    a.out[((size_t)(r.b * a.Hq + r.h) * a.N + r.i) * D + d] = O * s_inv[g];
-  }
-  if (threadIdx.x == 0) reset_counter(&a.ws_count[tile_id]);
+  merge_splits<GM, NWMAX>(a, tile_id, g0, gcount, bkv, hk, smem);
 }
 
 template <int DT, bool FUSED, bool ROPE>
@@ -406,7 +326,53 @@ int env_int(const char *name, int dflt) {
 
 }  // namespace
 
+// Matrix-core tile plan (blocks of queries, 16-bit storage): 16-row tiles;
+// four tiles per workgroup and one split when there are enough tiles to fill
+// the chip (prefill), else one tile per workgroup with the 4 waves sharing
+// its keys and the keys split like the streaming kernel's.
+AttnPlan plan_attn_mfma(int units, int G, int L) {
+  constexpr int kRows = 16, kStep = 32;
+  AttnPlan p{};
+  p.mfma = 1;
+  p.gm = kRows;
+  p.waves = 4;
+  const int tiles16 = (G + kRows - 1) / kRows;
+  const long unit_bytes = (long)L * 2 * kHeadDim * 2;
+  const int forced = env_int("KVD_ATTN_CHUNK", 0);
+  if ((long)units * tiles16 >= 64 && forced <= 0) {
+    p.rw = 4;
+    p.row_tiles = (tiles16 + 3) / 4;
+    p.chunk = ((L + kStep - 1) / kStep) * kStep;
+    p.splits = 1;
+  } else {
+    p.rw = 1;
+    p.row_tiles = tiles16;
+    const int min_chunk = kStep * 4;
+    int chunk = (unit_bytes <= 128 * 1024) ? L : (64 * 1024) / (2 * kHeadDim * 2);
+    if (forced > 0) chunk = forced;
+    chunk = ((chunk + min_chunk - 1) / min_chunk) * min_chunk;
+    const int max_splits = kMergeRows / kRows;
+    int splits = (L + chunk - 1) / chunk;
+    if (splits > max_splits) {
+      chunk = (((L + max_splits - 1) / max_splits + min_chunk - 1) / min_chunk) * min_chunk;
+      splits = (L + chunk - 1) / chunk;
+    }
+    const size_t tiles = (size_t)units * p.row_tiles;
+    if (splits > 1 && tiles > (size_t)kMaxCounters) {
+      chunk = ((L + min_chunk - 1) / min_chunk) * min_chunk;
+      splits = 1;
+    }
+    p.chunk = chunk;
+    p.splits = splits;
+  }
+  const size_t tiles = (size_t)units * p.row_tiles;
+  p.part_floats = (p.splits > 1) ? tiles * p.splits * kRows * kPStride : 0;
+  p.counters = tiles;
+  return p;
+}
+
 hipError_t launch_attn(int dtype, const AttnArgs &a, hipStream_t s) {
+  if (a.mfma) return launch_attn_mfma(dtype, a, s);
   const dim3 grid(a.splits, a.row_tiles, a.Bkv * a.Hkv);
   const dim3 block(64 * a.waves);
   const bool fused = a.k_new != nullptr;
@@ -425,8 +391,10 @@ hipError_t launch_attn(int dtype, const AttnArgs &a, hipStream_t s) {
 // 128 KB (each workgroup then takes about 64 KB, one round of loads); below
 // that, one workgroup per unit avoids the cross-workgroup merge, which costs
 // three memory round trips.
-AttnPlan plan_attn(int dtype, int units, int G, int L, bool rope) {
+AttnPlan plan_attn(int dtype, int units, int G, int N, int L, bool rope) {
   AttnPlan p{};
+  const bool use_mfma = dtype != F32 && N > 1 && env_int("KVD_ATTN_MFMA", 1) != 0;
+  if (use_mfma) return plan_attn_mfma(units, G, L);
   p.gm = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
   p.row_tiles = (G + p.gm - 1) / p.gm;
   const int tile = (dtype == F32) ? AttnGeom<F32>::TILE : AttnGeom<F16>::TILE;

@@ -1,0 +1,333 @@
+// Decode attention for blocks of queries (N > 1: speculative verification,
+// prompt prefill) on gfx950 matrix cores, fp16/bf16 storage.
+//
+// Both products run on v_mfma_f32_16x16x32 in their transposed form, so every
+// lane works for a single query row:
+//   S^T = K Q^T    A = 16 keys x 32 dims (a lane: one key, 8 contiguous dims
+//                  = one 16-byte load), B = 32 dims x 16 query rows (a lane:
+//                  one row, 8 dims); lane l ends with the scores of row l%16
+//                  against keys 4*(l/16)+i of each 16-key tile.
+//   O^T = V^T P^T  B = P^T: exactly the 8 probabilities lane l already holds
+//                  (keys 4*(l/16)+i of the two 16-key tiles, taken in that
+//                  order as the contraction index); A = V^T for 16 output dims,
+//                  with the dims interleaved (dim 4c + t in row c of tile t)
+//                  so that lane l reads the 8 bytes [4c, 4c+4) of each of its
+//                  8 keys: 16 lanes cover a whole 128-byte V row. Lane l ends
+//                  with O[row l%16][16*(l/16) .. +16).
+// Softmax runs online per row in the log2 domain. P (and rotated queries) are
+// fed to the MFMA as a high and a low part in the storage type, so their
+// rounding stays far below the output tolerance; K, V and stored queries are
+// exact in the storage type already.
+//
+// A workgroup of 4 waves covers RW 16-row tiles: RW = 4 (prefill: each wave
+// its own rows, all keys of the chunk) or RW = 1 (verification: the 4 waves
+// share the rows and take every 4th 32-key step, merged in LDS). Splits over
+// keys are merged as in the streaming kernel.
+#include <stdlib.h>
+
+#include "kvd_attn_common.hpp"
+#include "kvd_device.hpp"
+#include "kvd_internal.hpp"
+
+namespace kvd {
+
+namespace {
+
+constexpr int kRows = 16;     // query rows per MFMA tile
+constexpr int kStep = 32;     // keys per MFMA step
+constexpr int kWaves = 4;
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int DT>
+__device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (DT == F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// x as a high and a low part in the storage type: hi = round(x), lo = round(x - hi).
+template <int DT>
+__device__ __forceinline__ void split_hi_lo(const float *x, u32x4 &hi, u32x4 &lo) {
+  float h[8], r[8];
+  hi = pack16<DT>(x);
+  unpack16<DT>(hi, h);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = x[e] - h[e];
+  lo = pack16<DT>(r);
+}
+
+// 16-bit element t (0..3) of an 8-byte chunk.
+__device__ __forceinline__ uint32_t elem16(u32x2 c, int t) {
+  const uint32_t w = (t < 2) ? c[0] : c[1];
+  return (t & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+template <int DT, int RW, bool FUSED, bool ROPE>
+__global__ __launch_bounds__(64 * kWaves) void attn_mfma_kernel(AttnArgs a) {
+  constexpr int D = kHeadDim;
+  constexpr int ROWB = kHeadDim * 2;
+  constexpr int VPR = ROWB / 16;
+  constexpr int NPH = kWaves / RW;  // waves sharing a row tile
+  static_assert(DT != F32, "matrix-core tiles take 16-bit storage");
+
+  hoist_args(a);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, gq = lane >> 4;
+  const int split = blockIdx.x, unit = blockIdx.z;
+  const int rt = blockIdx.y * RW + wave % RW;  // 16-row tile of this wave
+  const int phase = wave / RW;
+  const int bkv = unit / a.Hkv, hk = unit % a.Hkv;
+  const int k0 = split * a.chunk;
+  const int kspan = min(k0 + a.chunk, a.L);
+  const size_t head = (size_t)bkv * a.Hkv + hk;
+  char *kc = static_cast<char *>(a.k) + head * a.S_max * ROWB;
+  char *vc = static_cast<char *>(a.v) + head * a.S_max * ROWB;
+  const int nb0 = max(k0, a.new_base);
+
+  // ---- this lane's query row and the keys it sees
+  const int grow = rt * kRows + c;
+  const bool active = grow < a.G;
+  RowId r{0, 0, 0};
+  if (active) r = row_id(a, bkv, hk, grow);
+  const int lim = active ? ((a.causal_base < 0) ? a.L : a.causal_base + r.i + 1) : 0;
+  const int kend = min(kspan, (int)groups_max<1>((float)lim));  // wave-uniform
+
+  // ---- query operand: dims [8gq, +8) and [32 + 8gq, +8) of the row; a rotary
+  // pair (i, i + 32) sits in one lane
+  u32x4 qraw[2] = {u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}};
+  if (active) {
+    const char *qrow = static_cast<const char *>(a.q) + out_row(a, r) * 2;
+    qraw[0] = load16(qrow + gq * 16);
+    qraw[1] = load16(qrow + 64 + gq * 16);
+  }
+
+  // ---- fused append (as in the streaming kernel)
+  __shared__ u32x4 s_new[FUSED ? 2 * kMaxFusedRows * VPR : 1];
+  if constexpr (FUSED) {
+    constexpr int HALF_VECS = kHeadDim / 2 / 8;
+    const char *kn = static_cast<const char *>(a.k_new) + head * a.T_new * ROWB;
+    const char *vn = static_cast<const char *>(a.v_new) + head * a.T_new * ROWB;
+    const int n = (kspan - nb0) * HALF_VECS;
+    for (int t = threadIdx.x; t < n; t += blockDim.x) {
+      const int rr = t / HALF_VECS, j = t % HALF_VECS;
+      const int pos = nb0 + rr;
+      const size_t src = (size_t)(pos - a.new_base) * ROWB;
+      const PairChunks ch = load_pair<DT>(kn + src, vn + src, j, pos, ROPE ? a.rope_base : 0.f);
+      s_new[rr * VPR + j] = ch.klo;
+      s_new[rr * VPR + j + VPR / 2] = ch.khi;
+      s_new[(kMaxFusedRows + rr) * VPR + j] = ch.vlo;
+      s_new[(kMaxFusedRows + rr) * VPR + j + VPR / 2] = ch.vhi;
+      if (blockIdx.y == 0) store_pair<DT>(kc + (size_t)pos * ROWB, vc + (size_t)pos * ROWB, j, ch);
+    }
+    __syncthreads();
+  }
+
+  u32x4 qhi[2], qlo[2];
+  if constexpr (ROPE) {
+    float x0[8], x1[8];
+    unpack16<DT>(qraw[0], x0);
+    unpack16<DT>(qraw[1], x1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float cs, sn;
+      rope_cos_sin(a.causal_base + r.i, gq * 8 + e, a.rope_base, cs, sn);
+      rope_rotate(x0[e], x1[e], cs, sn);
+    }
+    split_hi_lo<DT>(x0, qhi[0], qlo[0]);
+    split_hi_lo<DT>(x1, qhi[1], qlo[1]);
+  } else {
+    qhi[0] = qraw[0];
+    qhi[1] = qraw[1];
+    qlo[0] = qlo[1] = u32x4{0, 0, 0, 0};
+  }
+
+  float m = -INFINITY, lsum = 0.f;
+  f32x4 o[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int s0 = k0 + phase * kStep; s0 < kend; s0 += NPH * kStep) {
+    // K: tile t, dims chunk kk -> key s0 + 16t + c, 16 bytes at dims 8gq + 32kk
+    u32x4 ka[2][2];
+    // V: lane's 8 keys s0 + {4gq + j (j < 4), 16 + 4gq + j - 4}, bytes [8c, 8c + 8)
+    u32x2 vv[8];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int key = s0 + 16 * t + c;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        ka[t][kk] = u32x4{0, 0, 0, 0};
+        if (key < kend) {
+          if (FUSED && key >= nb0) ka[t][kk] = s_new[(key - nb0) * VPR + gq + 4 * kk];
+          else ka[t][kk] = load16(kc + (size_t)key * ROWB + gq * 16 + kk * 64);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int key = s0 + ((j < 4) ? 4 * gq + j : 16 + 4 * gq + j - 4);
+      vv[j] = u32x2{0, 0};
+      if (key < kend) {
+        if (FUSED && key >= nb0) {
+          const u32x4 row = s_new[(kMaxFusedRows + key - nb0) * VPR + c / 2];
+          vv[j] = (c & 1) ? u32x2{row[2], row[3]} : u32x2{row[0], row[1]};
+        } else {
+          vv[j] = *reinterpret_cast<const u32x2 *>(vc + (size_t)key * ROWB + c * 8);
+        }
+      }
+    }
+    // scores S^T: st[t][i] = q_row . k_(s0 + 16t + 4gq + i)
+    f32x4 st[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      st[t] = mfma<DT>(ka[t][0], qhi[0], f32x4{0.f, 0.f, 0.f, 0.f});
+      st[t] = mfma<DT>(ka[t][1], qhi[1], st[t]);
+      if constexpr (ROPE) {
+        st[t] = mfma<DT>(ka[t][0], qlo[0], st[t]);
+        st[t] = mfma<DT>(ka[t][1], qlo[1], st[t]);
+      }
+    }
+    float sc[8];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int t = j >> 2, i = j & 3;
+      const int key = s0 + 16 * t + 4 * gq + i;
+      sc[j] = (key < lim && key < kend) ? st[t][i] * a.scale_log2 : -INFINITY;
+      mt = fmaxf(mt, sc[j]);
+    }
+    mt = groups_max<16>(mt);  // the row's 32 keys sit in lanes c, c+16, c+32, c+48
+    const float mn = fmaxf(m, mt);
+    float p[8];
+    float alpha = 1.f, ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[j] = 0.f;
+    if (mn != -INFINITY) {
+      alpha = exp2f(m - mn);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        p[j] = exp2f(sc[j] - mn);
+        ps += p[j];
+      }
+      m = mn;
+    }
+    lsum = lsum * alpha + ps;
+    u32x4 phi, plo;
+    split_hi_lo<DT>(p, phi, plo);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      u32x4 va;  // V^T rows 4c + t: element t of each of the 8 key chunks
+#pragma unroll
+      for (int w = 0; w < 4; ++w) va[w] = elem16(vv[2 * w], t) | (elem16(vv[2 * w + 1], t) << 16);
+      o[t] *= alpha;
+      o[t] = mfma<DT>(va, phi, o[t]);
+      o[t] = mfma<DT>(va, plo, o[t]);
+    }
+  }
+  lsum = groups_sum<16>(lsum);  // the row's keys were spread over the 4 lane groups
+
+  // ---- lane l holds O[row c][16gq + 4i + t] = o[t][i]; merge the phases
+  // that shared the row tile, then write the rows or publish the partial
+  constexpr int kWaveFloats = kWaves * kRows * (D + 2);
+  constexpr int kStageFloats = kMergeRows * kPStride;
+  constexpr int kSmem = kWaveFloats > kStageFloats ? kWaveFloats : kStageFloats;
+  __shared__ __attribute__((aligned(16))) float smem[kSmem];
+  const size_t tile_id = (size_t)unit * a.row_tiles + blockIdx.y;
+  if constexpr (RW == kWaves) {
+    // one wave per row tile, no split (the plan guarantees it)
+    if (active) {
+      const float inv = 1.f / lsum;
+      float *orow = a.out + out_row(a, r) + 16 * gq;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) orow[4 * i + t] = o[t][i] * inv;
+      }
+    }
+    return;
+  } else {
+    float *sm_o = smem;                        // [phase][row][D]
+    float *sm_m = smem + kWaves * kRows * D;   // [phase][row]
+    float *sm_l = sm_m + kWaves * kRows;       // [phase][row]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) sm_o[(phase * kRows + c) * D + 16 * gq + 4 * i + t] = o[t][i];
+    }
+    if (gq == 0) {
+      sm_m[phase * kRows + c] = m;
+      sm_l[phase * kRows + c] = lsum;
+    }
+    __syncthreads();
+    const int g0 = blockIdx.y * kRows;
+    const int gcount = min(kRows, a.G - g0);
+    float *part = a.ws_part + (tile_id * a.splits + split) * kRows * kPStride;
+    for (int idx = threadIdx.x; idx < kRows * D; idx += blockDim.x) {
+      const int g = idx / D, d = idx % D;
+      if (g >= gcount) continue;
+      float mw[NPH];
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NPH; ++w) {
+        mw[w] = sm_m[w * kRows + g];
+        M = fmaxf(M, mw[w]);
+      }
+      float Ls = 0.f, O = 0.f;
+#pragma unroll
+      for (int w = 0; w < NPH; ++w) {
+        if (mw[w] != -INFINITY) {
+          const float f = exp2f(mw[w] - M);
+          Ls = fmaf(sm_l[w * kRows + g], f, Ls);
+          O = fmaf(sm_o[(w * kRows + g) * D + d], f, O);
+        }
+      }
+      if (a.splits == 1) {
+        a.out[out_row(a, row_id(a, bkv, hk, g0 + g)) + d] = O / Ls;
+      } else {
+        publish(part + g * kPStride + d, O);
+        if (d == 0) {
+          publish(part + g * kPStride + D, M);
+          publish(part + g * kPStride + D + 1, Ls);
+        }
+      }
+    }
+    if (a.splits == 1) return;
+    merge_splits<kRows, kWaves>(a, tile_id, g0, gcount, bkv, hk, smem);
+  }
+}
+
+template <int DT, int RW>
+void launch_rw(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
+  const bool fused = a.k_new != nullptr, rope = a.rope_base > 0.f;
+  if (fused) {
+    if (rope) launch_kernel(attn_mfma_kernel<DT, RW, true, true>, grid, block, s, a);
+    else launch_kernel(attn_mfma_kernel<DT, RW, true, false>, grid, block, s, a);
+  } else {
+    if (rope) launch_kernel(attn_mfma_kernel<DT, RW, false, true>, grid, block, s, a);
+    else launch_kernel(attn_mfma_kernel<DT, RW, false, false>, grid, block, s, a);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_mfma(int dtype, const AttnArgs &a, hipStream_t s) {
+  const dim3 grid(a.splits, a.row_tiles, a.Bkv * a.Hkv);
+  const dim3 block(64 * kWaves);
+  if (dtype == F16) {
+    if (a.rw == kWaves) launch_rw<F16, kWaves>(a, grid, block, s);
+    else launch_rw<F16, 1>(a, grid, block, s);
+  } else {
+    if (a.rw == kWaves) launch_rw<BF16, kWaves>(a, grid, block, s);
+    else launch_rw<BF16, 1>(a, grid, block, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvd

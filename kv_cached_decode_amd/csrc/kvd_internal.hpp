@@ -59,6 +59,8 @@ struct AttnArgs {
   int row_tiles;                 // ceil(G / rows per tile)
   int waves;                     // waves per workgroup
   int gm;                        // rows per tile (template bucket)
+  int mfma;                      // 1: matrix-core tile kernel (blocks of queries)
+  int rw;                        // matrix-core kernel: 16-row tiles per workgroup (1 or 4)
 };
 
 struct VerifyArgs {
@@ -76,10 +78,10 @@ struct VerifyArgs {
 
 // Attention planning shared by the entry points and the workspace-size query.
 struct AttnPlan {
-  int gm, row_tiles, chunk, splits, waves;
+  int gm, row_tiles, chunk, splits, waves, mfma, rw;
   size_t part_floats, counters;
 };
-AttnPlan plan_attn(int dtype, int units, int G, int L, bool rope);
+AttnPlan plan_attn(int dtype, int units, int G, int N, int L, bool rope);
 
 void plan_verify(int B, int R, int V, int &chunk, int &chunks);
 
@@ -106,6 +108,7 @@ inline void launch_kernel(void (*kernel)(Args...), dim3 grid, dim3 block, hipStr
 hipError_t launch_append(int dtype, const AppendArgs &a, hipStream_t s);
 hipError_t launch_reorder(int dtype, const ReorderArgs &a, hipStream_t s);
 hipError_t launch_attn(int dtype, const AttnArgs &a, hipStream_t s);
+hipError_t launch_attn_mfma(int dtype, const AttnArgs &a, hipStream_t s);
 hipError_t launch_verify(const VerifyArgs &a, hipStream_t s);
 
 }  // namespace kvd

@@ -110,8 +110,11 @@ def test_whisper_greedy_sweep_lengths(layer):
 
 # Plans forced through the tuning variables, so that split boundaries and the
 # wide (16-wave) variant are covered at lengths the default plan runs unsplit.
+# Blocks of queries (N > 1, 16-bit storage) take the matrix-core kernel by
+# default; "stream" runs them through the streaming kernel instead.
 PLANS = {"default": {}, "chunk128": {"KVD_ATTN_CHUNK": "128"},
-         "wide": {"KVD_ATTN_WAVES": "16"}, "wide_chunk512": {"KVD_ATTN_WAVES": "16", "KVD_ATTN_CHUNK": "512"}}
+         "wide": {"KVD_ATTN_WAVES": "16"}, "wide_chunk512": {"KVD_ATTN_WAVES": "16", "KVD_ATTN_CHUNK": "512"},
+         "stream": {"KVD_ATTN_MFMA": "0"}, "stream_chunk128": {"KVD_ATTN_MFMA": "0", "KVD_ATTN_CHUNK": "128"}}
 
 
 @pytest.fixture(params=list(PLANS))
@@ -176,11 +179,11 @@ def test_large_scores_online_rescale(dtype, plan):
 # ------------------------------------------------------ speculative verify ----
 
 @pytest.mark.parametrize("L_before", [64, 128, 443])
-def test_verify_attention_n5(L_before):
+def test_verify_attention_n5(L_before, plan):
     """Five draft rows appended at once, causal among themselves, over the
     self cache and the cross cache (large-v2 layer shape)."""
     w = I.WHISPER_VERIFY
-    say(f"case: verify attention L_before={L_before}")
+    say(f"case: verify attention L_before={L_before} plan={plan}")
     layer = 3
     L = L_before + 5
     k_all, v_all = I.self_kv(w, layer)
@@ -434,10 +437,10 @@ def test_cross_cache_per_row_and_shared_agree():
     ("bf16", 2, 9, 3, 40, 100, 10000.0),    # long block: append then attend
     ("f32", 2, 4, 4, 3, 70, 10000.0),
 ])
-def test_step_self_equals_append_then_attend(dtype, B, Hq, Hkv, N, L, rope):
+def test_step_self_equals_append_then_attend(dtype, B, Hq, Hkv, N, L, rope, plan):
     """decode_step_self leaves the cache exactly as kv_append does and returns
     decode_attn_self's output, and both match the oracle."""
-    say(f"case: step_self {dtype} B={B} Hq={Hq} Hkv={Hkv} N={N} L={L} rope={rope}")
+    say(f"case: step_self {dtype} B={B} Hq={Hq} Hkv={Hkv} N={N} L={L} rope={rope} plan={plan}")
     g = np.random.default_rng(L * 7 + N)
     S = L + 3
     k_all = O.narrow(g.standard_normal((B, Hkv, L, 64)), dtype)
