@@ -171,7 +171,7 @@ def time_cross_kernel(torch, kb, eng: Engine, reps: int = 8):
     return float(np.mean(kernel)) * 1e-3, float(np.mean(period)) * 1e-3
 
 
-def cpu_baseline(target_s: float = 15.0):
+def cpu_baseline(target_s: float = 12.0):
     """The CPU oracle (numpy, float64) on a bounded sample of the same steps:
     full 32-layer steps at lengths spread over 1..448, BLAS pinned to one
     thread."""
@@ -192,7 +192,8 @@ def cpu_baseline(target_s: float = 15.0):
     kv = [I.self_kv(w, l) for l in range(LAYERS)]
     lengths = [1, 112, 224, 336, 448, 56, 168, 280, 392, 28, 140, 252, 364, 420]
     spent, times, used = 0.0, [], []
-    for L in lengths:
+    for n in range(200):  # the length list, repeated until the time target
+        L = lengths[n % len(lengths)]
         caches = []
         for l in range(LAYERS):
             c = O.ConcatCache(1, H, D, "f16")
@@ -214,7 +215,7 @@ def cpu_baseline(target_s: float = 15.0):
         limiter.unregister()
     mean = float(np.mean(times))
     return {"value": 1.0 / mean, "unit": "steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(times)} full 32-layer decode steps at self lengths {used} "
+            "sample": f"{len(times)} full 32-layer decode steps at self lengths {sorted(set(used))} "
                       f"(oracle: numpy float64, BLAS limited to 1 thread), {spent:.1f} s total"}
 
 
@@ -225,13 +226,28 @@ def main():
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--eager", action="store_true", help="also time eager (no graph) launches")
+    ap.add_argument("--workload", default="greedy", choices=["greedy", "verify", "beam", "gqa"],
+                    help="greedy (the headline line) or a further workload")
     ap.add_argument("--unfused", action="store_true",
                     help="separate kv_append and decode_attn_self launches (96 per step)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the decode step has no multi-GPU path in this build)", file=sys.stderr)
+              "(the decode step runs on a single GPU)", file=sys.stderr)
         sys.exit(2)
+    if args.workload != "greedy":
+        import torch
+        from kv_cached_decode_amd import binding as kb
+        if not torch.cuda.is_available():
+            print("bench.py needs a GPU", file=sys.stderr)
+            sys.exit(1)
+        kb.lib()
+        fn = {"verify": workload_verify, "beam": workload_beam, "gqa": workload_gqa}[args.workload]
+        line = fn(torch, kb, max(1, args.steps // 448) * 4)
+        line.update({"n_gpus": 1, "dtype": "bf16" if args.workload == "gqa" else "f16",
+                     "data": "synthetic", "higher_is_better": True})
+        print(json.dumps(line), flush=True)
+        return
 
     import torch
     from kv_cached_decode_amd import binding as kb
@@ -312,6 +328,191 @@ def main():
     if eager is not None:
         line["eager_steps_per_s"] = round(eager, 2)
     print(json.dumps(line), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Further workloads (measurement modes, selected with --workload; the default
+# is the greedy line above). Inputs are seeded torch draws on the device; the
+# parity tests check these shapes against the oracle.
+# ---------------------------------------------------------------------------
+
+
+def _graph_steps(torch, fn, steps):
+    """One captured graph per step index."""
+    graphs = []
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for s in steps:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                fn(s)
+            graphs.append(g)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def _time_graphs(torch, graphs, reps):
+    for g in graphs[: min(len(graphs), 16)]:
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        for g in graphs:
+            g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / (reps * len(graphs))
+
+
+def _kernel_us(torch, kb, launch, n=64):
+    """Mean kernel duration of `launch` (HIP events at kernel begin / end)."""
+    stream = torch.cuda.current_stream()
+    pairs = []
+    for i in range(n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        b.record(stream)
+        kb.time_next_launch(a, b)
+        launch(i)
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in pairs])) * 1e3
+
+
+def workload_verify(torch, kb, reps):
+    """Speculative verification at the large-v2 shape: per step, 32 layers of
+    [append 5 draft rows + self attention of 5 causal queries, cross attention
+    of 5 queries over 1500 frames], then verify_accept over [1, 5, 51865]."""
+    g = torch.Generator(device="cuda").manual_seed(3)
+    rn = lambda *sh: (torch.randn(*sh, generator=g, device="cuda") / 8).half()
+    N, V = 5, 51865
+    self_c, cross_c = [], []
+    for _ in range(LAYERS):
+        c = kb.Cache(1, H, S_MAX, torch.float16)
+        c.k.copy_(rn(1, H, S_MAX, D)); c.v.copy_(rn(1, H, S_MAX, D))
+        self_c.append(c)
+        x = kb.Cache(1, H, FRAMES, torch.float16)
+        x.k.copy_(rn(1, H, FRAMES, D)); x.v.copy_(rn(1, H, FRAMES, D))
+        cross_c.append(x)
+    q, qx = rn(LAYERS, 1, H, N, D), rn(LAYERS, 1, H, N, D)
+    kn, vn = rn(LAYERS, 1, H, N, D), rn(LAYERS, 1, H, N, D)
+    out = torch.empty((LAYERS, 1, H, N, D), dtype=torch.float32, device="cuda")
+    outx = torch.empty_like(out)
+    logits = torch.randn(1, N, V, generator=g, device="cuda") * 2
+    draft = torch.randint(0, V, (1, N), generator=g, device="cuda", dtype=torch.int32)
+    acc = torch.empty(1, dtype=torch.int32, device="cuda")
+    nxt = torch.empty(1, dtype=torch.int32, device="cuda")
+    ws = kb.workspace(max(kb.attn_workspace_bytes(1, H, N, FRAMES), kb.verify_workspace_bytes(1, N, V)))
+    lens = [64, 128, 192, 256, 320, 384, 443]
+
+    def step(i):
+        L = lens[i] + N
+        for l in range(LAYERS):
+            kb.decode_step_self(q[l], kn[l], vn[l], self_c[l], L, 1 / 8, out=out[l], ws=ws)
+            kb.decode_attn_cross(qx[l], cross_c[l], FRAMES, 1 / 8, out=outx[l], ws=ws)
+        kb.verify_accept(logits, draft, ws=ws, accept_len=acc, next_token=nxt)
+
+    graphs = _graph_steps(torch, step, range(len(lens)))
+    sec = _time_graphs(torch, graphs, reps)
+    kv = sum(LAYERS * (2 * (L + N) * ROW_BYTES + CROSS_BYTES + 2 * N * ROW_BYTES) for L in lens) / len(lens)
+    self_us = _kernel_us(torch, kb, lambda i: kb.decode_step_self(q[i % LAYERS], kn[i % LAYERS], vn[i % LAYERS], self_c[i % LAYERS], 448, 1 / 8, out=out[0], ws=ws))
+    cross_us = _kernel_us(torch, kb, lambda i: kb.decode_attn_cross(qx[i % LAYERS], cross_c[i % LAYERS], FRAMES, 1 / 8, out=outx[0], ws=ws))
+    verify_us = _kernel_us(torch, kb, lambda i: kb.verify_accept(logits, draft, ws=ws, accept_len=acc, next_token=nxt))
+    p = [0.75 ** k * 0.25 for k in range(5)] + [0.75 ** 5]
+    tokens = sum(pk * t for pk, t in zip(p, [1, 2, 3, 4, 5, 5]))
+    return {"metric": "speculative verify steps/s (N=5 drafts), large-v2 shape, 1 GPU",
+            "value": round(1 / sec, 2), "unit": "verify steps/s", "ms_per_step": round(sec * 1e3, 4),
+            "effective_kv_gbps": round(kv / sec / 1e9, 1),
+            "tokens_per_s_at_p075": round(tokens / sec, 1),
+            "kernels_us": {"step_self_N5_len448 (matrix-core tile)": round(self_us, 3),
+                           "cross_N5": round(cross_us, 3), "verify_accept_V51865": round(verify_us, 3)},
+            "config": {"workload": "whisper-large-v2 verify: 32 layers x [append 5 + self N=5, cross N=5 "
+                                   "over 1500] + verify_accept [1, 5, 51865]; len before 64..443"}}
+
+
+def workload_beam(torch, kb, reps):
+    """Beam search with 5 beams at the large-v2 shape: per step, 32 layers of
+    [kv_reorder by parent beams, append + self attention, cross attention over
+    a cross cache shared by the beams]; 224 steps."""
+    g = torch.Generator(device="cuda").manual_seed(4)
+    rn = lambda *sh: (torch.randn(*sh, generator=g, device="cuda") / 8).half()
+    B, steps = 5, 224
+    self_c, cross_c = [], []
+    for _ in range(LAYERS):
+        c = kb.Cache(B, H, S_MAX, torch.float16)
+        c.k.copy_(rn(B, H, S_MAX, D)); c.v.copy_(rn(B, H, S_MAX, D))
+        self_c.append(c)
+        x = kb.Cache(1, H, FRAMES, torch.float16)
+        x.k.copy_(rn(1, H, FRAMES, D)); x.v.copy_(rn(1, H, FRAMES, D))
+        cross_c.append(x)
+    q, qx = rn(LAYERS, B, H, 1, D), rn(LAYERS, B, H, 1, D)
+    kn, vn = rn(LAYERS, B, H, 1, D), rn(LAYERS, B, H, 1, D)
+    parents = torch.randint(0, B, (steps, B), generator=g, device="cuda", dtype=torch.int32)
+    out = torch.empty((LAYERS, B, H, 1, D), dtype=torch.float32, device="cuda")
+    outx = torch.empty_like(out)
+    ws = kb.workspace(kb.attn_workspace_bytes(B, H, 1, FRAMES))
+
+    def step(s):
+        for l in range(LAYERS):
+            if s > 0:
+                kb.kv_reorder(self_c[l], parents[s], s)
+            kb.decode_step_self(q[l], kn[l], vn[l], self_c[l], s + 1, 1 / 8, out=out[l], ws=ws)
+            kb.decode_attn_cross(qx[l], cross_c[l], FRAMES, 1 / 8, out=outx[l], ws=ws)
+
+    graphs = _graph_steps(torch, step, range(steps))
+    sec = _time_graphs(torch, graphs, reps)
+    # reorder moves (reads and writes) the rows of the beams whose parent differs
+    changed = float((parents != torch.arange(B, device="cuda")).sum().item()) / steps
+    kv = sum(LAYERS * (B * 2 * (s + 1) * ROW_BYTES + CROSS_BYTES + B * 2 * ROW_BYTES
+                       + 2 * changed * 2 * s * ROW_BYTES) for s in range(steps)) / steps
+    reorder_us = _kernel_us(torch, kb, lambda i: kb.kv_reorder(self_c[i % LAYERS], parents[100], 200))
+    return {"metric": "beam-search decode steps/s (5 beams), large-v2 shape, 1 GPU",
+            "value": round(1 / sec, 2), "unit": "steps/s", "ms_per_step": round(sec * 1e3, 4),
+            "effective_kv_gbps": round(kv / sec / 1e9, 1),
+            "kernels_us": {"kv_reorder_len200": round(reorder_us, 3)},
+            "config": {"workload": "whisper-large-v2 beam 5: 32 layers x [kv_reorder, append + self, "
+                                   "cross shared by beams]; 224 steps"}}
+
+
+def workload_gqa(torch, kb, reps):
+    """GQA decoder-only LM: 30 layers, B=8, 9 query / 3 KV heads of 64, bf16,
+    RoPE base 10000. Prefill of 512 prompt tokens (append + causal attention of
+    512 queries, matrix-core tile), then decode steps from length 513 to 1024."""
+    g = torch.Generator(device="cuda").manual_seed(5)
+    rn = lambda *sh: torch.randn(*sh, generator=g, device="cuda").bfloat16()
+    Lyr, B, Hq, Hk, P, S = 30, 8, 9, 3, 512, 1024
+    caches = [kb.Cache(B, Hk, S, torch.bfloat16) for _ in range(Lyr)]
+    qp, kp, vp = rn(Lyr, B, Hq, P, D), rn(Lyr, B, Hk, P, D), rn(Lyr, B, Hk, P, D)
+    qd, kd, vd = rn(Lyr, B, Hq, 1, D), rn(Lyr, B, Hk, 1, D), rn(Lyr, B, Hk, 1, D)
+    outp = torch.empty((B, Hq, P, D), dtype=torch.float32, device="cuda")
+    outd = torch.empty((Lyr, B, Hq, 1, D), dtype=torch.float32, device="cuda")
+    ws = kb.workspace(max(kb.attn_workspace_bytes(B, Hq, P, P), kb.attn_workspace_bytes(B, Hq, 1, S)))
+
+    def prefill(_):
+        for l in range(Lyr):
+            kb.decode_step_self(qp[l], kp[l], vp[l], caches[l], P, 0.125, rope_base=1e4, out=outp, ws=ws)
+
+    def decode(s):
+        for l in range(Lyr):
+            kb.decode_step_self(qd[l], kd[l], vd[l], caches[l], s + 1, 0.125, rope_base=1e4, out=outd[l], ws=ws)
+
+    pg = _graph_steps(torch, prefill, [0])
+    t_prefill = _time_graphs(torch, pg, max(1, reps))
+    dg = _graph_steps(torch, decode, range(P, S))
+    sec = _time_graphs(torch, dg, reps)
+    row = Hk * D * 2
+    kv = sum(Lyr * B * (2 * (s + 1) * row + 2 * row) for s in range(P, S)) / (S - P)
+    prefill_us = _kernel_us(torch, kb, lambda i: kb.decode_attn_self(qp[i % Lyr], caches[i % Lyr], P, 0.125, rope_base=1e4, out=outp, ws=ws), n=30)
+    flops = Lyr * B * Hq * 2 * 2 * D * (P * (P + 1) / 2)
+    return {"metric": "GQA decode steps/s (B=8, 9q/3kv heads, len 513..1024), 1 GPU",
+            "value": round(1 / sec, 2), "unit": "steps/s", "ms_per_step": round(sec * 1e3, 4),
+            "effective_kv_gbps": round(kv / sec / 1e9, 1),
+            "prefill_ms": round(t_prefill * 1e3, 4),
+            "prefill_attention_kernel_us": round(prefill_us, 3),
+            "prefill_attention_tflops": round(flops / Lyr / (prefill_us * 1e-6) / 1e12, 2),
+            "config": {"workload": "GQA LM: 30 layers, B8, Hq9/Hkv3 x 64, bf16, RoPE 1e4; prefill 512 "
+                                   "then decode to 1024"}}
 
 
 if __name__ == "__main__":

@@ -32,6 +32,11 @@ int check_cache(const kvd_cache *c) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? KVD_OK : KVD_ERR_LAUNCH; }
 
+// Rotary angle step: theta_i = base^(-2i/D) = 2^(-i * step).
+double rope_step_of(float rope_base) {
+  return rope_base > 0.f ? 2.0 * log2((double)rope_base) / kvd::kHeadDim : 0.0;
+}
+
 // Every workspace starts with a fixed block of arrival counters, zero at rest
 // (each kernel that counts arrivals sets its counters back to zero), so one
 // workspace can serve calls with different plans: partial results of one call
@@ -118,6 +123,7 @@ int kv_append(const kvd_cache *cache, const void *k_new, const void *v_new, int3
   a.T = T;
   a.pos = pos;
   a.rope_base = rope_base;
+  a.rope_step = rope_step_of(rope_base);
   return status_of(kvd::launch_append(cache->dtype, a, static_cast<hipStream_t>(stream)));
 }
 
@@ -178,6 +184,7 @@ int prepare_self(AttnArgs &a, const void *q, const void *k_new, const void *v_ne
   a.T_new = k_new ? N : 0;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.rope_base = rope_base;
+  a.rope_step = rope_step_of(rope_base);
   return prepare_attn(a, cache->dtype, ws, ws_bytes);
 }
 
@@ -217,6 +224,7 @@ int decode_step_self(const void *q, const void *k_new, const void *v_new, int32_
     ap.T = N;
     ap.pos = len - N;
     ap.rope_base = rope_base;
+    ap.rope_step = rope_step_of(rope_base);
     const int sa = status_of(kvd::launch_append(cache->dtype, ap, s));
     if (sa) return sa;
   }

@@ -125,7 +125,7 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
       const int r = t / HALF_VECS, j = t % HALF_VECS;
       const int pos = nb0 + r;
       const size_t src = (size_t)(pos - a.new_base) * ROWB;
-      const PairChunks c = load_pair<DT>(kn + src, vn + src, j, pos, ROPE ? a.rope_base : 0.f);
+      const PairChunks c = load_pair<DT>(kn + src, vn + src, j, pos, ROPE ? a.rope_step : 0.0);
       s_new[r * VPR + j] = c.klo;
       s_new[r * VPR + j + VPR / 2] = c.khi;
       s_new[(kMaxFusedRows + r) * VPR + j] = c.vlo;
@@ -137,6 +137,8 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
 
   // ---- query rows: rotate (fp32), fold in scale*log2(e)
   float qf[GM][VE];
+  float rc[ROPE ? VE : 1], rs[ROPE ? VE : 1];  // cos / sin at position rpos
+  int rpos = -1;
 #pragma unroll
   for (int g = 0; g < GM; ++g) {
 #pragma unroll
@@ -144,7 +146,12 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
     if (g < gcount) {
       if constexpr (ROPE) {
         const RowId r = row_id(a, bkv, hk, g0 + g);
-        rope_slice_f32<DT>(qraw[g], qpart[g], ds, a.causal_base + r.i, a.rope_base, qf[g]);
+        const int pos = a.causal_base + r.i;
+        if (pos != rpos) {  // rows of one position share their cos / sin
+          rope_slice_cs<DT>(ds, pos, a.rope_step, rc, rs);
+          rpos = pos;
+        }
+        rope_slice_f32<DT>(qraw[g], qpart[g], ds, rc, rs, qf[g]);
       } else {
         unpack16<DT>(qraw[g], qf[g]);
       }

@@ -119,7 +119,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_mfma_kernel(AttnArgs a) {
       const int rr = t / HALF_VECS, j = t % HALF_VECS;
       const int pos = nb0 + rr;
       const size_t src = (size_t)(pos - a.new_base) * ROWB;
-      const PairChunks ch = load_pair<DT>(kn + src, vn + src, j, pos, ROPE ? a.rope_base : 0.f);
+      const PairChunks ch = load_pair<DT>(kn + src, vn + src, j, pos, ROPE ? a.rope_step : 0.0);
       s_new[rr * VPR + j] = ch.klo;
       s_new[rr * VPR + j + VPR / 2] = ch.khi;
       s_new[(kMaxFusedRows + rr) * VPR + j] = ch.vlo;
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float cs, sn;
-      rope_cos_sin(a.causal_base + r.i, gq * 8 + e, a.rope_base, cs, sn);
+      rope_cos_sin(a.causal_base + r.i, gq * 8 + e, a.rope_step, cs, sn);
       rope_rotate(x0[e], x1[e], cs, sn);
     }
     split_hi_lo<DT>(x0, qhi[0], qlo[0]);

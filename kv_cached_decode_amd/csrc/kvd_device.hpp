@@ -93,15 +93,17 @@ template <int DT> __device__ __forceinline__ u32x4 pack16(const float *in) {
 }
 
 // Rotary embedding of pair (i, i + D/2) at absolute position pos: angle
-// pos * base^(-2i/D). The angle and its cosine/sine are evaluated in fp64 and
-// rounded to fp32 once; the rotation itself is fp32.
-__device__ __forceinline__ void rope_cos_sin(int pos, int i, float base, float &c, float &s) {
-  const double theta = pow((double)base, -2.0 * (double)i / (double)kHeadDim);
+// pos * theta_i with theta_i = base^(-2i/D) = 2^(-i * step), step = 2 log2(base)
+// / D computed on the host in fp64. The angle is formed and reduced modulo 2 pi
+// in fp64 (two-constant Cody-Waite), then cos / sin are evaluated in fp32 on
+// the reduced angle (|r| <= pi).
+__device__ __forceinline__ void rope_cos_sin(int pos, int i, double step, float &c, float &s) {
+  const double theta = exp2(-(double)i * step);
   const double ang = (double)pos * theta;
-  double sd, cd;
-  sincos(ang, &sd, &cd);
-  c = (float)cd;
-  s = (float)sd;
+  const double k = rint(ang * 0.15915494309189535);  // 1 / (2 pi)
+  double r = fma(-k, 6.283185307179586, ang);        // 2 pi, high part
+  r = fma(-k, 2.4492935982947064e-16, r);            // 2 pi, low part
+  sincosf((float)r, &s, &c);
 }
 __device__ __forceinline__ void rope_rotate(float &lo, float &hi, float c, float s) {
   const float l = lo, h = hi;
@@ -176,12 +178,23 @@ template <> __device__ __forceinline__ float group_sum<16>(float x) {
   return x;
 }
 
-// The 16-byte slice `ds` of a query row rotated at position pos, in fp32
-// (queries are not stored, so they are not rounded): `partner` is slice
-// ds ^ (LPR/2) of the same row, the other half of every rotary pair.
+// cos / sin of the VE rotary pairs held by lane slice `ds` of a row at
+// position pos (slice ds and ds ^ (LPR/2) hold the two halves of the pairs
+// (ds % (LPR/2)) * VE + e).
 template <int DT>
-__device__ __forceinline__ void rope_slice_f32(u32x4 mine, u32x4 partner, int ds, int pos,
-                                               float base, float *x) {
+__device__ __forceinline__ void rope_slice_cs(int ds, int pos, double step, float *c, float *s) {
+  constexpr int VE = vec_elems<DT>();
+  constexpr int LPR = kHeadDim / VE;
+#pragma unroll
+  for (int e = 0; e < VE; ++e) rope_cos_sin(pos, (ds % (LPR / 2)) * VE + e, step, c[e], s[e]);
+}
+
+// The 16-byte slice `ds` of a query row rotated with those cos / sin, in fp32
+// (queries are not stored, so they are not rounded): `partner` is slice
+// ds ^ (LPR/2) of the same row.
+template <int DT>
+__device__ __forceinline__ void rope_slice_f32(u32x4 mine, u32x4 partner, int ds, const float *c,
+                                               const float *s, float *x) {
   constexpr int VE = vec_elems<DT>();
   constexpr int LPR = kHeadDim / VE;
   float p[VE];
@@ -190,11 +203,9 @@ __device__ __forceinline__ void rope_slice_f32(u32x4 mine, u32x4 partner, int ds
   const bool is_lo = ds < LPR / 2;
 #pragma unroll
   for (int e = 0; e < VE; ++e) {
-    float c, s;
-    rope_cos_sin(pos, (ds % (LPR / 2)) * VE + e, base, c, s);
     float lo = is_lo ? x[e] : p[e];
     float hi = is_lo ? p[e] : x[e];
-    rope_rotate(lo, hi, c, s);
+    rope_rotate(lo, hi, c[e], s[e]);
     x[e] = is_lo ? lo : hi;
   }
 }
@@ -235,9 +246,10 @@ __device__ __forceinline__ void reset_counter(uint32_t *counter) {
 struct PairChunks {
   u32x4 klo, khi, vlo, vhi;
 };
+// step = 2 log2(base) / D, or 0: no rotation.
 template <int DT>
 __device__ __forceinline__ PairChunks load_pair(const char *k_src, const char *v_src, int j,
-                                                int pos, float base) {
+                                                int pos, double step) {
   constexpr int VE = vec_elems<DT>();
   constexpr int EB = Storage<DT>::bytes;
   const int lo_off = j * VE * EB, hi_off = (kHeadDim / 2 + j * VE) * EB;
@@ -246,14 +258,14 @@ __device__ __forceinline__ PairChunks load_pair(const char *k_src, const char *v
   c.khi = load16(k_src + hi_off);
   c.vlo = load16(v_src + lo_off);
   c.vhi = load16(v_src + hi_off);
-  if (base > 0.f) {
+  if (step > 0.0) {
     float lo[VE], hi[VE];
     unpack16<DT>(c.klo, lo);
     unpack16<DT>(c.khi, hi);
 #pragma unroll
     for (int e = 0; e < VE; ++e) {
       float cs, sn;
-      rope_cos_sin(pos, j * VE + e, base, cs, sn);
+      rope_cos_sin(pos, j * VE + e, step, cs, sn);
       rope_rotate(lo[e], hi[e], cs, sn);
     }
     c.klo = pack16<DT>(lo);

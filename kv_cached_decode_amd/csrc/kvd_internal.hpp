@@ -26,6 +26,7 @@ struct AppendArgs {
   const void *k_new, *v_new;     // [B][H][T][D]
   int B, H, S_max, T, pos;
   float rope_base;               // > 0: rotate keys at pos + t
+  double rope_step;              // 2 log2(rope_base) / D (0: no rotation)
 };
 
 struct ReorderArgs {
@@ -53,6 +54,7 @@ struct AttnArgs {
   int new_base, T_new;           // new rows sit at [new_base, new_base + T_new); INT_MAX: none
   float scale_log2;              // scale * log2(e)
   float rope_base;               // > 0: rotate q at causal_base + i (and new keys)
+  double rope_step;              // 2 log2(rope_base) / D (0: no rotation)
   // plan
   int chunk;                     // keys per workgroup
   int splits;                    // workgroups per (unit, row tile)
