@@ -81,9 +81,11 @@ typedef struct kvd_cache {
  * pos = 0); [N] workflow steps 2-3 and the prefill phase (T = prompt length).
  *   k_new, v_new: device, [B][H][T][D] in cache->dtype.
  *   rope_base > 0: each key row is first rotated at its absolute position
- *     pos + t (pairs (i, i + D/2) turn by (pos + t) * rope_base^(-2i/D)),
- *     computed in fp32 and rounded to nearest-even into the cache; values
- *     are copied as they are. rope_base == 0: a bit-exact copy of both.
+ *     pos + t (pairs (i, i + D/2) turn by (pos + t) * rope_base^(-2i/D));
+ *     the angle is formed and reduced modulo 2 pi in fp64, its cos / sin and
+ *     the rotation are computed in fp32, and the result is rounded to
+ *     nearest-even into the cache; values are copied as they are.
+ *     rope_base == 0: a bit-exact copy of both.
  * Errors: KVD_ERR_NULL, KVD_ERR_SHAPE (T < 1, pos < 0, D != 64, B/H < 1),
  *   KVD_ERR_DTYPE, KVD_ERR_CAPACITY (pos + T > S_max), KVD_ERR_ALIGN. */
 int kv_append(const kvd_cache *cache, const void *k_new, const void *v_new,
