@@ -240,11 +240,8 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
     }
   }
 
-  // ---- merge the waves of the workgroup in LDS; the same buffer later
-  // stages the split partials
-  constexpr int kWaveFloats = NWMAX * GM * (D + 2);
-  constexpr int kStageFloats = kMergeRows * kPStride;
-  constexpr int kSmem = kWaveFloats > kStageFloats ? kWaveFloats : kStageFloats;
+  // ---- merge the waves of the workgroup in LDS
+  constexpr int kSmem = NWMAX * GM * (D + 2);
   __shared__ __attribute__((aligned(16))) float smem[kSmem];
   float *sm_o = smem;                       // [nw][GM][D]
   float *sm_m = smem + NWMAX * GM * D;  // [nw][GM]
@@ -298,7 +295,7 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
   }
   if (a.splits == 1) return;
 
-  merge_splits<GM, NWMAX>(a, tile_id, g0, gcount, bkv, hk, smem);
+  merge_splits<GM>(a, tile_id, g0, gcount, bkv, hk);
 }
 
 template <int DT, bool FUSED, bool ROPE>
@@ -358,7 +355,7 @@ AttnPlan plan_attn_mfma(int units, int G, int L) {
     int chunk = (unit_bytes <= 128 * 1024) ? L : (64 * 1024) / (2 * kHeadDim * 2);
     if (forced > 0) chunk = forced;
     chunk = ((chunk + min_chunk - 1) / min_chunk) * min_chunk;
-    const int max_splits = kMergeRows / kRows;
+    const int max_splits = kMaxSplits;
     int splits = (L + chunk - 1) / chunk;
     if (splits > max_splits) {
       chunk = (((L + max_splits - 1) / max_splits + min_chunk - 1) / min_chunk) * min_chunk;
@@ -425,7 +422,7 @@ AttnPlan plan_attn(int dtype, int units, int G, int N, int L, bool rope) {
   p.waves = waves;
 
   const int min_chunk = tile * waves;
-  const int max_splits = kMergeRows / p.gm < 64 ? kMergeRows / p.gm : 64;
+  const int max_splits = kMaxSplits;
   chunk = ((chunk + min_chunk - 1) / min_chunk) * min_chunk;
   if (chunk < min_chunk) chunk = min_chunk;
   int splits = (L + chunk - 1) / chunk;

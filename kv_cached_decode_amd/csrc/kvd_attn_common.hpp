@@ -10,12 +10,7 @@
 namespace kvd {
 
 constexpr int kPStride = kHeadDim + 4;  // partial row: o[D], m, l, 2 pad floats (16-byte rows)
-constexpr int kMergeRows = 128;         // splits * rows per tile the merge can stage
 constexpr int kMaxWaves = 16;           // the widest workgroup (1024 threads)
-
-// Floats each thread stages in the final merge, for workgroups of 64 * NWMAX.
-template <int NWMAX>
-constexpr int stage_iters() { return (kMergeRows * kPStride + 64 * NWMAX - 1) / (64 * NWMAX); }
 
 struct RowId {
   int b, h, i;
@@ -48,62 +43,65 @@ __device__ __forceinline__ void hoist_args(const AttnArgs &a) {
 
 // After every thread has published its part of this workgroup's partial
 // (rows g < gcount of tile `tile_id`, split blockIdx.x), count the arrival;
-// the last workgroup of the tile stages every split's partial in LDS (all
-// loads in flight at once), weighs the splits (one lane per split in wave 0)
-// and writes the rows' outputs, combining splits in split order so that the
-// result does not depend on arrival order. smem holds kMergeRows * kPStride
-// floats.
-template <int GM, int NWMAX>
-__device__ void merge_splits(const AttnArgs &a, size_t tile_id, int g0, int gcount, int bkv, int hk,
-                             float *smem) {
+// the last workgroup of the tile to arrive merges the splits. Each of its
+// waves takes whole rows, one dim per lane (D equals the wavefront width):
+// lane j reads m and l of split j, so the max, the weights and their sum are
+// wavefront reductions; every lane reads o[dim] of a batch of splits with all
+// loads in flight, and the outputs are summed in split order so that the
+// result does not depend on the arrival order. No LDS and no barrier.
+template <int GM>
+__device__ void merge_splits(const AttnArgs &a, size_t tile_id, int g0, int gcount, int bkv,
+                             int hk) {
   constexpr int D = kHeadDim;
+  constexpr int NB = 16;              // o loads in flight per lane
+  constexpr int SS = GM * kPStride;   // floats between two splits of one row
+  static_assert(D == 64, "one lane per dim");
   __shared__ int s_last;
-  __shared__ float s_w[kMergeRows], s_inv[GM];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   wait_stores();
   __syncthreads();
-  if (threadIdx.x == 0) s_last = (arrive(&a.ws_count[tile_id]) == (uint32_t)(a.splits - 1)) ? 1 : 0;
+  if (threadIdx.x == 0) {
+    const bool last = arrive(&a.ws_count[tile_id]) == (uint32_t)(a.splits - 1);
+    if (last) reset_counter(&a.ws_count[tile_id]);  // every split has arrived
+    s_last = last;
+  }
   __syncthreads();
   if (!s_last) return;
 
-  const int n = a.splits * GM * kPStride;
-  const float *src = a.ws_part + tile_id * a.splits * GM * kPStride;
-  constexpr int kStageIters = stage_iters<NWMAX>();
-  uint32_t stage[kStageIters];
-#pragma unroll
-  for (int j = 0; j < kStageIters; ++j) {
-    const int i = threadIdx.x + j * blockDim.x;
-    if (i < n) stage[j] = fetch_u32(src + i);
-  }
-#pragma unroll
-  for (int j = 0; j < kStageIters; ++j) {
-    const int i = threadIdx.x + j * blockDim.x;
-    if (i < n) smem[i] = __builtin_bit_cast(float, stage[j]);
-  }
-  __syncthreads();
-  if (wave == 0) {
-    for (int g = 0; g < gcount; ++g) {
-      const bool on = lane < a.splits;
-      const float ms = on ? smem[(lane * GM + g) * kPStride + D] : -INFINITY;
-      const float ls = on ? smem[(lane * GM + g) * kPStride + D + 1] : 0.f;
-      const float M = groups_max<1>(ms);
-      const float w = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
-      const float L = groups_sum<1>(ls * w);
-      if (on) s_w[lane * GM + g] = w;
-      if (lane == 0) s_inv[g] = 1.f / L;
+  const int S = a.splits;  // at most 64 (the planner's bound)
+  const float *src = a.ws_part + tile_id * S * SS;
+  for (int g = wave; g < gcount; g += nw) {
+    const float *row = src + g * kPStride;
+    float mj = -INFINITY, lj = 0.f;
+    if (lane < S) {
+      mj = __builtin_bit_cast(float, fetch_u32(row + lane * SS + D));
+      lj = __builtin_bit_cast(float, fetch_u32(row + lane * SS + D + 1));
     }
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < GM * D; idx += blockDim.x) {
-    const int g = idx / D, d = idx % D;
-    if (g >= gcount) continue;
+    float ob[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      ob[j] = (j < S) ? __builtin_bit_cast(float, fetch_u32(row + j * SS + lane)) : 0.f;
+    const float M = groups_max<1>(mj);
+    const float wj = (mj == -INFINITY) ? 0.f : exp2f(mj - M);
+    const float inv = 1.f / groups_sum<1>(lj * wj);
     float O = 0.f;
-#pragma unroll 8
-    for (int sp = 0; sp < a.splits; ++sp)
-      O = fmaf(smem[(sp * GM + g) * kPStride + d], s_w[sp * GM + g], O);
-    a.out[out_row(a, row_id(a, bkv, hk, g0 + g)) + d] = O * s_inv[g];
+    for (int s0 = 0; s0 < S; s0 += NB) {
+      if (s0 > 0) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          ob[j] = (s0 + j < S) ? __builtin_bit_cast(float, fetch_u32(row + (s0 + j) * SS + lane)) : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        if (s0 + j < S) {
+          const float w = __builtin_bit_cast(
+              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), s0 + j));
+          O = fmaf(ob[j], w, O);
+        }
+      }
+    }
+    a.out[out_row(a, row_id(a, bkv, hk, g0 + g)) + lane] = O * inv;
   }
-  if (threadIdx.x == 0) reset_counter(&a.ws_count[tile_id]);
 }
 
 }  // namespace kvd

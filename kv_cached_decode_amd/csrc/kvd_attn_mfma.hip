@@ -235,9 +235,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_mfma_kernel(AttnArgs a) {
 
   // ---- lane l holds O[row c][16gq + 4i + t] = o[t][i]; merge the phases
   // that shared the row tile, then write the rows or publish the partial
-  constexpr int kWaveFloats = kWaves * kRows * (D + 2);
-  constexpr int kStageFloats = kMergeRows * kPStride;
-  constexpr int kSmem = kWaveFloats > kStageFloats ? kWaveFloats : kStageFloats;
+  constexpr int kSmem = (RW == kWaves) ? 1 : kWaves * kRows * (D + 2);
   __shared__ __attribute__((aligned(16))) float smem[kSmem];
   const size_t tile_id = (size_t)unit * a.row_tiles + blockIdx.y;
   if constexpr (RW == kWaves) {
@@ -299,7 +297,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_mfma_kernel(AttnArgs a) {
       }
     }
     if (a.splits == 1) return;
-    merge_splits<kRows, kWaves>(a, tile_id, g0, gcount, bkv, hk, smem);
+    merge_splits<kRows>(a, tile_id, g0, gcount, bkv, hk);
   }
 }
 

@@ -18,6 +18,7 @@ constexpr int kMaxCounters = 4096;
 // decode_step_self: new rows appended inside the attention launch (more are
 // appended by a separate kv_append launch first).
 constexpr int kMaxFusedRows = 16;
+constexpr int kMaxSplits = 64;  // key splits per tile: the merge gives each split one lane
 // verify_accept: (value, index) pairs one batch row may stage for its merge.
 constexpr int kMaxVerifyPartials = 2048;
 
