@@ -123,15 +123,18 @@ class Engine:
                                   out=self.out_cross[l], ws=self.ws)
 
 
-def capture_graphs(torch, eng: Engine, fused: bool):
+def capture_graphs(torch, eng: Engine, fused: bool, per_graph: int = 1):
+    """One graph per block of `per_graph` consecutive steps; graphs[i] runs
+    steps [i * per_graph, (i + 1) * per_graph)."""
     graphs = []
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(stream):
-        for s in range(S_MAX):
+        for s0 in range(0, S_MAX, per_graph):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=stream):
-                eng.step(s, fused)
+                for s in range(s0, s0 + per_graph):
+                    eng.step(s, fused)
             graphs.append(g)
     torch.cuda.current_stream().wait_stream(stream)
     torch.cuda.synchronize()
@@ -226,6 +229,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--eager", action="store_true", help="also time eager (no graph) launches")
+    ap.add_argument("--graph-steps", type=int, default=1,
+                    help="decode steps captured per graph (1: one graph per step)")
     ap.add_argument("--workload", default="greedy", choices=["greedy", "verify", "beam", "gqa"],
                     help="greedy (the headline line) or a further workload")
     ap.add_argument("--unfused", action="store_true",
@@ -261,20 +266,26 @@ def main():
     eng = Engine(torch, kb, I)
     print("bench: capturing graphs", file=sys.stderr, flush=True)
     fused = not args.unfused
-    graphs = capture_graphs(torch, eng, fused)
+    K = args.graph_steps
+    if S_MAX % K or args.steps % K or args.warmup % K:
+        print(f"--graph-steps {K} must divide {S_MAX}, --steps and --warmup", file=sys.stderr)
+        sys.exit(2)
+    graphs = capture_graphs(torch, eng, fused, K)
+    nblk = S_MAX // K
 
     # warmup
-    for i in range(args.warmup):
-        graphs[i % S_MAX].replay()
+    for i in range(args.warmup // K):
+        graphs[i % nblk].replay()
     torch.cuda.synchronize()
 
     # timed region: steps continue from where warmup stopped (wrapping at 448)
-    start = args.warmup
-    seq = [(start + i) % S_MAX for i in range(args.steps)]
+    start = args.warmup // K
+    blocks = [(start + i) % nblk for i in range(args.steps // K)]
+    seq = [b * K + j for b in blocks for j in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in seq:
-        graphs[s].replay()
+    for b in blocks:
+        graphs[b].replay()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     kv_bytes = sum(kv_bytes_per_step(s + 1) for s in seq)
@@ -311,8 +322,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD, "layers": LAYERS, "batch": 1, "heads": H,
                    "head_dim": D, "self_len": "1..448 (steps wrap)", "cross_frames": FRAMES,
-                   "launch": ("one hipGraph per step, 64 kernels (append fused into self "
-                              "attention)") if fused else "one hipGraph per step, 96 kernels"},
+                   "launch": (f"one hipGraph per {K} step(s), "
+                              + ("64 kernels per step (append fused into self attention)"
+                                 if fused else "96 kernels per step"))},
         "effective_kv_gbps": round(gbps, 1),
         "hbm_peak_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "kernel": "decode_attn_cross (attn_kernel<f16, 1>)",

@@ -50,7 +50,7 @@ int prepare_attn(AttnArgs &a, int dtype, void *ws, size_t ws_bytes) {
   const int units = a.Bkv * a.Hkv;
   const AttnPlan p = kvd::plan_attn(dtype, units, a.G, a.N, a.L, a.rope_base > 0.f);
   if (p.row_tiles > 65535 || units > 65535) return KVD_ERR_SHAPE;  // grid limits
-  if (p.splits > kvd::kMaxSplits) return KVD_ERR_SHAPE;  // the merge has one lane per split
+  if (p.splits > kvd::kMaxSplits) return KVD_ERR_SHAPE;  // the merge gives each split one lane
   a.chunk = p.chunk;
   a.splits = p.splits;
   a.row_tiles = p.row_tiles;

@@ -9,9 +9,8 @@
 // own online-softmax state (running max m, sum l, unnormalised o, in the log2
 // domain), so the key loop has no cross-group traffic; groups are merged once
 // per wave, waves once per workgroup in LDS. Splits are merged by the last
-// workgroup of the unit to arrive: it stages every split's partial in LDS
-// with all loads in flight at once and combines them in split order, so the
-// result does not depend on arrival order.
+// workgroup of the tile to arrive, in split order, so the result does not
+// depend on arrival order.
 //
 // With new rows (k_new/v_new, at most kMaxFusedRows of them), the kernel also
 // performs the cache append of the step: each workgroup rotates and rounds
@@ -240,10 +239,10 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
     }
   }
 
-  // ---- merge the waves of the workgroup in LDS
-  constexpr int kSmem = NWMAX * GM * (D + 2);
-  __shared__ __attribute__((aligned(16))) float smem[kSmem];
-  float *sm_o = smem;                       // [nw][GM][D]
+  // ---- merge the waves in LDS; then write the rows (one workgroup per
+  // tile) or publish the workgroup's partial and merge the splits
+  __shared__ __attribute__((aligned(16))) float smem[NWMAX * GM * (D + 2)];
+  float *sm_o = smem;                   // [nw][GM][D]
   float *sm_m = smem + NWMAX * GM * D;  // [nw][GM]
   float *sm_l = sm_m + NWMAX * GM;      // [nw][GM]
   if (kr == 0) {
@@ -260,12 +259,10 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
     }
   }
   __syncthreads();
-
   const size_t tile_id = (size_t)unit * a.row_tiles + rt;
   float *part = a.ws_part + (tile_id * a.splits + split) * GM * kPStride;
-  for (int idx = threadIdx.x; idx < GM * D; idx += blockDim.x) {
+  for (int idx = threadIdx.x; idx < gcount * D; idx += blockDim.x) {
     const int g = idx / D, d = idx % D;
-    if (g >= gcount) continue;
     float mw[NWMAX];
     float M = -INFINITY;
 #pragma unroll
@@ -283,8 +280,7 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
       }
     }
     if (a.splits == 1) {
-      const RowId r = row_id(a, bkv, hk, g0 + g);
-      a.out[((size_t)(r.b * a.Hq + r.h) * a.N + r.i) * D + d] = O / Ls;
+      a.out[out_row(a, row_id(a, bkv, hk, g0 + g)) + d] = O / Ls;
     } else {
       publish(part + g * kPStride + d, O);
       if (d == 0) {
@@ -294,7 +290,6 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
     }
   }
   if (a.splits == 1) return;
-
   merge_splits<GM>(a, tile_id, g0, gcount, bkv, hk);
 }
 
@@ -390,11 +385,11 @@ hipError_t launch_attn(int dtype, const AttnArgs &a, hipStream_t s) {
 
 // Split plan: a pure function of the shape (and of the tuning variables
 // KVD_ATTN_WAVES / KVD_ATTN_CHUNK when set), so results are reproducible run
-// to run. The numbers come from timing the kernel on MI355X: a CU keeps about
-// 55 KB of loads in flight, so a unit's keys are split when they exceed about
-// 128 KB (each workgroup then takes about 64 KB, one round of loads); below
-// that, one workgroup per unit avoids the cross-workgroup merge, which costs
-// three memory round trips.
+// to run. The thresholds come from timing back-to-back launches in a graph on
+// MI355X: up to 96 KB of keys a unit stays on one workgroup (16 waves above
+// 64 KB), which avoids the cross-workgroup merge (two memory round trips:
+// the arrival count, then the partials); beyond that the keys are split into
+// chunks of at least 32 KB and at most 8 splits.
 AttnPlan plan_attn(int dtype, int units, int G, int N, int L, bool rope) {
   AttnPlan p{};
   const bool use_mfma = dtype != F32 && N > 1 && env_int("KVD_ATTN_MFMA", 1) != 0;
@@ -408,14 +403,17 @@ AttnPlan plan_attn(int dtype, int units, int G, int N, int L, bool rope) {
   const bool wide_ok = p.gm <= 2 && !rope;
 
   int waves = 4, chunk;
-  if (tiles >= 256 || unit_bytes <= 128 * 1024) {
+  if (tiles >= 256 || unit_bytes <= 96 * 1024) {
     chunk = L;  // one workgroup per (unit, row tile)
     if (tiles < 256 && unit_bytes > 64 * 1024 && wide_ok) waves = kMaxWaves;
   } else {
-    chunk = (64 * 1024) / key_bytes;
+    // at least 32 KB of keys per workgroup (one round of loads for 4 waves),
+    // at most 8 splits (the merge costs grow with the split count)
+    chunk = max((32 * 1024) / key_bytes, (L + 7) / 8);
   }
   const int env_waves = env_int("KVD_ATTN_WAVES", 0);
-  if (env_waves == 1 || env_waves == 2 || env_waves == 4 || (env_waves == kMaxWaves && wide_ok))
+  if (env_waves == 1 || env_waves == 2 || env_waves == 4 ||
+      ((env_waves == 8 || env_waves == kMaxWaves) && wide_ok))
     waves = env_waves;
   const int forced = env_int("KVD_ATTN_CHUNK", 0);
   if (forced > 0) chunk = forced;

@@ -41,36 +41,23 @@ __device__ __forceinline__ void hoist_args(const AttnArgs &a) {
                "s"(f8), "s"(f9), "s"(f10), "s"(f11), "s"(a.k), "s"(a.v), "s"(a.q));
 }
 
-// After every thread has published its part of this workgroup's partial
-// (rows g < gcount of tile `tile_id`, split blockIdx.x), count the arrival;
-// the last workgroup of the tile to arrive merges the splits. Each of its
-// waves takes whole rows, one dim per lane (D equals the wavefront width):
-// lane j reads m and l of split j, so the max, the weights and their sum are
-// wavefront reductions; every lane reads o[dim] of a batch of splits with all
-// loads in flight, and the outputs are summed in split order so that the
-// result does not depend on the arrival order. No LDS and no barrier.
+// Merge of S published partials (o, m, l) of tile `tile_id`, numbered
+// 0..S-1 in a fixed order, by one wavefront: it takes rows g_first,
+// g_first + g_step, ... (< gcount), one dim per lane (D equals the wavefront
+// width). Lane j reads m and l of partial j, so the max, the weights and
+// their sum are wavefront reductions; every lane reads o[dim] of a batch of
+// partials with all loads in flight, and the outputs are summed in partial
+// order so that the result does not depend on the arrival order.
 template <int GM>
-__device__ void merge_splits(const AttnArgs &a, size_t tile_id, int g0, int gcount, int bkv,
-                             int hk) {
+__device__ void merge_rows(const AttnArgs &a, size_t tile_id, int S, int g0, int gcount, int bkv,
+                           int hk, int g_first, int g_step) {
   constexpr int D = kHeadDim;
   constexpr int NB = 16;              // o loads in flight per lane
-  constexpr int SS = GM * kPStride;   // floats between two splits of one row
+  constexpr int SS = GM * kPStride;   // floats between two partials of one row
   static_assert(D == 64, "one lane per dim");
-  __shared__ int s_last;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  wait_stores();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const bool last = arrive(&a.ws_count[tile_id]) == (uint32_t)(a.splits - 1);
-    if (last) reset_counter(&a.ws_count[tile_id]);  // every split has arrived
-    s_last = last;
-  }
-  __syncthreads();
-  if (!s_last) return;
-
-  const int S = a.splits;  // at most 64 (the planner's bound)
+  const int lane = threadIdx.x & 63;
   const float *src = a.ws_part + tile_id * S * SS;
-  for (int g = wave; g < gcount; g += nw) {
+  for (int g = g_first; g < gcount; g += g_step) {
     const float *row = src + g * kPStride;
     float mj = -INFINITY, lj = 0.f;
     if (lane < S) {
@@ -102,6 +89,27 @@ __device__ void merge_splits(const AttnArgs &a, size_t tile_id, int g0, int gcou
     }
     a.out[out_row(a, row_id(a, bkv, hk, g0 + g)) + lane] = O * inv;
   }
+}
+
+// After every thread has published its part of this workgroup's partial
+// (rows g < gcount of tile `tile_id`, partial blockIdx.x of a.splits), count
+// the arrival; the last workgroup of the tile to arrive merges the partials,
+// each of its waves taking every nw-th row. No LDS and no barrier in the
+// merge.
+template <int GM>
+__device__ void merge_splits(const AttnArgs &a, size_t tile_id, int g0, int gcount, int bkv,
+                             int hk) {
+  __shared__ int s_last;
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const bool last = arrive(&a.ws_count[tile_id]) == (uint32_t)(a.splits - 1);
+    if (last) reset_counter(&a.ws_count[tile_id]);  // every split has arrived
+    s_last = last;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  merge_rows<GM>(a, tile_id, a.splits, g0, gcount, bkv, hk, threadIdx.x >> 6, blockDim.x >> 6);
 }
 
 }  // namespace kvd
