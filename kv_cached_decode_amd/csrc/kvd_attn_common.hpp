@@ -52,7 +52,7 @@ template <int GM>
 __device__ void merge_rows(const AttnArgs &a, size_t tile_id, int S, int g0, int gcount, int bkv,
                            int hk, int g_first, int g_step) {
   constexpr int D = kHeadDim;
-  constexpr int NB = 16;              // o loads in flight per lane
+  constexpr int NB = 8;               // o loads in flight per lane (default plans: <= 8 splits)
   constexpr int SS = GM * kPStride;   // floats between two partials of one row
   static_assert(D == 64, "one lane per dim");
   const int lane = threadIdx.x & 63;
