@@ -37,7 +37,7 @@ METRIC = "decode-attn steps/s + effective KV GB/s (% HBM peak), large-v2 shape, 
 WORKLOAD = ("whisper-large-v2 greedy decode step: 32 layers x [append T=1 + self attention "
             "N=1 over len 1..448, cross attention over 1500 frames], B1, 20 heads x 64, fp16 "
             "storage / fp32 accumulate")
-KERNEL_SOURCES = ["kv_cached_decode_amd/csrc/kvd_attn.hip",
+KERNEL_SOURCES = ["kv_cached_decode_amd/csrc/kvd_attn.hip", "kv_cached_decode_amd/csrc/kvd_attn_common.hpp",
                   "kv_cached_decode_amd/csrc/kvd_device.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_cross_attention.json")
 
@@ -141,37 +141,83 @@ def capture_graphs(torch, eng: Engine, fused: bool, per_graph: int = 1):
     return graphs
 
 
-def time_cross_kernel(torch, kb, eng: Engine, reps: int = 8):
-    """Cross-attention kernel duration, measured with HIP events on the
-    launch stream: kvd_time_next_launch makes each timed launch record its
-    events at kernel begin and end (the duration rocprofv3 reports for the
-    kernel). Launches cycle over the 32 layers, so none re-reads the cache the
-    previous one read. Also returns the launch period of back-to-back batches
-    (kernel plus the gap to the next dispatch)."""
+def _event_durations(torch, kb, calls):
+    """Mean kernel duration of calls() (each makes exactly one launch), with
+    HIP events recorded at kernel begin and end on the launch stream."""
     stream = torch.cuda.current_stream()
     pairs = []
-    for r in range(reps):
-        for l in range(LAYERS):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)   # creates the events
-            b.record(stream)
-            kb.time_next_launch(a, b)
-            eng.cross(l, (r * 37 + l) % S_MAX)
-            pairs.append((a, b))
-    batches = []
-    for r in range(reps):
+    for fn in calls:
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for l in range(LAYERS):
-            eng.cross(l, (r * 41 + l) % S_MAX)
+        a.record(stream)   # creates the events
         b.record(stream)
-        batches.append((a, b))
+        kb.time_next_launch(a, b)
+        fn()
+        pairs.append((a, b))
     torch.cuda.synchronize()
-    kernel = [a.elapsed_time(b) for a, b in pairs]
-    period = [a.elapsed_time(b) / LAYERS for a, b in batches]
-    return float(np.mean(kernel)) * 1e-3, float(np.mean(period)) * 1e-3
+    return float(np.mean([a.elapsed_time(b) for a, b in pairs])) * 1e-3
+
+
+def _graph_period(torch, calls, reps: int = 20):
+    """Seconds per call when calls() run back to back inside one captured
+    graph (as in a decode step)."""
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        for fn in calls:   # warm: plans, code objects
+            fn()
+        with torch.cuda.graph(g, stream=stream):
+            for fn in calls:
+                fn()
+    torch.cuda.current_stream().wait_stream(stream)
+    g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e-3 / (reps * len(calls))
+
+
+def time_cross_kernel(torch, kb, eng: Engine, reps: int = 8):
+    """Cross-attention kernel: mean duration (HIP events at kernel begin and
+    end on the launch stream, kvd_time_next_launch) over launches that cycle
+    through the 32 layers, so none re-reads the cache the previous one read;
+    and the period of back-to-back launches over the 32 layers in a graph."""
+    calls = [lambda l=l, r=r: eng.cross(l, (r * 37 + l) % S_MAX)
+             for r in range(reps) for l in range(LAYERS)]
+    dur = _event_durations(torch, kb, calls)
+    period = _graph_period(torch, [lambda l=l: eng.cross(l, l) for l in range(LAYERS)])
+    return dur, period
+
+
+def attainable(torch, kb, eng: Engine, reps: int = 8):
+    """The same bytes read by a plain streaming-read kernel (kvd_read_probe),
+    timed the same way: K and V of the 32 layers' cross caches in turn; plus
+    the rate of that probe at other sizes (working sets cycled through a
+    1 GiB buffer)."""
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    half = CROSS_BYTES // 2
+    calls = [lambda l=l: kb.read_probe(eng.cross_c[l].k, eng.cross_c[l].v, half, sink)
+             for _ in range(reps) for l in range(LAYERS)]
+    dur = _event_durations(torch, kb, calls)
+    period = _graph_period(torch, [lambda l=l: kb.read_probe(eng.cross_c[l].k, eng.cross_c[l].v,
+                                                             half, sink) for l in range(LAYERS)])
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    curve = {}
+    for mb in (1, 2, 4, 8, 16, 64, 512):
+        n = mb << 20
+        regions = max(1, min(32, (1 << 30) // n))
+        calls = [lambda i=i: kb.read_probe(buf[i * n:(i + 1) * n], None, n, sink)
+                 for _ in range(2) for i in range(regions)]
+        t = _event_durations(torch, kb, calls)
+        curve[f"{mb}MB"] = round(n / t / 1e9, 1)
+    del buf
+    return dur, period, curve
 
 
 def cpu_baseline(target_s: float = 12.0):
@@ -300,8 +346,9 @@ def main():
         eager = args.steps / (time.perf_counter() - t1)
 
     k_avg, k_period = time_cross_kernel(torch, kb, eng)
-    achieved = CROSS_BYTES / k_avg / 1e9
+    achieved = CROSS_BYTES / k_period / 1e9
     traffic = measured_traffic()
+    p_avg, p_period, curve = attainable(torch, kb, eng)
 
     cpu = None if args.no_cpu else cpu_baseline()
 
@@ -332,9 +379,19 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
                      "bytes_per_launch": CROSS_BYTES,
-                     "avg_launch_us": round(k_avg * 1e6, 3),
-                     "launch_period_us": round(k_period * 1e6, 3),
-                     "timing": "HIP events at kernel begin/end (hipExtLaunchKernel), 256 launches"},
+                     "avg_launch_us": round(k_period * 1e6, 3),
+                     "timing": ("per-launch time of 32 back-to-back launches (one per layer) in a "
+                                "hipGraph, HIP events on the replay stream, 20 replays; "
+                                "the same kernel launched alone, HIP events at its begin/end "
+                                "(hipExtLaunchKernel, 256 launches): "
+                                f"{k_avg * 1e6:.3f} us")},
+        "attainable": {"probe": "kvd_read_probe: plain streaming read of the same K/V bytes in one "
+                                "launch, timed the same way",
+                       "avg_launch_us": round(p_period * 1e6, 3),
+                       "gbps": round(CROSS_BYTES / p_period / 1e9, 1),
+                       "alone_launch_us": round(p_avg * 1e6, 3),
+                       "cross_frac_of_attainable": round(p_period / k_period, 4),
+                       "probe_gbps_by_size_alone": curve},
         "cpu_baseline": cpu,
     }
     if eager is not None:

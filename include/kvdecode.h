@@ -184,6 +184,16 @@ int verify_accept(const void *logits, int32_t logits_dtype, int32_t B, int32_t R
 size_t kvd_attn_workspace_bytes(int32_t B, int32_t Hq, int32_t N, int32_t len_max);
 size_t kvd_verify_workspace_bytes(int32_t B, int32_t R, int32_t V);
 
+/* Measurement aid: a plain streaming read of `bytes` from a and, when b is
+ * not NULL, `bytes` from b, in one launch on `stream` (every 16-byte vector
+ * is loaded once; nothing is written except, with negligible probability, one
+ * word at `sink`). Its duration is the attainable time for a kernel that
+ * reads that many bytes once, the yardstick for the attention kernels.
+ *   a, b: device, 16-byte aligned; bytes: a multiple of 16, > 0.
+ *   sink: device uint32, 4-byte aligned.
+ * Errors: KVD_ERR_NULL, KVD_ERR_SHAPE, KVD_ERR_ALIGN, KVD_ERR_LAUNCH. */
+int kvd_read_probe(const void *a, const void *b, size_t bytes, uint32_t *sink, void *stream);
+
 /* Profiling aid: the next kernel launch made by the calling thread records
  * `start_event` when the kernel begins and `stop_event` when it ends (created
  * hipEvent_t handles, or NULL), so hipEventElapsedTime gives the kernel's own

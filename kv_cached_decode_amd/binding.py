@@ -55,6 +55,7 @@ _SIGNATURES = {
     "kvd_verify_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
     "kvd_status_string": (ctypes.c_char_p, [c_int]),
     "kvd_time_next_launch": (c_int, [c_void_p, c_void_p]),
+    "kvd_read_probe": (c_int, [c_void_p, c_void_p, c_size_t, c_void_p, c_void_p]),
 }
 
 
@@ -154,6 +155,14 @@ def time_next_launch(start: "torch.cuda.Event", stop: "torch.cuda.Event"):
     and `stop` at kernel end (both events must have been recorded once, which
     creates them)."""
     _check("kvd_time_next_launch", lib().kvd_time_next_launch(start.cuda_event, stop.cuda_event))
+
+
+def read_probe(a: torch.Tensor, b: torch.Tensor | None, nbytes: int, sink: torch.Tensor):
+    """Plain streaming read of nbytes from a (and from b): the attainable
+    rate for one launch that reads that much."""
+    _check("kvd_read_probe", lib().kvd_read_probe(
+        _dev(a, "a"), _dev(b, "b") if b is not None else None, int(nbytes), _dev(sink, "sink"),
+        _stream()))
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:

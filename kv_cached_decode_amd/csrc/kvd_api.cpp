@@ -84,6 +84,14 @@ kvd::LaunchTiming kvd::take_launch_timing() {
 
 extern "C" {
 
+int kvd_read_probe(const void *a, const void *b, size_t bytes, uint32_t *sink, void *stream) {
+  if (!a || !sink) return KVD_ERR_NULL;
+  if (bytes == 0 || bytes % 16) return KVD_ERR_SHAPE;
+  if (!aligned16(a) || (b && !aligned16(b)) || !aligned4(sink)) return KVD_ERR_ALIGN;
+  kvd::ProbeArgs p{a, b, bytes / 16, sink};
+  return status_of(kvd::launch_probe(p, static_cast<hipStream_t>(stream)));
+}
+
 int kvd_time_next_launch(void *start_event, void *stop_event) {
   g_next_timing.start = static_cast<hipEvent_t>(start_event);
   g_next_timing.stop = static_cast<hipEvent_t>(stop_event);

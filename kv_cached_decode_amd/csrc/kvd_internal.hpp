@@ -114,4 +114,11 @@ hipError_t launch_attn(int dtype, const AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_mfma(int dtype, const AttnArgs &a, hipStream_t s);
 hipError_t launch_verify(const VerifyArgs &a, hipStream_t s);
 
+struct ProbeArgs {
+  const void *a, *b;  // buffers to read (b may be NULL)
+  size_t vecs;        // 16-byte vectors read from each
+  uint32_t *sink;
+};
+hipError_t launch_probe(const ProbeArgs &a, hipStream_t s);
+
 }  // namespace kvd

@@ -118,3 +118,14 @@ def test_workspace_sizes(lib):
     assert kb.attn_workspace_bytes(0, 20, 1, 448) == 0
     assert kb.verify_workspace_bytes(1, 5, 51865) > 16384
     assert kb.verify_workspace_bytes(1, 0, 10) == 0
+
+
+def test_read_probe_validation(lib):
+    f = lib.kvd_read_probe
+    assert f(None, None, 16, FAKE, None) == -1
+    assert f(FAKE, None, 16, None, None) == -1
+    assert f(FAKE, None, 0, FAKE, None) == -2
+    assert f(FAKE, None, 24, FAKE, None) == -2            # not a multiple of 16
+    assert f(MIS, None, 16, FAKE, None) == -7
+    assert f(FAKE, MIS, 16, FAKE, None) == -7
+    assert f(FAKE, None, 16, FAKE + 2, None) == -7

@@ -466,3 +466,26 @@ def test_step_self_equals_append_then_attend(dtype, B, Hq, Hkv, N, L, rope, plan
         oc.append(k_all[:, :, old], v_all[:, :, old], rope)
     oc.append(k_all[:, :, new], v_all[:, :, new], rope)
     assert max_err(o2, O.attend_self(q, oc, 0.125, rope_base=rope)) <= TOL[dtype]
+
+
+def test_read_probe_reads_every_vector():
+    """kvd_read_probe: a buffer whose only nonzero 16-byte vector folds to the
+    probe's marker makes it store that word; an all-zero buffer stores nothing."""
+    say("case: read probe")
+    magic = 0x9E3779B9 - (1 << 32)   # as int32
+    for n_vec, hot in ((1, 0), (4096 * 1024 + 7, 4096 * 1024 + 3), (100003, 77777)):
+        buf = torch.zeros(n_vec * 4, dtype=torch.int32, device="cuda")
+        sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+        kb.read_probe(buf, None, n_vec * 16, sink)
+        torch.cuda.synchronize()
+        assert int(sink[0]) == 0
+        buf[hot * 4] = magic
+        kb.read_probe(buf, None, n_vec * 16, sink)
+        torch.cuda.synchronize()
+        assert int(sink[0]) == magic
+        # the same vector in the second buffer
+        other = torch.zeros_like(buf)
+        sink.zero_()
+        kb.read_probe(other, buf, n_vec * 16, sink)
+        torch.cuda.synchronize()
+        assert int(sink[0]) == magic
