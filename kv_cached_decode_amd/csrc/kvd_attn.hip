@@ -347,7 +347,8 @@ AttnPlan plan_attn_mfma(int units, int G, int L) {
     p.rw = 1;
     p.row_tiles = tiles16;
     const int min_chunk = kStep * 4;
-    int chunk = (unit_bytes <= 128 * 1024) ? L : (64 * 1024) / (2 * kHeadDim * 2);
+    // as the streaming plan, with the one-workgroup limit at 64 KB (measured)
+    int chunk = (unit_bytes <= 64 * 1024) ? L : max(min_chunk, (L + 7) / 8);
     if (forced > 0) chunk = forced;
     chunk = ((chunk + min_chunk - 1) / min_chunk) * min_chunk;
     const int max_splits = kMaxSplits;
