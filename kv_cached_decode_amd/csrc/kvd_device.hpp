@@ -127,20 +127,33 @@ constexpr int kDppRowMirror = 0x140;   // lane i <- lane 15-i within 16 lanes
 constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7-i within 8 lanes
 
 constexpr int kDppRowRor8 = 0x128;     // lane i <- lane (i + 8) mod 16 within 16 lanes
-constexpr int kSwizzleSwap16 = 0x401F; // ds_swizzle bit mode: lane i <- lane i ^ 16
 
-// Value of lane (this lane ^ 8), (^ 16), (^ 32) in a 64-lane wavefront.
+// Value of lane (this lane ^ 8) in a 64-lane wavefront.
 __device__ __forceinline__ float lane_xor8(float x) { return dpp_mov<kDppRowRor8>(x); }
-__device__ __forceinline__ float lane_xor16(float x) {
-  return __builtin_bit_cast(float,
-                            __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), kSwizzleSwap16));
+
+// v_permlane16_swap / v_permlane32_swap with both operands x leave, in every
+// lane, the pair {x[lane], x[lane ^ 16]} (resp. ^ 32) in the two results, in
+// an order that depends on the lane; sum and max are symmetric, so they need
+// no select. (Lane layout checked on gfx950.)
+__device__ __forceinline__ float pair_sum16(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
-__device__ __forceinline__ float lane_xor32(float x) {
-  // v_permlane32_swap with both operands x: the first result holds x's upper
-  // half in lanes 32..63's place of the lower half and vice versa
+__device__ __forceinline__ float pair_max16(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ __forceinline__ float pair_sum32(float x) {
   const unsigned u = __builtin_bit_cast(unsigned, x);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __builtin_bit_cast(float, (threadIdx.x & 32) ? (unsigned)r[0] : (unsigned)r[1]);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+__device__ __forceinline__ float pair_max32(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
 }
 
 // Reduce over the 64 / FROM aligned groups of FROM lanes (lanes that differ
@@ -152,8 +165,8 @@ __device__ __forceinline__ float groups_max(float x) {
   if constexpr (FROM <= 2) x = fmaxf(x, dpp_mov<kDppQuadXor2>(x));
   if constexpr (FROM <= 4) x = fmaxf(x, dpp_mov<kDppHalfMirror>(x));
   if constexpr (FROM <= 8) x = fmaxf(x, lane_xor8(x));
-  if constexpr (FROM <= 16) x = fmaxf(x, lane_xor16(x));
-  return fmaxf(x, lane_xor32(x));
+  if constexpr (FROM <= 16) x = pair_max16(x);
+  return pair_max32(x);
 }
 template <int FROM>
 __device__ __forceinline__ float groups_sum(float x) {
@@ -161,8 +174,8 @@ __device__ __forceinline__ float groups_sum(float x) {
   if constexpr (FROM <= 2) x += dpp_mov<kDppQuadXor2>(x);
   if constexpr (FROM <= 4) x += dpp_mov<kDppHalfMirror>(x);
   if constexpr (FROM <= 8) x += lane_xor8(x);
-  if constexpr (FROM <= 16) x += lane_xor16(x);
-  return x + lane_xor32(x);
+  if constexpr (FROM <= 16) x = pair_sum16(x);
+  return pair_sum32(x);
 }
 
 template <int LANES> __device__ __forceinline__ float group_sum(float x);
