@@ -133,6 +133,7 @@ int kv_append(const kvd_cache *cache, const void *k_new, const void *v_new, int3
   a.pos = pos;
   a.rope_base = rope_base;
   a.rope_step = rope_step_of(rope_base);
+  a.rope_ratio = exp2(-a.rope_step);
   return status_of(kvd::launch_append(cache->dtype, a, static_cast<hipStream_t>(stream)));
 }
 
@@ -194,6 +195,7 @@ int prepare_self(AttnArgs &a, const void *q, const void *k_new, const void *v_ne
   a.scale_log2 = scale * 1.4426950408889634f;
   a.rope_base = rope_base;
   a.rope_step = rope_step_of(rope_base);
+  a.rope_ratio = exp2(-a.rope_step);
   return prepare_attn(a, cache->dtype, ws, ws_bytes);
 }
 
@@ -234,6 +236,7 @@ int decode_step_self(const void *q, const void *k_new, const void *v_new, int32_
     ap.pos = len - N;
     ap.rope_base = rope_base;
     ap.rope_step = rope_step_of(rope_base);
+    ap.rope_ratio = exp2(-ap.rope_step);
     const int sa = status_of(kvd::launch_append(cache->dtype, ap, s));
     if (sa) return sa;
   }

@@ -111,6 +111,15 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
     }
   }
 
+  // ---- rotary cos / sin at the first row's position: no memory access, so
+  // they are computed while the loads above are in flight
+  float rc[ROPE ? VE : 1], rs[ROPE ? VE : 1];  // cos / sin at position rpos
+  int rpos = -1;
+  if constexpr (ROPE) {
+    rpos = a.causal_base + row_id(a, bkv, hk, g0).i;
+    rope_slice_cs<DT>(ds, rpos, RopeStep{a.rope_step, a.rope_ratio}, rc, rs);
+  }
+
   // ---- fused append: the new rows of this key range are rotated and
   // rounded once into LDS (the loop reads them there); row tile 0 also writes
   // them into the cache
@@ -124,7 +133,7 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
       const int r = t / HALF_VECS, j = t % HALF_VECS;
       const int pos = nb0 + r;
       const size_t src = (size_t)(pos - a.new_base) * ROWB;
-      const PairChunks c = load_pair<DT>(kn + src, vn + src, j, pos, ROPE ? a.rope_step : 0.0);
+      const PairChunks c = load_pair<DT>(kn + src, vn + src, j, pos, RopeStep{ROPE ? a.rope_step : 0.0, a.rope_ratio});
       s_new[r * VPR + j] = c.klo;
       s_new[r * VPR + j + VPR / 2] = c.khi;
       s_new[(kMaxFusedRows + r) * VPR + j] = c.vlo;
@@ -136,8 +145,6 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
 
   // ---- query rows: rotate (fp32), fold in scale*log2(e)
   float qf[GM][VE];
-  float rc[ROPE ? VE : 1], rs[ROPE ? VE : 1];  // cos / sin at position rpos
-  int rpos = -1;
 #pragma unroll
   for (int g = 0; g < GM; ++g) {
 #pragma unroll
@@ -147,7 +154,7 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
         const RowId r = row_id(a, bkv, hk, g0 + g);
         const int pos = a.causal_base + r.i;
         if (pos != rpos) {  // rows of one position share their cos / sin
-          rope_slice_cs<DT>(ds, pos, a.rope_step, rc, rs);
+          rope_slice_cs<DT>(ds, pos, RopeStep{a.rope_step, a.rope_ratio}, rc, rs);
           rpos = pos;
         }
         rope_slice_f32<DT>(qraw[g], qpart[g], ds, rc, rs, qf[g]);

@@ -108,6 +108,12 @@ __global__ __launch_bounds__(64 * kWaves) void attn_mfma_kernel(AttnArgs a) {
     qraw[1] = load16(qrow + 64 + gq * 16);
   }
 
+  // ---- rotary cos / sin of the query row's pairs: no memory access, so
+  // they are computed while the loads above are in flight
+  float qc[ROPE ? 8 : 1], qs[ROPE ? 8 : 1];
+  if constexpr (ROPE)
+    rope_cos_sin_run<8>(a.causal_base + r.i, gq * 8, RopeStep{a.rope_step, a.rope_ratio}, qc, qs);
+
   // ---- fused append (as in the streaming kernel)
   __shared__ u32x4 s_new[FUSED ? 2 * kMaxFusedRows * VPR : 1];
   if constexpr (FUSED) {
@@ -119,7 +125,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_mfma_kernel(AttnArgs a) {
       const int rr = t / HALF_VECS, j = t % HALF_VECS;
       const int pos = nb0 + rr;
       const size_t src = (size_t)(pos - a.new_base) * ROWB;
-      const PairChunks ch = load_pair<DT>(kn + src, vn + src, j, pos, ROPE ? a.rope_step : 0.0);
+      const PairChunks ch = load_pair<DT>(kn + src, vn + src, j, pos, RopeStep{ROPE ? a.rope_step : 0.0, a.rope_ratio});
       s_new[rr * VPR + j] = ch.klo;
       s_new[rr * VPR + j + VPR / 2] = ch.khi;
       s_new[(kMaxFusedRows + rr) * VPR + j] = ch.vlo;
@@ -135,11 +141,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_mfma_kernel(AttnArgs a) {
     unpack16<DT>(qraw[0], x0);
     unpack16<DT>(qraw[1], x1);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float cs, sn;
-      rope_cos_sin(a.causal_base + r.i, gq * 8 + e, a.rope_step, cs, sn);
-      rope_rotate(x0[e], x1[e], cs, sn);
-    }
+    for (int e = 0; e < 8; ++e) rope_rotate(x0[e], x1[e], qc[e], qs[e]);
     split_hi_lo<DT>(x0, qhi[0], qlo[0]);
     split_hi_lo<DT>(x1, qhi[1], qlo[1]);
   } else {

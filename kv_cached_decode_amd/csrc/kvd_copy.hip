@@ -28,7 +28,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
   const size_t dst = ((size_t)bh * a.S_max + a.pos + t) * ROWB;
   const PairChunks c = load_pair<DT>(static_cast<const char *>(a.k_new) + src,
                                      static_cast<const char *>(a.v_new) + src, j, a.pos + t,
-                                     a.rope_step);
+                                     RopeStep{a.rope_step, a.rope_ratio});
   store_pair<DT>(static_cast<char *>(a.k_cache) + dst, static_cast<char *>(a.v_cache) + dst, j, c);
 }
 

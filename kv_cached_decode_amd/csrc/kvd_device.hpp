@@ -92,18 +92,45 @@ template <int DT> __device__ __forceinline__ u32x4 pack16(const float *in) {
   return v;
 }
 
-// Rotary embedding of pair (i, i + D/2) at absolute position pos: angle
-// pos * theta_i with theta_i = base^(-2i/D) = 2^(-i * step), step = 2 log2(base)
-// / D computed on the host in fp64. The angle is formed and reduced modulo 2 pi
-// in fp64 (two-constant Cody-Waite), then cos / sin are evaluated in fp32 on
-// the reduced angle (|r| <= pi).
-__device__ __forceinline__ void rope_cos_sin(int pos, int i, double step, float &c, float &s) {
-  const double theta = exp2(-(double)i * step);
-  const double ang = (double)pos * theta;
-  const double k = rint(ang * 0.15915494309189535);  // 1 / (2 pi)
-  double r = fma(-k, 6.283185307179586, ang);        // 2 pi, high part
-  r = fma(-k, 2.4492935982947064e-16, r);            // 2 pi, low part
-  sincosf((float)r, &s, &c);
+// Rotary angles. Pair (i, i + D/2) at absolute position pos turns by
+// pos * theta_i, theta_i = base^(-2i/D) = 2^(-i * step); the host passes
+// step = 2 log2(base) / D and ratio = 2^(-step) in fp64 (step == 0: no
+// rotation). For a run of n consecutive pairs i0 .. i0 + n - 1, theta_i0 comes
+// from one fp64 exp2 and each next theta from one fp64 multiply by ratio. The
+// angle is formed and reduced modulo pi/2 in fp64 (Cody-Waite reduction with
+// pi/2 split in two constants), so the reduced angle y (|y| <= pi/4) is
+// accurate to far below fp32 rounding; cos y and sin y come from their Taylor
+// polynomials in fp32 (degree 10 and 9: truncation below 2^-28 on |y| <= pi/4)
+// and the quadrant k mod 4 maps them onto cos / sin of the full angle.
+struct RopeStep {
+  double step, ratio;
+};
+
+template <int n>
+__device__ __forceinline__ void rope_cos_sin_run(int pos, int i0, RopeStep r, float *c, float *s) {
+  double theta = exp2(-(double)i0 * r.step);
+#pragma unroll
+  for (int e = 0; e < n; ++e) {
+    const double ang = (double)pos * theta;       // >= 0
+    const double k = rint(ang * 0.6366197723675814);   // 2 / pi
+    double yd = fma(-k, 1.5707963267948966, ang);      // pi/2, high part
+    yd = fma(-k, 6.123233995736766e-17, yd);           // pi/2, low part
+    const float y = (float)yd, y2 = y * y;
+    float ps = fmaf(y2, 2.7557319e-06f, -1.9841270e-04f);  // 1/9!, -1/7!
+    ps = fmaf(ps, y2, 8.3333333e-03f);                     // 1/5!
+    ps = fmaf(ps, y2, -1.6666667e-01f);                    // -1/3!
+    const float sy = fmaf(ps * y2, y, y);
+    float pc = fmaf(y2, -2.7557319e-07f, 2.4801587e-05f);  // -1/10!, 1/8!
+    pc = fmaf(pc, y2, -1.3888889e-03f);                    // -1/6!
+    pc = fmaf(pc, y2, 4.1666668e-02f);                     // 1/4!
+    pc = fmaf(pc, y2, -0.5f);
+    const float cy = fmaf(pc, y2, 1.0f);
+    const int q = (int)((long long)k & 3);
+    const float sv = (q & 1) ? cy : sy, cv = (q & 1) ? sy : cy;
+    s[e] = (q & 2) ? -sv : sv;                        // sin: s, c, -s, -c
+    c[e] = (q == 1 || q == 2) ? -cv : cv;             // cos: c, -s, -c, s
+    theta *= r.ratio;
+  }
 }
 __device__ __forceinline__ void rope_rotate(float &lo, float &hi, float c, float s) {
   const float l = lo, h = hi;
@@ -195,11 +222,10 @@ template <> __device__ __forceinline__ float group_sum<16>(float x) {
 // position pos (slice ds and ds ^ (LPR/2) hold the two halves of the pairs
 // (ds % (LPR/2)) * VE + e).
 template <int DT>
-__device__ __forceinline__ void rope_slice_cs(int ds, int pos, double step, float *c, float *s) {
+__device__ __forceinline__ void rope_slice_cs(int ds, int pos, RopeStep r, float *c, float *s) {
   constexpr int VE = vec_elems<DT>();
   constexpr int LPR = kHeadDim / VE;
-#pragma unroll
-  for (int e = 0; e < VE; ++e) rope_cos_sin(pos, (ds % (LPR / 2)) * VE + e, step, c[e], s[e]);
+  rope_cos_sin_run<VE>(pos, (ds % (LPR / 2)) * VE, r, c, s);
 }
 
 // The 16-byte slice `ds` of a query row rotated with those cos / sin, in fp32
@@ -259,10 +285,10 @@ __device__ __forceinline__ void reset_counter(uint32_t *counter) {
 struct PairChunks {
   u32x4 klo, khi, vlo, vhi;
 };
-// step = 2 log2(base) / D, or 0: no rotation.
+// r.step == 0: no rotation.
 template <int DT>
 __device__ __forceinline__ PairChunks load_pair(const char *k_src, const char *v_src, int j,
-                                                int pos, double step) {
+                                                int pos, RopeStep r) {
   constexpr int VE = vec_elems<DT>();
   constexpr int EB = Storage<DT>::bytes;
   const int lo_off = j * VE * EB, hi_off = (kHeadDim / 2 + j * VE) * EB;
@@ -271,16 +297,13 @@ __device__ __forceinline__ PairChunks load_pair(const char *k_src, const char *v
   c.khi = load16(k_src + hi_off);
   c.vlo = load16(v_src + lo_off);
   c.vhi = load16(v_src + hi_off);
-  if (step > 0.0) {
-    float lo[VE], hi[VE];
+  if (r.step > 0.0) {
+    float lo[VE], hi[VE], cs[VE], sn[VE];
     unpack16<DT>(c.klo, lo);
     unpack16<DT>(c.khi, hi);
+    rope_cos_sin_run<VE>(pos, j * VE, r, cs, sn);
 #pragma unroll
-    for (int e = 0; e < VE; ++e) {
-      float cs, sn;
-      rope_cos_sin(pos, j * VE + e, step, cs, sn);
-      rope_rotate(lo[e], hi[e], cs, sn);
-    }
+    for (int e = 0; e < VE; ++e) rope_rotate(lo[e], hi[e], cs[e], sn[e]);
     c.klo = pack16<DT>(lo);
     c.khi = pack16<DT>(hi);
   }

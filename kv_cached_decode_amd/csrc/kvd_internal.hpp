@@ -28,6 +28,7 @@ struct AppendArgs {
   int B, H, S_max, T, pos;
   float rope_base;               // > 0: rotate keys at pos + t
   double rope_step;              // 2 log2(rope_base) / D (0: no rotation)
+  double rope_ratio;             // 2^(-rope_step)
 };
 
 struct ReorderArgs {
@@ -56,6 +57,7 @@ struct AttnArgs {
   float scale_log2;              // scale * log2(e)
   float rope_base;               // > 0: rotate q at causal_base + i (and new keys)
   double rope_step;              // 2 log2(rope_base) / D (0: no rotation)
+  double rope_ratio;             // 2^(-rope_step)
   // plan
   int chunk;                     // keys per workgroup
   int splits;                    // workgroups per (unit, row tile)
