@@ -82,9 +82,10 @@ typedef struct kvd_cache {
  *   k_new, v_new: device, [B][H][T][D] in cache->dtype.
  *   rope_base > 0: each key row is first rotated at its absolute position
  *     pos + t (pairs (i, i + D/2) turn by (pos + t) * rope_base^(-2i/D));
- *     the angle is formed and reduced modulo 2 pi in fp64, its cos / sin and
- *     the rotation are computed in fp32, and the result is rounded to
- *     nearest-even into the cache; values are copied as they are.
+ *     the angle is formed and reduced modulo pi/2 in fp64, its cos / sin
+ *     (fp32 polynomials, error below 2^-23) and the rotation are computed in
+ *     fp32, and the result is rounded to nearest-even into the cache; values
+ *     are copied as they are.
  *     rope_base == 0: a bit-exact copy of both.
  * Errors: KVD_ERR_NULL, KVD_ERR_SHAPE (T < 1, pos < 0, D != 64, B/H < 1),
  *   KVD_ERR_DTYPE, KVD_ERR_CAPACITY (pos + T > S_max), KVD_ERR_ALIGN. */
