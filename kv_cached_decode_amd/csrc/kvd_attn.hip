@@ -79,22 +79,44 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
   }
   const int kend = min(kspan, kvis);
 
-  // ---- first tile of cached keys: in flight before anything else waits
-  u32x4 kv[kSteps], vv[kSteps];
-  auto load_tile = [&](int t) {
+  // ---- first tiles of cached keys: in flight before anything else waits.
+  // Without new rows, with few query rows and 4 waves (registers to spare;
+  // measured to pay only there), each wave keeps two tiles in flight: tile
+  // i + 2 is loaded into the buffer tile i just freed.
+  constexpr int PF = (!FUSED && GM <= 2 && NWMAX <= 4) ? 2 : 1;
+  u32x4 kA[kSteps], vA[kSteps], kB[PF == 2 ? kSteps : 1], vB[PF == 2 ? kSteps : 1];
+  auto load_tile = [&](u32x4 *kd, u32x4 *vd, int t) {
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
       const int key = t + s * RPL + kr;
-      kv[s] = u32x4{0, 0, 0, 0};
-      vv[s] = u32x4{0, 0, 0, 0};
+      kd[s] = u32x4{0, 0, 0, 0};
+      vd[s] = u32x4{0, 0, 0, 0};
       if (key < kend && (!FUSED || key < nb0)) {
-        kv[s] = load16(kc + (size_t)key * ROWB + ds * 16);
-        vv[s] = load16(vc + (size_t)key * ROWB + ds * 16);
+        kd[s] = load16(kc + (size_t)key * ROWB + ds * 16);
+        vd[s] = load16(vc + (size_t)key * ROWB + ds * 16);
       }
     }
   };
+  auto load_a = [&](int t) {  // the same into (kA, vA), written out
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      const int key = t + s * RPL + kr;
+      kA[s] = u32x4{0, 0, 0, 0};
+      vA[s] = u32x4{0, 0, 0, 0};
+      if (key < kend && (!FUSED || key < nb0)) {
+        kA[s] = load16(kc + (size_t)key * ROWB + ds * 16);
+        vA[s] = load16(vc + (size_t)key * ROWB + ds * 16);
+      }
+    }
+  };
+  const int stride = nw * TILE;
   int t0 = k0 + wave * TILE;
-  if (t0 < kend) load_tile(t0);
+  if constexpr (PF == 2) {  // (each form measured fastest for its kernels)
+    if (t0 < kend) load_tile(kA, vA, t0);
+    if (t0 + stride < kend) load_tile(kB, vB, t0 + stride);
+  } else {
+    if (t0 < kend) load_a(t0);
+  }
 
   // ---- query rows: their loads go out before anything waits
   u32x4 qraw[GM], qpart[GM];
@@ -175,7 +197,8 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
     for (int e = 0; e < VE; ++e) o[g][e] = 0.f;
   }
 
-  while (t0 < kend) {
+  // one tile: the keys [t0, t0 + TILE) of this wave, held in (kv, vv)
+  auto step = [&](u32x4 *kv, u32x4 *vv) {
     if constexpr (FUSED) {  // new rows of this tile come from LDS
 #pragma unroll
       for (int s = 0; s < kSteps; ++s) {
@@ -207,8 +230,9 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
     float vf[kSteps][VE];
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) unpack16<DT>(vv[s], vf[s]);
-    t0 += nw * TILE;
-    if (t0 < kend) load_tile(t0);  // next tile in flight during this one's math
+    // the buffer is free: the tile PF strides ahead goes in flight during
+    // this one's math
+    if (t0 + PF * stride < kend) load_tile(kv, vv, t0 + PF * stride);
 #pragma unroll
     for (int g = 0; g < GM; ++g) {
       float mt = sc[0][g];
@@ -229,6 +253,74 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
         }
         l[g] = ls;
         m[g] = mn;
+      }
+    }
+    t0 += stride;
+  };
+  if constexpr (PF == 2) {
+    while (t0 < kend) {
+      step(kA, vA);
+      if (t0 >= kend) break;
+      step(kB, vB);
+    }
+  } else {
+    // the same tile step written out on the one buffer (the compiler
+    // schedules this form better than the step above called through pointers)
+    while (t0 < kend) {
+      if constexpr (FUSED) {
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+          const int key = t0 + s * RPL + kr;
+          if (key < kend && key >= nb0) {
+            kA[s] = s_new[(key - nb0) * VPR + ds];
+            vA[s] = s_new[(kMaxFusedRows + key - nb0) * VPR + ds];
+          }
+        }
+      }
+      float sc[kSteps][GM];
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) {
+        float kf[VE];
+        unpack16<DT>(kA[s], kf);
+        const int key = t0 + s * RPL + kr;
+#pragma unroll
+        for (int g = 0; g < GM; ++g) {
+          sc[s][g] = -INFINITY;
+          if (g < gcount) {
+            float d = 0.f;
+#pragma unroll
+            for (int e = 0; e < VE; ++e) d = fmaf(qf[g][e], kf[e], d);
+            d = group_sum<LPR>(d);
+            if (key < lim[g] && key < kend) sc[s][g] = d;
+          }
+        }
+      }
+      float vf[kSteps][VE];
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) unpack16<DT>(vA[s], vf[s]);
+      t0 += stride;
+      if (t0 < kend) load_a(t0);
+#pragma unroll
+      for (int g = 0; g < GM; ++g) {
+        float mt = sc[0][g];
+#pragma unroll
+        for (int s = 1; s < kSteps; ++s) mt = fmaxf(mt, sc[s][g]);
+        const float mn = fmaxf(m[g], mt);
+        if (mn != -INFINITY) {
+          const float alpha = exp2f(m[g] - mn);
+          float ls = l[g] * alpha;
+#pragma unroll
+          for (int e = 0; e < VE; ++e) o[g][e] *= alpha;
+#pragma unroll
+          for (int s = 0; s < kSteps; ++s) {
+            const float p = exp2f(sc[s][g] - mn);
+            ls += p;
+#pragma unroll
+            for (int e = 0; e < VE; ++e) o[g][e] = fmaf(p, vf[s][e], o[g][e]);
+          }
+          l[g] = ls;
+          m[g] = mn;
+        }
       }
     }
   }
@@ -310,12 +402,11 @@ void launch_gm(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
   }
 }
 
-// The 16-wave variant (one wide workgroup per unit): at most 2 query rows and
-// no rotary work, so that it fits 128 registers without spilling.
+// The 16-wave variant (one wide workgroup per unit): one query row and no
+// rotary work, so that it fits 128 registers without spilling.
 template <int DT, bool FUSED>
 void launch_wide(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
-  if (a.gm == 1) launch_kernel(attn_kernel<DT, 1, FUSED, kMaxWaves, false>, grid, block, s, a);
-  else launch_kernel(attn_kernel<DT, 2, FUSED, kMaxWaves, false>, grid, block, s, a);
+  launch_kernel(attn_kernel<DT, 1, FUSED, kMaxWaves, false>, grid, block, s, a);
 }
 
 template <int DT, bool FUSED>
@@ -408,7 +499,7 @@ AttnPlan plan_attn(int dtype, int units, int G, int N, int L, bool rope) {
   const int key_bytes = 2 * kHeadDim * ((dtype == F32) ? 4 : 2);  // K + V row
   const long unit_bytes = (long)L * key_bytes;
   const size_t tiles = (size_t)units * p.row_tiles;
-  const bool wide_ok = p.gm <= 2 && !rope;
+  const bool wide_ok = p.gm == 1 && !rope;
 
   int waves = 4, chunk;
   if (tiles >= 256 || unit_bytes <= 96 * 1024) {
