@@ -485,7 +485,7 @@ hipError_t launch_attn(int dtype, const AttnArgs &a, hipStream_t s) {
 // Split plan: a pure function of the shape (and of the tuning variables
 // KVD_ATTN_WAVES / KVD_ATTN_CHUNK when set), so results are reproducible run
 // to run. The thresholds come from timing back-to-back launches in a graph on
-// MI355X: up to 96 KB of keys a unit stays on one workgroup (16 waves above
+// MI355X: up to 96 KB of keys a unit stays on one workgroup (8 waves above
 // 64 KB), which avoids the cross-workgroup merge (two memory round trips:
 // the arrival count, then the partials); beyond that the keys are split into
 // chunks of at least 32 KB and at most 8 splits.
@@ -504,7 +504,7 @@ AttnPlan plan_attn(int dtype, int units, int G, int N, int L, bool rope) {
   int waves = 4, chunk;
   if (tiles >= 256 || unit_bytes <= 96 * 1024) {
     chunk = L;  // one workgroup per (unit, row tile)
-    if (tiles < 256 && unit_bytes > 64 * 1024 && wide_ok) waves = kMaxWaves;
+    if (tiles < 256 && unit_bytes > 64 * 1024 && wide_ok) waves = 8;  // measured: 8 beats 16
   } else {
     // at least 32 KB of keys per workgroup (one round of loads for 4 waves),
     // at most 8 splits (the merge costs grow with the split count)
