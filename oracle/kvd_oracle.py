@@ -29,7 +29,11 @@ theta_i = base^(-2i/D) and is applied to keys before they are cached and to
 queries at attention time; argmax ties go to the lowest index; verify row i
 is compared with draft i. The rotary variant itself is a reading (the pages
 name only the start_pos argument): parity for it is pinned to the RoFormer
-identities, not to the pages.
+identities, not to the pages. Beam-search candidate scoring follows the
+decoder's update steps on [W]; the readings there: natural-log softmax, each
+beam's K + 1 best tokens with equal values in index order, candidates with
+equal scores in the order beam then rank, and end-of-text candidates met
+before the K-th next beam recorded as finished.
 """
 from __future__ import annotations
 
@@ -292,6 +296,65 @@ def verify_accept(logits: np.ndarray, draft: np.ndarray):
     for b in range(B):
         acc[b], nxt[b] = accept(am[b], draft[b])
     return am, acc, nxt
+
+
+# ---------------------------------------------------------------------------
+# Beam-search candidate scoring ([W] beam-search decoder, update steps 1-3;
+# step 4 is reorder() above).
+# ---------------------------------------------------------------------------
+
+
+def log_softmax_rows(logits: np.ndarray) -> np.ndarray:
+    """Natural-log softmax over the last axis, in float64, max-subtracted."""
+    x = np.asarray(logits, dtype=np.float64)
+    m = x.max(axis=-1, keepdims=True)
+    return x - (m + np.log(np.exp(x - m).sum(axis=-1, keepdims=True)))
+
+
+def beam_select(logits: np.ndarray, sum_logprobs: np.ndarray, eot: int):
+    """One beam-search update for each audio row b of logits [B, K, V] (K
+    beams) with running scores sum_logprobs [B, K]:
+
+      1. log-probabilities of each beam's row, and its K + 1 best tokens
+         (larger first, equal values: lower token first);
+      2. every candidate (beam j, token t) scores sum_logprobs[b, j] + logp;
+      3. candidates in order of score (larger first; equal scores keep the
+         order beam, then rank) are taken one by one: an end-of-text token is
+         recorded as finished (its beam and score), any other token becomes
+         the next beam, until K next beams are chosen.
+
+    Returns (parent [B, K], token [B, K], score [B, K], finished_count [B],
+    finished_parent [B, K] (-1 past the count), finished_score [B, K]
+    (nan past the count)).
+    """
+    B, K, V = logits.shape
+    lp = log_softmax_rows(logits)
+    parent = np.empty((B, K), dtype=np.int32)
+    token = np.empty((B, K), dtype=np.int32)
+    score = np.empty((B, K), dtype=np.float64)
+    fin_count = np.zeros(B, dtype=np.int32)
+    fin_parent = np.full((B, K), -1, dtype=np.int32)
+    fin_score = np.full((B, K), np.nan)
+    idx = np.arange(V)
+    for b in range(B):
+        cands = []
+        for j in range(K):
+            order = np.lexsort((idx, -lp[b, j]))[:K + 1]   # by -logp, then index
+            for r, t in enumerate(order):
+                cands.append((float(sum_logprobs[b, j]) + lp[b, j, t], j, r, int(t)))
+        cands.sort(key=lambda c: (-c[0], c[1], c[2]))
+        kept = 0
+        for sc, j, _, t in cands:
+            if t == eot:
+                fin_parent[b, fin_count[b]] = j
+                fin_score[b, fin_count[b]] = sc
+                fin_count[b] += 1
+            else:
+                parent[b, kept], token[b, kept], score[b, kept] = j, t, sc
+                kept += 1
+                if kept == K:
+                    break
+    return parent, token, score, fin_count, fin_parent, fin_score
 
 
 # ---------------------------------------------------------------------------

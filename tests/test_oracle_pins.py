@@ -375,3 +375,90 @@ def test_accept_length_distribution_at_p_075():
     assert np.all(np.abs(counts - trials * p) < 4 * sd + 1)
     mean_tokens = (counts * np.array([1, 2, 3, 4, 5, 5])).sum() / trials
     assert mean_tokens == pytest.approx(sum(p * np.array([1, 2, 3, 4, 5, 5])), abs=0.15)
+
+
+# ---------------------------------------------------------------------------
+# Beam-search candidate scoring
+# ---------------------------------------------------------------------------
+
+
+def test_log_softmax_matches_scipy():
+    from scipy.special import log_softmax
+    g = np.random.default_rng(11)
+    x = g.standard_normal((3, 5, 1000)) * 4
+    np.testing.assert_allclose(O.log_softmax_rows(x), log_softmax(x, axis=-1), rtol=0, atol=1e-12)
+
+
+def test_beam_select_hand_example():
+    ex = json.load(open(os.path.join(GOLDEN, "beam_select_hand_example.json")))
+    parent, token, score, fc, fp, fs = O.beam_select(np.array(ex["logits"]), np.array(ex["sum_logprobs"]),
+                                                     ex["eot"])
+    assert parent.tolist() == ex["parent"] and token.tolist() == ex["token"]
+    np.testing.assert_allclose(score, ex["score"], rtol=0, atol=1e-15)
+    assert fc.tolist() == ex["finished_count"] and fp.tolist() == ex["finished_parent"]
+    assert abs(fs[0, 0] - ex["finished_score"][0][0]) < 1e-15 and np.isnan(fs[0, 1])
+
+
+def _beam_brute_force(logits, sums, eot):
+    """Every (beam, token) pair of the full vocabulary, not only each beam's
+    K + 1 best: the result must not change (a token outside a beam's K + 1
+    best has K better non-end-of-text tokens in its own beam)."""
+    B, K, V = logits.shape
+    lp = O.log_softmax_rows(logits)
+    out = []
+    for b in range(B):
+        cands = []
+        for j in range(K):
+            rank = {int(t): r for r, t in enumerate(sorted(range(V), key=lambda t: (-lp[b, j, t], t)))}
+            for t in range(V):
+                cands.append((sums[b, j] + lp[b, j, t], j, rank[t], t))
+        cands.sort(key=lambda c: (-c[0], c[1], c[2]))
+        kept, fin = [], []
+        for sc, j, _, t in cands:
+            if t == eot:
+                fin.append((j, sc))
+            else:
+                kept.append((j, t, sc))
+                if len(kept) == K:
+                    break
+        out.append((kept, fin))
+    return out
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_beam_select_equals_brute_force(seed):
+    g = np.random.default_rng([12, seed])
+    B, K, V = 2, 1 + seed % 4, 9
+    logits = np.round(g.standard_normal((B, K, V)) * 2) / 2      # half-integers: ties happen
+    sums = np.round(g.standard_normal((B, K)) * 2) / 2
+    eot = int(g.integers(0, V))
+    logits[0, 0, eot] = logits[0, 0].max() + 1                  # some beam's best is end-of-text
+    parent, token, score, fc, fp, fs = O.beam_select(logits, sums, eot)
+    for b, (kept, fin) in enumerate(_beam_brute_force(logits, sums, eot)):
+        assert [(int(parent[b, i]), int(token[b, i])) for i in range(K)] == [(j, t) for j, t, _ in kept]
+        np.testing.assert_allclose(score[b], [s for _, _, s in kept], rtol=0, atol=1e-12)
+        assert fc[b] == len(fin)
+        assert [int(fp[b, i]) for i in range(fc[b])] == [j for j, _ in fin]
+
+
+def test_beam_select_one_beam_is_greedy_argmax():
+    g = np.random.default_rng(13)
+    logits = g.standard_normal((4, 1, 500)) * 3
+    am = O.argmax_rows(logits[:, 0])
+    eot = 499
+    parent, token, score, fc, _, _ = O.beam_select(logits, np.zeros((4, 1)), eot)
+    assert (token[:, 0] == am).all() and (parent == 0).all() and (fc == 0).all()
+    logits[2, 0, eot] = 100.0                                   # end-of-text wins row 2
+    parent, token, score, fc, fp, _ = O.beam_select(logits, np.zeros((4, 1)), eot)
+    second = np.argsort(-logits[2, 0], kind="stable")[1]
+    assert fc.tolist() == [0, 0, 1, 0] and fp[2, 0] == 0 and token[2, 0] == second
+
+
+def test_beam_select_row_shift_invariance():
+    g = np.random.default_rng(14)
+    logits = g.standard_normal((2, 3, 300))
+    sums = g.standard_normal((2, 3))
+    a = O.beam_select(logits, sums, 7)
+    b = O.beam_select(logits + np.array([5.0, -3.0, 0.25])[None, :, None], sums, 7)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(x, y, rtol=0, atol=1e-12)
