@@ -178,12 +178,43 @@ int verify_accept(const void *logits, int32_t logits_dtype, int32_t B, int32_t R
                   int32_t *accept_len, int32_t *next_token, void *ws,
                   size_t ws_bytes, void *stream);
 
+/* beam_select - one beam-search update for each audio row b, following the
+ * beam-search decoder's update steps on [W] (step 4, reordering the caches
+ * to the new beam order, is kv_reorder with the `parent` produced here):
+ *   1. log-probabilities of each beam's logits row (natural-log softmax) and
+ *      the beam's K + 1 best tokens (larger logit first; equal logits: lower
+ *      token first);
+ *   2. candidate (beam j, token t) scores sum_logprobs[b][j] + logp_j(t);
+ *   3. candidates are taken in order of score (larger first; equal scores
+ *      in the order beam, then rank): an `eot` token is recorded as finished,
+ *      any other token becomes the next beam, until K next beams are chosen.
+ *   logits: device, [B][K][V] of logits_dtype, 16-byte aligned; every row
+ *     needs a finite maximum (NaN is outside the contract).
+ *   sum_logprobs: device fp32 [B][K], the beams' running scores.
+ *   eot: end-of-text token (any value; one outside [0, V) never matches).
+ *   parent, token: device int32 [B][K]: next beam k continues beam
+ *     parent[b][k] with token[b][k]; score: device fp32 [B][K], its running
+ *     score (log-probabilities and scores in fp32).
+ *   finished_count: device int32 [B]; finished_parent (int32) and
+ *     finished_score (fp32): device [B][K], the first finished_count entries
+ *     in the order met, then -1 / NaN.
+ *   ws: device workspace of ws_bytes >= kvd_beam_workspace_bytes(B, K, V),
+ *     zero-filled before its first use and left that way.
+ * Errors: KVD_ERR_NULL, KVD_ERR_DTYPE, KVD_ERR_SHAPE (B < 1, B > 4096,
+ *   K outside [1, 16], V < K + 1, K * ceil(V / 4096) > 227),
+ *   KVD_ERR_WORKSPACE, KVD_ERR_ALIGN. */
+int beam_select(const void *logits, int32_t logits_dtype, int32_t B, int32_t K, int32_t V,
+                const float *sum_logprobs, int32_t eot, int32_t *parent, int32_t *token,
+                float *score, int32_t *finished_count, int32_t *finished_parent,
+                float *finished_score, void *ws, size_t ws_bytes, void *stream);
+
 /* Workspace sizes (bytes) for the calls above: 0 for invalid sizes, and 0
  * when no call of that shape merges split partials (a NULL workspace is then
  * accepted). A workspace sized for the largest len (or frames) serves every
  * smaller one. */
 size_t kvd_attn_workspace_bytes(int32_t B, int32_t Hq, int32_t N, int32_t len_max);
 size_t kvd_verify_workspace_bytes(int32_t B, int32_t R, int32_t V);
+size_t kvd_beam_workspace_bytes(int32_t B, int32_t K, int32_t V);
 
 /* Measurement aid: a plain streaming read of `bytes` from a and, when b is
  * not NULL, `bytes` from b, in one launch on `stream` (every 16-byte vector

@@ -53,6 +53,10 @@ _SIGNATURES = {
                               c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "kvd_attn_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32]),
     "kvd_verify_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
+    "beam_select": (c_int, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_int32,
+                            c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                            c_void_p, c_size_t, c_void_p]),
+    "kvd_beam_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
     "kvd_status_string": (ctypes.c_char_p, [c_int]),
     "kvd_time_next_launch": (c_int, [c_void_p, c_void_p]),
     "kvd_read_probe": (c_int, [c_void_p, c_void_p, c_size_t, c_void_p, c_void_p]),
@@ -292,3 +296,40 @@ def verify_accept(logits: torch.Tensor, draft: torch.Tensor,
         _dev(next_token, "next_token", torch.int32), _dev(ws, "ws"),
         ws.numel() * ws.element_size(), _stream()))
     return accept_len, next_token, argmax_out
+
+
+def beam_workspace_bytes(B: int, K: int, V: int) -> int:
+    return int(lib().kvd_beam_workspace_bytes(B, K, V))
+
+
+def beam_select(logits: torch.Tensor, sum_logprobs: torch.Tensor, eot: int,
+                ws: torch.Tensor | None = None, out: dict | None = None) -> dict:
+    """One beam-search update: logits [B, K, V], running scores sum_logprobs
+    fp32 [B, K]. Returns a dict of device tensors: parent, token, score
+    [B, K]; finished_count [B]; finished_parent, finished_score [B, K]."""
+    if logits.dim() != 3 or tuple(sum_logprobs.shape) != tuple(logits.shape[:2]):
+        raise ValueError("logits must be [B, K, V] and sum_logprobs [B, K]")
+    if logits.dtype not in DTYPE_CODE:
+        raise ValueError(f"unsupported logits dtype {logits.dtype}")
+    B, K, V = logits.shape
+    dev = logits.device
+    if out is None:
+        out = {"parent": torch.empty((B, K), dtype=torch.int32, device=dev),
+               "token": torch.empty((B, K), dtype=torch.int32, device=dev),
+               "score": torch.empty((B, K), dtype=torch.float32, device=dev),
+               "finished_count": torch.empty(B, dtype=torch.int32, device=dev),
+               "finished_parent": torch.empty((B, K), dtype=torch.int32, device=dev),
+               "finished_score": torch.empty((B, K), dtype=torch.float32, device=dev)}
+    if ws is None:
+        ws = workspace(beam_workspace_bytes(B, K, V), dev)
+    _check("beam_select", lib().beam_select(
+        _dev(logits, "logits"), DTYPE_CODE[logits.dtype], B, K, V,
+        _dev(sum_logprobs, "sum_logprobs", torch.float32), int(eot),
+        _dev(out["parent"], "parent", torch.int32), _dev(out["token"], "token", torch.int32),
+        _dev(out["score"], "score", torch.float32),
+        _dev(out["finished_count"], "finished_count", torch.int32),
+        _dev(out["finished_parent"], "finished_parent", torch.int32),
+        _dev(out["finished_score"], "finished_score", torch.float32),
+        _dev(ws, "ws"), ws.numel() * ws.element_size(), _stream()))
+    return out
+

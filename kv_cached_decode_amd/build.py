@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvdecode.so")
-SOURCES = ["kvd_copy.hip", "kvd_attn.hip", "kvd_attn_mfma.hip", "kvd_verify.hip", "kvd_probe.hip",
+SOURCES = ["kvd_copy.hip", "kvd_attn.hip", "kvd_attn_mfma.hip", "kvd_verify.hip", "kvd_beam.hip",
+           "kvd_probe.hip",
            "kvd_api.cpp"]
 ARCH = "gfx950"
 

@@ -338,6 +338,49 @@ int verify_accept(const void *logits, int32_t logits_dtype, int32_t B, int32_t R
   return status_of(kvd::launch_verify(a, static_cast<hipStream_t>(stream)));
 }
 
+size_t kvd_beam_workspace_bytes(int32_t B, int32_t K, int32_t V) {
+  if (B < 1 || K < 1 || V < 1) return 0;
+  return kCounterBytes + (size_t)B * K * kvd::beam_chunks(V) * kvd::kBeamRec * sizeof(uint32_t);
+}
+
+int beam_select(const void *logits, int32_t logits_dtype, int32_t B, int32_t K, int32_t V,
+                const float *sum_logprobs, int32_t eot, int32_t *parent, int32_t *token,
+                float *score, int32_t *finished_count, int32_t *finished_parent,
+                float *finished_score, void *ws, size_t ws_bytes, void *stream) {
+  if (!logits || !sum_logprobs || !parent || !token || !score || !finished_count ||
+      !finished_parent || !finished_score)
+    return KVD_ERR_NULL;
+  if (!dtype_ok(logits_dtype)) return KVD_ERR_DTYPE;
+  if (B < 1 || B > kvd::kMaxCounters || K < 1 || K > kvd::kMaxBeamWidth || V < K + 1)
+    return KVD_ERR_SHAPE;
+  const int chunks = kvd::beam_chunks(V);
+  if ((int64_t)K * chunks * kvd::kBeamRec > kvd::kMaxBeamWords) return KVD_ERR_SHAPE;
+  if (!aligned16(logits) || !aligned4(sum_logprobs) || !aligned4(parent) || !aligned4(token) ||
+      !aligned4(score) || !aligned4(finished_count) || !aligned4(finished_parent) ||
+      !aligned4(finished_score))
+    return KVD_ERR_ALIGN;
+  if (!ws || ws_bytes < kvd_beam_workspace_bytes(B, K, V)) return KVD_ERR_WORKSPACE;
+  if (!aligned16(ws)) return KVD_ERR_ALIGN;
+  kvd::BeamArgs a;
+  a.logits = logits;
+  a.dtype = logits_dtype;
+  a.sum_logprobs = sum_logprobs;
+  a.parent = parent;
+  a.token = token;
+  a.score = score;
+  a.fin_count = finished_count;
+  a.fin_parent = finished_parent;
+  a.fin_score = finished_score;
+  a.ws_count = static_cast<uint32_t *>(ws);
+  a.ws_rec = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + kCounterBytes);
+  a.B = B;
+  a.K = K;
+  a.V = V;
+  a.eot = eot;
+  a.chunks = chunks;
+  return status_of(kvd::launch_beam(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t kvd_verify_workspace_bytes(int32_t B, int32_t R, int32_t V) {
   if (B < 1 || R < 1 || V < 1) return 0;
   int chunk = 0, chunks = 0;

@@ -116,6 +116,26 @@ hipError_t launch_attn(int dtype, const AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_mfma(int dtype, const AttnArgs &a, hipStream_t s);
 hipError_t launch_verify(const VerifyArgs &a, hipStream_t s);
 
+// Beam-search candidate scoring.
+constexpr int kMaxBeamWidth = 16;                    // beams per audio row
+constexpr int kBeamRec = 2 + 2 * (kMaxBeamWidth + 1);  // words per chunk record
+constexpr int kMaxBeamWords = 8192;                  // records staged by the last workgroup
+struct BeamArgs {
+  const void *logits;            // [B][K][V]
+  int dtype;
+  const float *sum_logprobs;     // [B][K]
+  int32_t *parent, *token;       // [B][K]
+  float *score;                  // [B][K]
+  int32_t *fin_count;            // [B]
+  int32_t *fin_parent;           // [B][K]
+  float *fin_score;              // [B][K]
+  uint32_t *ws_count;            // [B]
+  uint32_t *ws_rec;              // [B][K][chunks][kBeamRec]
+  int B, K, V, eot, chunks;
+};
+int beam_chunks(int V);
+hipError_t launch_beam(const BeamArgs &a, hipStream_t s);
+
 struct ProbeArgs {
   const void *a, *b;  // buffers to read (b may be NULL)
   size_t vecs;        // 16-byte vectors read from each

@@ -21,6 +21,7 @@ DTYPES = ("f32", "f16", "bf16")
 # stream ids: each kind of tensor draws from its own numpy SeedSequence branch
 _S_SELF_K, _S_SELF_V, _S_CROSS_K, _S_CROSS_V = 1, 2, 3, 4
 _S_Q_SELF, _S_Q_CROSS, _S_PARENT, _S_LOGITS, _S_DRAFT = 5, 6, 7, 8, 9
+_S_BEAM_LOGITS, _S_BEAM_SCORES = 10, 11
 
 
 def rng(seed: int, *key: int) -> np.random.Generator:
@@ -160,3 +161,16 @@ def verify_logits(w: Workload, trial: int, B: int = 1, R: int | None = None,
     rand_tok = gd.integers(0, V, size=(B, N))
     draft = np.where(match, planted[:, :N], rand_tok).astype(np.int32)
     return np.ascontiguousarray(logits), np.ascontiguousarray(draft)
+
+
+def beam_logits(w: Workload, step: int, B: int = 1, K: int | None = None, V: int = 51865,
+                sigma: float = 2.0):
+    """Beam-search scoring inputs of one step: logits [B, K, V] ~ N(0,
+    sigma^2) (f32) and running scores [B, K], uniform in [-step - 1, -step]
+    (running log-probabilities fall as a sequence grows)."""
+    K = w.B if K is None else K
+    g = rng(w.seed, _S_BEAM_LOGITS, step)
+    logits = g.standard_normal(size=(B, K, V), dtype=np.float32) * np.float32(sigma)
+    sums = (rng(w.seed, _S_BEAM_SCORES, step).random(size=(B, K)) - 1.0 - step).astype(np.float32)
+    return np.ascontiguousarray(logits), np.ascontiguousarray(sums)
+

@@ -129,3 +129,25 @@ def test_read_probe_validation(lib):
     assert f(MIS, None, 16, FAKE, None) == -7
     assert f(FAKE, MIS, 16, FAKE, None) == -7
     assert f(FAKE, None, 16, FAKE + 2, None) == -7
+
+
+def test_beam_select_validation(lib):
+    f = lib.beam_select
+    ws_need = kb.beam_workspace_bytes(1, 5, 51865)
+    assert ws_need > 16384
+    ok = [FAKE, kb.F32, 1, 5, 51865, FAKE, 50256] + [FAKE] * 6 + [FAKE, ws_need, None]
+
+    def call(**kw):
+        args = list(ok)
+        names = ["logits", "dt", "B", "K", "V", "sums", "eot", "parent", "token", "score", "fc", "fp",
+                 "fs", "ws", "wsb", "stream"]
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return f(*args)
+    assert call(logits=None) == -1
+    assert call(fs=None) == -1
+    assert call(dt=9) == -3
+    assert call(K=0) == -2 and call(K=17) == -2 and call(V=5) == -2 and call(B=0) == -2
+    assert call(K=16, V=4096 * 15) == -2          # 16 beams x 15 chunks of records exceed the staging
+    assert call(ws=None) == -6 and call(wsb=ws_need - 4) == -6
+    assert call(logits=MIS) == -7 and call(parent=FAKE + 2) == -7

@@ -492,3 +492,83 @@ def test_read_probe_reads_every_vector():
         kb.read_probe(other, buf, n_vec * 16, sink)
         torch.cuda.synchronize()
         assert int(sink[0]) == magic
+
+
+# ---------------------------------------------------------------------------
+# Beam-search candidate scoring
+# ---------------------------------------------------------------------------
+
+def _beam_check(logits_stored, dtype, sums, eot, res, tol=1e-4):
+    """Token choices must equal the oracle's wherever the oracle's candidate
+    order has no near-tie (gap <= tol, where fp32 and fp64 may order
+    differently); scores within tol."""
+    ref = O.beam_select(O.widen(logits_stored, dtype), sums.astype(np.float64), eot)
+    parent, token, score = (from_dev(res[k], None) for k in ("parent", "token", "score"))
+    fc, fp, fs = (from_dev(res[k], None) for k in ("finished_count", "finished_parent", "finished_score"))
+    B, K, _ = logits_stored.shape
+    lp = O.log_softmax_rows(O.widen(logits_stored, dtype))
+    for b in range(B):
+        cands = []
+        for j in range(K):
+            top = np.lexsort((np.arange(lp.shape[-1]), -lp[b, j]))[:K + 1]
+            cands += [sums[b, j] + lp[b, j, t] for t in top]
+        walked = np.sort(np.array(cands))[::-1][:K + ref[3][b] + 1]   # the walk and the next one
+        gaps = -np.diff(walked)
+        # equal scores are ordered alike on both sides; gaps within fp32
+        # rounding may not be
+        tight = bool(np.any((gaps > 0) & (gaps <= tol)))
+        if not tight:
+            assert parent[b].tolist() == ref[0][b].tolist(), (b, parent[b], ref[0][b])
+            assert token[b].tolist() == ref[1][b].tolist()
+            assert fc[b] == ref[3][b] and fp[b, :fc[b]].tolist() == ref[4][b, :fc[b]].tolist()
+            assert (fp[b, fc[b]:] == -1).all() and np.isnan(fs[b, fc[b]:]).all()
+        for i in range(K):   # every chosen next beam is a real candidate with its score
+            j, t = int(parent[b, i]), int(token[b, i])
+            assert t != eot and abs(score[b, i] - (sums[b, j] + lp[b, j, t])) <= tol
+        np.testing.assert_allclose(np.sort(score[b]), np.sort(ref[2][b]), rtol=0, atol=tol)
+    return ref
+
+
+@pytest.mark.parametrize("step", range(8))
+def test_beam_select_whisper_shape(step):
+    """5 beams over the 51865-token vocabulary, fp32 logits ~ N(0, 4)."""
+    w = I.WHISPER_BEAM
+    say(f"case: beam select step {step}")
+    logits, sums = I.beam_logits(w, step)
+    eot = 50256
+    if step % 2:   # end-of-text the best candidate of the best-scoring beam
+        j = int(np.argmax(sums[0]))
+        logits[0, j, eot] = logits[0, j].max() + 3.0
+    res = kb.beam_select(to_dev(logits, "f32"), torch.from_numpy(sums).cuda(), eot)
+    torch.cuda.synchronize()
+    ref = _beam_check(logits, "f32", sums, eot, res)
+    if step % 2:
+        assert ref[3][0] >= 1
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("B,K,V", [(3, 1, 17), (2, 4, 4097), (1, 16, 20000), (2, 3, 4), (4, 8, 12289)])
+def test_beam_select_shapes(dtype, B, K, V):
+    say(f"case: beam select {dtype} B={B} K={K} V={V}")
+    g = np.random.default_rng([21, B, K, V])
+    logits = I.to_storage(g.standard_normal((B, K, V), dtype=np.float32) * 2, dtype)
+    sums = (-g.random((B, K)) * 3).astype(np.float32)
+    eot = V - 1
+    res = kb.beam_select(to_dev(logits, dtype), torch.from_numpy(sums).cuda(), eot)
+    torch.cuda.synchronize()
+    _beam_check(logits, dtype, sums, eot, res)
+
+
+def test_beam_select_repeated_calls_share_workspace():
+    """The workspace counters reset themselves: ten calls in a row on one
+    workspace, alternating shapes."""
+    say("case: beam select repeated")
+    ws = kb.workspace(max(kb.beam_workspace_bytes(2, 5, 51865), kb.beam_workspace_bytes(3, 2, 999)))
+    for i in range(10):
+        B, K, V = (2, 5, 51865) if i % 2 == 0 else (3, 2, 999)
+        g = np.random.default_rng([22, i])
+        logits = (g.standard_normal((B, K, V)) * 2).astype(np.float32)
+        sums = (-g.random((B, K))).astype(np.float32)
+        res = kb.beam_select(to_dev(logits, "f32"), torch.from_numpy(sums).cuda(), 3, ws=ws)
+        torch.cuda.synchronize()
+        _beam_check(logits, "f32", sums, 3, res)
