@@ -501,12 +501,14 @@ def workload_verify(torch, kb, reps):
 
 
 def workload_beam(torch, kb, reps):
-    """Beam search with 5 beams at the large-v2 shape: per step, 32 layers of
-    [kv_reorder by parent beams, append + self attention, cross attention over
-    a cross cache shared by the beams]; 224 steps."""
+    """Beam search with 5 beams at the large-v2 shape: per step, beam_select
+    over [1, 5, 51865] fp32 logits (N(0, 4)) with the running scores the step
+    before produced, then 32 layers of [kv_reorder by the selected parents,
+    append + self attention, cross attention over a cross cache shared by the
+    beams]; 224 steps."""
     g = torch.Generator(device="cuda").manual_seed(4)
     rn = lambda *sh: (torch.randn(*sh, generator=g, device="cuda") / 8).half()
-    B, steps = 5, 224
+    B, steps, V, eot = 5, 224, 51865, 50256
     self_c, cross_c = [], []
     for _ in range(LAYERS):
         c = kb.Cache(B, H, S_MAX, torch.float16)
@@ -517,31 +519,49 @@ def workload_beam(torch, kb, reps):
         cross_c.append(x)
     q, qx = rn(LAYERS, B, H, 1, D), rn(LAYERS, B, H, 1, D)
     kn, vn = rn(LAYERS, B, H, 1, D), rn(LAYERS, B, H, 1, D)
-    parents = torch.randint(0, B, (steps, B), generator=g, device="cuda", dtype=torch.int32)
+    logits = torch.randn(steps, 1, B, V, generator=g, device="cuda") * 2
+    outs = [kb.beam_select(logits[0], torch.zeros(1, B, device="cuda"), eot) for _ in range(2)]
+    for o in outs:
+        o["score"].zero_()
     out = torch.empty((LAYERS, B, H, 1, D), dtype=torch.float32, device="cuda")
     outx = torch.empty_like(out)
     ws = kb.workspace(kb.attn_workspace_bytes(B, H, 1, FRAMES))
+    wsb = kb.workspace(kb.beam_workspace_bytes(1, B, V))
 
     def step(s):
+        cur, prev = outs[s % 2], outs[(s + 1) % 2]
+        kb.beam_select(logits[s], prev["score"], eot, ws=wsb, out=cur)
+        parent = cur["parent"][0]
         for l in range(LAYERS):
             if s > 0:
-                kb.kv_reorder(self_c[l], parents[s], s)
+                kb.kv_reorder(self_c[l], parent, s)
             kb.decode_step_self(q[l], kn[l], vn[l], self_c[l], s + 1, 1 / 8, out=out[l], ws=ws)
             kb.decode_attn_cross(qx[l], cross_c[l], FRAMES, 1 / 8, out=outx[l], ws=ws)
 
     graphs = _graph_steps(torch, step, range(steps))
+    # one untimed pass records the parents the scoring chose
+    changed = 0
+    for s, gr in enumerate(graphs):
+        gr.replay()
+        changed += int((outs[s % 2]["parent"][0].cpu() != torch.arange(B, dtype=torch.int32)).sum())
+    changed /= steps
     sec = _time_graphs(torch, graphs, reps)
     # reorder moves (reads and writes) the rows of the beams whose parent differs
-    changed = float((parents != torch.arange(B, device="cuda")).sum().item()) / steps
     kv = sum(LAYERS * (B * 2 * (s + 1) * ROW_BYTES + CROSS_BYTES + B * 2 * ROW_BYTES
-                       + 2 * changed * 2 * s * ROW_BYTES) for s in range(steps)) / steps
-    reorder_us = _kernel_us(torch, kb, lambda i: kb.kv_reorder(self_c[i % LAYERS], parents[100], 200))
+                       + 2 * changed * 2 * s * ROW_BYTES) + B * V * 4 for s in range(steps)) / steps
+    parent = outs[0]["parent"][0]
+    reorder_us = _kernel_us(torch, kb, lambda i: kb.kv_reorder(self_c[i % LAYERS], parent, 200))
+    select_us = _kernel_us(torch, kb, lambda i: kb.beam_select(logits[i % steps], outs[1]["score"], eot,
+                                                              ws=wsb, out=outs[0]))
     return {"metric": "beam-search decode steps/s (5 beams), large-v2 shape, 1 GPU",
             "value": round(1 / sec, 2), "unit": "steps/s", "ms_per_step": round(sec * 1e3, 4),
             "effective_kv_gbps": round(kv / sec / 1e9, 1),
-            "kernels_us": {"kv_reorder_len200": round(reorder_us, 3)},
-            "config": {"workload": "whisper-large-v2 beam 5: 32 layers x [kv_reorder, append + self, "
-                                   "cross shared by beams]; 224 steps"}}
+            "beams_changed_per_step": round(changed, 2),
+            "kernels_us": {"kv_reorder_len200": round(reorder_us, 3),
+                           "beam_select_5x51865": round(select_us, 3)},
+            "config": {"workload": "whisper-large-v2 beam 5: beam_select [1, 5, 51865] + 32 layers x "
+                                   "[kv_reorder by its parents, append + self, cross shared by beams]; "
+                                   "224 steps"}}
 
 
 def workload_gqa(torch, kb, reps):

@@ -27,7 +27,7 @@
  *     accumulates in fp32 and writes fp32 output.
  *   - Head dimension D must be 64.
  *   - All device buffers are contiguous, row-major in the order written, and
- *     16-byte aligned. The caller owns every buffer; the library allocates
+ *     16-byte aligned, except where a call states otherwise. The caller owns every buffer; the library allocates
  *     nothing and keeps no state between calls.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
  *     default stream). Calls are thread-safe; two calls that share a
@@ -163,7 +163,8 @@ int decode_attn_cross(const void *q, int32_t B, int32_t Hq, int32_t N,
  *   accept_len[b] = n = first i < N with draft[b][i] != argmax[i], else N,
  *   next_token[b] = argmax[n] if n < R, else -1 (all N drafts kept and no
  *     bonus row).
- *   logits: device, [B][R][V] of logits_dtype; R = N (row i scores draft i)
+ *   logits: device, [B][R][V] of logits_dtype, aligned to its element; R = N
+ *     (row i scores draft i)
  *     or N + 1 (a bonus row after the last draft).
  *   draft: device int32 [B][N] (any value; one outside [0, V) never matches).
  *   argmax_out: device int32 [B][R] or NULL.
@@ -172,7 +173,8 @@ int decode_attn_cross(const void *q, int32_t B, int32_t Hq, int32_t N,
  *     zero-filled before its first use and left that way.
  * Errors: KVD_ERR_NULL, KVD_ERR_SHAPE (B, N, V < 1; N > 63; B > 4096;
  *   R * ceil(V / 4096) > 2048), KVD_ERR_ROWS,
- *   KVD_ERR_DTYPE, KVD_ERR_WORKSPACE, KVD_ERR_ALIGN (logits only). */
+ *   KVD_ERR_DTYPE, KVD_ERR_WORKSPACE, KVD_ERR_ALIGN (logits not aligned to
+ *   their element, other pointers to 4 bytes). */
 int verify_accept(const void *logits, int32_t logits_dtype, int32_t B, int32_t R,
                   int32_t V, const int32_t *draft, int32_t N, int32_t *argmax_out,
                   int32_t *accept_len, int32_t *next_token, void *ws,
@@ -188,8 +190,8 @@ int verify_accept(const void *logits, int32_t logits_dtype, int32_t B, int32_t R
  *   3. candidates are taken in order of score (larger first; equal scores
  *      in the order beam, then rank): an `eot` token is recorded as finished,
  *      any other token becomes the next beam, until K next beams are chosen.
- *   logits: device, [B][K][V] of logits_dtype, 16-byte aligned; every row
- *     needs a finite maximum (NaN is outside the contract).
+ *   logits: device, [B][K][V] of logits_dtype, aligned to its element; every
+ *     row needs a finite maximum (NaN is outside the contract).
  *   sum_logprobs: device fp32 [B][K], the beams' running scores.
  *   eot: end-of-text token (any value; one outside [0, V) never matches).
  *   parent, token: device int32 [B][K]: next beam k continues beam
@@ -201,7 +203,8 @@ int verify_accept(const void *logits, int32_t logits_dtype, int32_t B, int32_t R
  *   ws: device workspace of ws_bytes >= kvd_beam_workspace_bytes(B, K, V),
  *     zero-filled before its first use and left that way.
  * Errors: KVD_ERR_NULL, KVD_ERR_DTYPE, KVD_ERR_SHAPE (B < 1, B > 4096,
- *   K outside [1, 16], V < K + 1, K * ceil(V / 4096) > 227),
+ *   K outside [1, 16], V < K + 1, (K + 1) * ceil(V / 2048) > 512: e.g.
+ *   V <= 61440 at K = 16, V <= 174080 at K = 5),
  *   KVD_ERR_WORKSPACE, KVD_ERR_ALIGN. */
 int beam_select(const void *logits, int32_t logits_dtype, int32_t B, int32_t K, int32_t V,
                 const float *sum_logprobs, int32_t eot, int32_t *parent, int32_t *token,

@@ -19,6 +19,10 @@ namespace {
 bool dtype_ok(int dt) { return dt == KVD_F32 || dt == KVD_F16 || dt == KVD_BF16; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+// Aligned to its element type (logits are read one element at a time).
+bool elem_aligned(const void *p, int dtype) {
+  return (reinterpret_cast<uintptr_t>(p) & (dtype == KVD_F32 ? 3u : 1u)) == 0;
+}
 
 // Shared checks of a cache descriptor.
 int check_cache(const kvd_cache *c) {
@@ -310,7 +314,7 @@ int verify_accept(const void *logits, int32_t logits_dtype, int32_t B, int32_t R
   if (!dtype_ok(logits_dtype)) return KVD_ERR_DTYPE;
   if (B < 1 || N < 1 || V < 1 || N > 63 || B > kvd::kMaxCounters) return KVD_ERR_SHAPE;
   if (R != N && R != N + 1) return KVD_ERR_ROWS;
-  if (!aligned16(logits)) return KVD_ERR_ALIGN;
+  if (!elem_aligned(logits, logits_dtype)) return KVD_ERR_ALIGN;
   if (!aligned4(draft) || !aligned4(accept_len) || !aligned4(next_token) ||
       (argmax_out && !aligned4(argmax_out)))
     return KVD_ERR_ALIGN;
@@ -354,8 +358,9 @@ int beam_select(const void *logits, int32_t logits_dtype, int32_t B, int32_t K, 
   if (B < 1 || B > kvd::kMaxCounters || K < 1 || K > kvd::kMaxBeamWidth || V < K + 1)
     return KVD_ERR_SHAPE;
   const int chunks = kvd::beam_chunks(V);
-  if ((int64_t)K * chunks * kvd::kBeamRec > kvd::kMaxBeamWords) return KVD_ERR_SHAPE;
-  if (!aligned16(logits) || !aligned4(sum_logprobs) || !aligned4(parent) || !aligned4(token) ||
+  if ((int64_t)(K + 1) * chunks > kvd::kMaxBeamEntries) return KVD_ERR_SHAPE;
+  if (!elem_aligned(logits, logits_dtype) || !aligned4(sum_logprobs) || !aligned4(parent) ||
+      !aligned4(token) ||
       !aligned4(score) || !aligned4(finished_count) || !aligned4(finished_parent) ||
       !aligned4(finished_score))
     return KVD_ERR_ALIGN;

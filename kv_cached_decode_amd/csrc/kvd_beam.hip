@@ -6,13 +6,21 @@
 // Search、Logit フィルター、KV キャッシュ" (the step after them, reordering the
 // cache, is kv_reorder).
 //
-// Workgroup (chunk, beam, row) reads 4096 logits (16 per thread, all loads
-// issued first) and publishes a record: the chunk's max, its sum of
-// exp(x - max), and its K + 1 best (value, index) pairs, found in K + 1
-// rounds of a (value, index) argmax in which the owner of each round's winner
-// drops it. The last workgroup of the audio row to arrive stages every record
-// in LDS, combines the chunks of each beam (log-sum-exp and the K + 1 best),
-// ranks the candidates in parallel and walks them in order.
+// Orders are taken on 64-bit keys whose unsigned order is the order wanted:
+// (logit, token) pairs and candidates become one integer each, so a selection
+// step is one 64-bit max over the wavefront in lane exchanges (DPP and
+// permlane swaps), with no LDS round trip and no barrier.
+//
+// Workgroup (chunk, beam, row) reads 2048 logits (4 per thread) and publishes
+// a record: the chunk's max, its sum of exp(x - max), and its K + 1 best keys.
+// Each wavefront finds its own K + 1 best in K + 1 rounds (the lane holding a
+// round's winner drops it and rescans its items); wavefront 0 merges the eight
+// lists the same way. The last workgroup of the audio row to arrive gives each
+// beam to a wavefront: log-sum-exp over the chunk records, then the beam's
+// K + 1 best out of every chunk's entries, again in rounds. The K (K + 1)
+// candidates are then placed in parallel: a candidate's position in the walk
+// is the number of candidates ranked before it, and the end-of-text ones among
+// them fix whether the walk reaches it and which output slot it takes.
 #include <limits.h>
 #include <math.h>
 
@@ -23,11 +31,18 @@ namespace kvd {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kItems = 16;
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int kItems = 4;
 constexpr int kChunk = kThreads * kItems;
-constexpr int kStageIters = kMaxBeamWords / kThreads;
-constexpr int kMaxCand = kMaxBeamWidth * (kMaxBeamWidth + 1);
+constexpr int kMaxKP = kMaxBeamWidth + 1;
+constexpr int kTopLane = (kWaves * kMaxKP + 63) / 64;       // wave lists merged per lane
+constexpr int kEntLane = kMaxBeamEntries / 64;              // chunk entries per lane
+constexpr int kChunkLane = (kMaxBeamEntries / 2 + 63) / 64;  // chunk records per lane (K >= 1)
+constexpr int kMaxCand = kMaxBeamWidth * kMaxKP;
+constexpr uint32_t kTokBits = 23;                            // tokens < 2^23 (V <= 2048 * 256)
+static_assert(kMaxCand <= kThreads, "one thread per candidate");
+static_assert((kMaxCand - 1) < (1 << (32 - kTokBits)), "candidate number fits its field");
 
 template <int DT>
 __device__ __forceinline__ float load_logit(const char *row, int e) {
@@ -36,9 +51,85 @@ __device__ __forceinline__ float load_logit(const char *row, int e) {
   else return __builtin_bit_cast(float, (uint32_t)reinterpret_cast<const uint16_t *>(row)[e] << 16);
 }
 
-// (v, i) ranks before (bv, bi): larger value, or equal value and lower index.
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
+// Unsigned integers that compare as the floats do (-0 taken as +0; NaN is
+// outside the contract), and back.
+__device__ __forceinline__ uint32_t order_bits(float v) {
+  uint32_t u = __builtin_bit_cast(uint32_t, v);
+  if (u == 0x80000000u) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float order_value(uint32_t k) {
+  return __builtin_bit_cast(float, (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// (logit, token): larger logit first, equal logits lower token first. Every
+// such key is nonzero; 0 stands for "none" and ranks last.
+__device__ __forceinline__ uint64_t entry_key(float v, int tok) {
+  return ((uint64_t)order_bits(v) << 32) | (uint32_t)~tok;
+}
+// Candidate t = beam * (K + 1) + rank with token tok: larger score first,
+// equal scores smaller t first; the token rides in the low bits.
+__device__ __forceinline__ uint64_t cand_key(float score, int t, int tok) {
+  return ((uint64_t)order_bits(score) << 32) |
+         ((uint32_t)(kMaxCand - 1 - t) << kTokBits) | (uint32_t)tok;
+}
+__device__ __forceinline__ int cand_token(uint64_t k) { return (int)(k & ((1u << kTokBits) - 1)); }
+
+__device__ __forceinline__ uint64_t max64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_mov64(uint64_t x) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+// The pair {x[lane], x[lane ^ 16]} (resp. ^ 32) arrives in the two results in
+// the same lane-dependent order for both halves, so halves pair up by result.
+__device__ __forceinline__ uint64_t pair_max64_16(uint64_t x) {
+  const unsigned lo = (unsigned)x, hi = (unsigned)(x >> 32);
+  const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  return max64(((uint64_t)(unsigned)h[0] << 32) | (unsigned)l[0],
+               ((uint64_t)(unsigned)h[1] << 32) | (unsigned)l[1]);
+}
+__device__ __forceinline__ uint64_t pair_max64_32(uint64_t x) {
+  const unsigned lo = (unsigned)x, hi = (unsigned)(x >> 32);
+  const auto l = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  const auto h = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  return max64(((uint64_t)(unsigned)h[0] << 32) | (unsigned)l[0],
+               ((uint64_t)(unsigned)h[1] << 32) | (unsigned)l[1]);
+}
+// Max over the wavefront; every lane ends with it.
+__device__ __forceinline__ uint64_t wave_max64(uint64_t x) {
+  x = max64(x, dpp_mov64<kDppQuadXor1>(x));
+  x = max64(x, dpp_mov64<kDppQuadXor2>(x));
+  x = max64(x, dpp_mov64<kDppHalfMirror>(x));
+  x = max64(x, dpp_mov64<kDppRowRor8>(x));
+  return pair_max64_32(pair_max64_16(x));
+}
+
+// The wavefront's n best keys among the N keys each lane holds (0 = none):
+// lane r (r < n) returns the r-th. Each round takes the wavefront max; the
+// lane holding it (keys are distinct) clears it and rescans.
+template <int N>
+__device__ __forceinline__ uint64_t wave_top(uint64_t (&k)[N], int n, int lane) {
+  uint64_t best = 0;
+#pragma unroll
+  for (int q = 0; q < N; ++q) best = max64(best, k[q]);
+  uint64_t mine = 0;
+  for (int r = 0; r < n; ++r) {
+    const uint64_t win = wave_max64(best);
+    if (lane == r) mine = win;
+    if (best == win && win != 0) {
+      best = 0;
+#pragma unroll
+      for (int q = 0; q < N; ++q) {
+        if (k[q] == win) k[q] = 0;
+        best = max64(best, k[q]);
+      }
+    }
+  }
+  return mine;
 }
 
 template <int DT>
@@ -50,190 +141,143 @@ __global__ __launch_bounds__(kThreads) void beam_kernel(BeamArgs a) {
   const char *row = static_cast<const char *>(a.logits) +
                     (size_t)(b * K + j) * a.V * Storage<DT>::bytes;
   float x[kItems];
-  uint32_t avail = 0;  // bit jj: element e0 + jj * kThreads + tid exists and is not taken
 #pragma unroll
-  for (int jj = 0; jj < kItems; ++jj) {
-    const int e = e0 + jj * kThreads + tid;
-    x[jj] = -INFINITY;
-    if (e < a.V) {
-      x[jj] = load_logit<DT>(row, e);
-      avail |= 1u << jj;
-    }
+  for (int q = 0; q < kItems; ++q) {
+    const int e = e0 + q * kThreads + tid;
+    x[q] = (e < a.V) ? load_logit<DT>(row, e) : -INFINITY;
   }
 
-  __shared__ float s_f[4];
-  __shared__ int s_i[4];
-  __shared__ float s_tv[kMaxBeamWidth + 1];
-  __shared__ int s_ti[kMaxBeamWidth + 1];
+  __shared__ float s_max[kWaves], s_sum[kWaves];
+  __shared__ uint64_t s_top[kWaves * kMaxKP];
   __shared__ int s_last;
 
-  // ---- chunk max and sum of exp(x - max)
-  float mx = -INFINITY;
+  // ---- chunk max, then the sum of exp(x - max) (a chunk of -inf sums to 0)
+  float mx = x[0];
 #pragma unroll
-  for (int jj = 0; jj < kItems; ++jj) mx = fmaxf(mx, x[jj]);
+  for (int q = 1; q < kItems; ++q) mx = fmaxf(mx, x[q]);
   mx = groups_max<1>(mx);
-  if (lane == 0) s_f[wave] = mx;
+  if (lane == 0) s_max[wave] = mx;
+  uint64_t k[kItems];
+#pragma unroll
+  for (int q = 0; q < kItems; ++q) {
+    const int e = e0 + q * kThreads + tid;
+    k[q] = (e < a.V) ? entry_key(x[q], e) : 0;
+  }
   __syncthreads();
-  const float cmax = fmaxf(fmaxf(s_f[0], s_f[1]), fmaxf(s_f[2], s_f[3]));
-  __syncthreads();
+  float cmax = s_max[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) cmax = fmaxf(cmax, s_max[w]);
+  const float ref = (cmax == -INFINITY) ? 0.f : cmax;
   float se = 0.f;
 #pragma unroll
-  for (int jj = 0; jj < kItems; ++jj)
-    if (avail & (1u << jj)) se += expf(x[jj] - cmax);
+  for (int q = 0; q < kItems; ++q) se += expf(x[q] - ref);  // padding is -inf: adds 0
   se = groups_sum<1>(se);
-  if (lane == 0) s_f[wave] = se;
-  __syncthreads();
-  const float csum = (s_f[0] + s_f[1]) + (s_f[2] + s_f[3]);
+  if (lane == 0) s_sum[wave] = se;
 
-  // ---- the chunk's K + 1 best (value, index), one argmax round each
-  for (int r = 0; r < KP; ++r) {
-    float bv = -INFINITY;
-    int bi = INT_MAX;
-#pragma unroll
-    for (int jj = 0; jj < kItems; ++jj) {  // ascending index within the thread
-      const int e = e0 + jj * kThreads + tid;
-      if ((avail & (1u << jj)) && better(x[jj], e, bv, bi)) {
-        bv = x[jj];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    __syncthreads();  // the previous round's readers are done with s_f / s_i
-    if (lane == 0) {
-      s_f[wave] = bv;
-      s_i[wave] = bi;
-    }
-    __syncthreads();
-    bv = s_f[0];
-    bi = s_i[0];
-    for (int w = 1; w < 4; ++w)
-      if (better(s_f[w], s_i[w], bv, bi)) {
-        bv = s_f[w];
-        bi = s_i[w];
-      }
-    if (tid == 0) {
-      s_tv[r] = bv;
-      s_ti[r] = bi;
-    }
-    if (bi != INT_MAX && ((bi - e0) & (kThreads - 1)) == tid)  // its owner drops it
-      avail &= ~(1u << ((bi - e0) / kThreads));
-  }
+  // ---- each wavefront's K + 1 best, then wavefront 0 merges the lists
+  const uint64_t top = wave_top(k, KP, lane);
+  if (lane < KP) s_top[wave * KP + lane] = top;
   __syncthreads();
-
-  // ---- publish the record, count the arrival
-  uint32_t *rec = a.ws_rec + ((size_t)(b * K + j) * a.chunks + c) * kBeamRec;
-  if (tid == 0) publish(reinterpret_cast<float *>(rec), cmax);
-  if (tid == 1) publish(reinterpret_cast<float *>(rec) + 1, csum);
-  if (tid < KP) {
-    publish(reinterpret_cast<float *>(rec) + 2 + 2 * tid, s_tv[tid]);
-    publish(reinterpret_cast<int32_t *>(rec) + 3 + 2 * tid, s_ti[tid]);
+  if (wave == 0) {
+    uint64_t m[kTopLane];
+#pragma unroll
+    for (int q = 0; q < kTopLane; ++q) {
+      const int t = lane + 64 * q;
+      m[q] = (t < kWaves * KP) ? s_top[t] : 0;
+    }
+    float csum = s_sum[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) csum += s_sum[w];
+    const uint64_t best = wave_top(m, KP, lane);
+    uint32_t *rec = a.ws_rec + ((size_t)(b * K + j) * a.chunks + c) * kBeamRec;
+    if (lane == 0) publish(reinterpret_cast<float *>(rec), cmax);
+    if (lane == 1) publish(reinterpret_cast<float *>(rec) + 1, csum);
+    if (lane < KP) publish(reinterpret_cast<uint64_t *>(rec + 2) + lane, best);
+    wait_stores();  // the wavefront's record is in place before it counts
+    if (lane == 0)
+      s_last = (arrive(&a.ws_count[b]) == (uint32_t)(K * a.chunks - 1)) ? 1 : 0;
   }
-  wait_stores();
-  __syncthreads();
-  if (tid == 0) s_last = (arrive(&a.ws_count[b]) == (uint32_t)(K * a.chunks - 1)) ? 1 : 0;
   __syncthreads();
   if (!s_last) return;
 
-  // ---- last workgroup of audio row b: stage every record (all loads in
-  // flight), then merge
-  __shared__ uint32_t s_rec[kMaxBeamWords];
-  __shared__ float s_cs[kMaxCand];
-  __shared__ int s_ct[kMaxCand];
-  __shared__ int s_order[kMaxCand];
-  const int n = K * a.chunks * kBeamRec;
-  const uint32_t *src = a.ws_rec + (size_t)b * K * a.chunks * kBeamRec;
-  uint32_t st[kStageIters];
+  // ---- last workgroup of audio row b: beam bj on wavefront bj mod 8
+  __shared__ uint64_t s_cand[kMaxCand];
+  __shared__ int s_nf;
+  if (tid == 0) s_nf = 0;
+  const int E = a.chunks * KP;
+  for (int bj = wave; bj < K; bj += kWaves) {
+    const uint32_t *br = a.ws_rec + (size_t)(b * K + bj) * a.chunks * kBeamRec;
+    uint64_t ent[kEntLane];
 #pragma unroll
-  for (int it = 0; it < kStageIters; ++it) {
-    const int i = tid + it * kThreads;
-    if (i < n) st[it] = fetch_u32(src + i);
-  }
+    for (int q = 0; q < kEntLane; ++q) {
+      const int e = lane + 64 * q;
+      ent[q] = (e < E) ? fetch_u64(br + (e / KP) * kBeamRec + 2 + 2 * (e % KP)) : 0;
+    }
+    float cm[kChunkLane], cs[kChunkLane];
 #pragma unroll
-  for (int it = 0; it < kStageIters; ++it) {
-    const int i = tid + it * kThreads;
-    if (i < n) s_rec[i] = st[it];
-  }
-  __syncthreads();
-
-  if (tid < K) {  // beam tid: log-sum-exp over chunks, then its K + 1 best tokens
-    const uint32_t *br = s_rec + (size_t)tid * a.chunks * kBeamRec;
-    float M = -INFINITY;
-    for (int cc = 0; cc < a.chunks; ++cc) M = fmaxf(M, __builtin_bit_cast(float, br[cc * kBeamRec]));
+    for (int q = 0; q < kChunkLane; ++q) {
+      const int cc = lane + 64 * q;
+      const bool in = cc < a.chunks;
+      cm[q] = in ? __builtin_bit_cast(float, fetch_u32(br + cc * kBeamRec)) : -INFINITY;
+      cs[q] = in ? __builtin_bit_cast(float, fetch_u32(br + cc * kBeamRec + 1)) : 0.f;
+    }
+    const float sl = a.sum_logprobs[b * K + bj];
+    float M = cm[0];
+#pragma unroll
+    for (int q = 1; q < kChunkLane; ++q) M = fmaxf(M, cm[q]);
+    M = groups_max<1>(M);  // finite: the row has a finite maximum
     float S = 0.f;
-    for (int cc = 0; cc < a.chunks; ++cc) {
-      const float cm = __builtin_bit_cast(float, br[cc * kBeamRec]);
-      S += __builtin_bit_cast(float, br[cc * kBeamRec + 1]) * expf(cm - M);
-    }
+#pragma unroll
+    for (int q = 0; q < kChunkLane; ++q) S += cs[q] * expf(cm[q] - M);
+    S = groups_sum<1>(S);
     const float lse = M + logf(S);
-    const float base = a.sum_logprobs[b * K + tid];
-    // round r takes the best entry ranked after round r - 1's (entries are
-    // distinct tokens, so the order is strict)
-    float pv = INFINITY;
-    int pi = -1;
-    for (int r = 0; r < KP; ++r) {
-      float bv = -INFINITY;
-      int bi = INT_MAX;
-      for (int cc = 0; cc < a.chunks; ++cc) {
-        for (int q = 0; q < KP; ++q) {
-          const float v = __builtin_bit_cast(float, br[cc * kBeamRec + 2 + 2 * q]);
-          const int i = (int)br[cc * kBeamRec + 3 + 2 * q];
-          if (i == INT_MAX) continue;  // chunk had fewer than K + 1 elements
-          if (better(pv, pi, v, i) && better(v, i, bv, bi)) {
-            bv = v;
-            bi = i;
-          }
-        }
-      }
-      s_cs[tid * KP + r] = base + (bv - lse);
-      s_ct[tid * KP + r] = bi;
-      pv = bv;
-      pi = bi;
+    const uint64_t best = wave_top(ent, KP, lane);
+    if (lane < KP) {
+      const float v = order_value((uint32_t)(best >> 32));
+      const int tok = (int)~(uint32_t)best;
+      const int t = bj * KP + lane;
+      s_cand[t] = cand_key(sl + (v - lse), t, tok);
     }
   }
   __syncthreads();
 
-  // ---- rank the K (K + 1) candidates: larger score first, equal scores in
-  // the order beam, then rank (the candidate's number)
+  // ---- the walk, in parallel: candidate t ranks after `rank` others, `eots`
+  // of them end-of-text. The walk reaches it while fewer than K others were
+  // kept; end-of-text then goes to finished slot `eots`, any other token to
+  // next-beam slot rank - eots.
   const int nc = K * KP;
-  for (int t = tid; t < nc; t += kThreads) {
-    const float sc = s_cs[t];
-    int rank = 0;
+  if (tid < nc) {
+    const uint64_t me = s_cand[tid];
+    int rank = 0, eots = 0;
+#pragma unroll 8
     for (int u = 0; u < nc; ++u) {
-      const float su = s_cs[u];
-      rank += (su > sc || (su == sc && u < t)) ? 1 : 0;
+      const uint64_t o = s_cand[u];
+      const int before = (o > me) ? 1 : 0;
+      rank += before;
+      eots += before & ((cand_token(o) == a.eot) ? 1 : 0);
     }
-    s_order[rank] = t;
-  }
-  __syncthreads();
-
-  if (tid == 0) {
-    int kept = 0, nf = 0;
-    for (int i = 0; i < nc && kept < K; ++i) {
-      const int t = s_order[i];
-      const int beam = t / KP, tok = s_ct[t];
+    const int kept = rank - eots;
+    if (kept < K) {
+      const int beam = tid / KP, tok = cand_token(me);
+      const float sc = order_value((uint32_t)(me >> 32));
       if (tok == a.eot) {
-        a.fin_parent[b * K + nf] = beam;
-        a.fin_score[b * K + nf] = s_cs[t];
-        ++nf;
+        a.fin_parent[b * K + eots] = beam;
+        a.fin_score[b * K + eots] = sc;
+        atomicAdd(&s_nf, 1);
       } else {
         a.parent[b * K + kept] = beam;
         a.token[b * K + kept] = tok;
-        a.score[b * K + kept] = s_cs[t];
-        ++kept;
+        a.score[b * K + kept] = sc;
       }
     }
-    for (int i = nf; i < K; ++i) {
-      a.fin_parent[b * K + i] = -1;
-      a.fin_score[b * K + i] = __builtin_nanf("");
-    }
+  }
+  __syncthreads();
+  const int nf = s_nf;
+  if (tid >= nf && tid < K) {
+    a.fin_parent[b * K + tid] = -1;
+    a.fin_score[b * K + tid] = __builtin_nanf("");
+  }
+  if (tid == 0) {
     a.fin_count[b] = nf;
     reset_counter(&a.ws_count[b]);
   }

@@ -119,7 +119,7 @@ hipError_t launch_verify(const VerifyArgs &a, hipStream_t s);
 // Beam-search candidate scoring.
 constexpr int kMaxBeamWidth = 16;                    // beams per audio row
 constexpr int kBeamRec = 2 + 2 * (kMaxBeamWidth + 1);  // words per chunk record
-constexpr int kMaxBeamWords = 8192;                  // records staged by the last workgroup
+constexpr int kMaxBeamEntries = 512;                 // chunk entries merged per beam (8 per lane)
 struct BeamArgs {
   const void *logits;            // [B][K][V]
   int dtype;

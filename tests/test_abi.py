@@ -107,7 +107,8 @@ def test_verify_accept_validation(lib):
     assert f(FAKE, 0, 1, 5, 0, FAKE, 5, None, FAKE, FAKE, FAKE, big, None) == -2
     assert f(FAKE, 0, 1, 5, 51865, FAKE, 5, None, FAKE, FAKE, None, 0, None) == -6
     assert f(FAKE, 0, 1, 5, 51865, FAKE, 5, None, FAKE, FAKE, FAKE, 100, None) == -6
-    assert f(MIS, 0, 1, 5, 51865, FAKE, 5, None, FAKE, FAKE, FAKE, big, None) == -7
+    assert f(FAKE + 2, 0, 1, 5, 51865, FAKE, 5, None, FAKE, FAKE, FAKE, big, None) == -7  # f32
+    assert f(FAKE + 1, 1, 1, 5, 51865, FAKE, 5, None, FAKE, FAKE, FAKE, big, None) == -7  # f16
 
 
 def test_workspace_sizes(lib):
@@ -148,6 +149,8 @@ def test_beam_select_validation(lib):
     assert call(fs=None) == -1
     assert call(dt=9) == -3
     assert call(K=0) == -2 and call(K=17) == -2 and call(V=5) == -2 and call(B=0) == -2
-    assert call(K=16, V=4096 * 15) == -2          # 16 beams x 15 chunks of records exceed the staging
+    assert call(K=16, V=61441) == -2              # 31 chunks x 17 entries exceed the 512 merged per beam
+    assert call(K=1, V=524289) == -2               # 257 chunks x 2 entries
     assert call(ws=None) == -6 and call(wsb=ws_need - 4) == -6
-    assert call(logits=MIS) == -7 and call(parent=FAKE + 2) == -7
+    assert call(logits=FAKE + 2) == -7 and call(logits=FAKE + 1, dt=kb.F16) == -7
+    assert call(parent=FAKE + 2) == -7

@@ -559,6 +559,43 @@ def test_beam_select_shapes(dtype, B, K, V):
     _beam_check(logits, dtype, sums, eot, res)
 
 
+@pytest.mark.parametrize("B,K,V", [(1, 16, 61440), (1, 1, 524288)])
+def test_beam_select_largest_vocabulary(B, K, V):
+    """The largest vocabulary each beam width takes: every lane of the merge
+    holds 8 chunk entries."""
+    say(f"case: beam select limit B={B} K={K} V={V}")
+    g = np.random.default_rng([23, K, V])
+    logits = (g.standard_normal((B, K, V)) * 2).astype(np.float32)
+    sums = (-g.random((B, K)) * 3).astype(np.float32)
+    res = kb.beam_select(to_dev(logits, "f32"), torch.from_numpy(sums).cuda(), V - 1)
+    torch.cuda.synchronize()
+    _beam_check(logits, "f32", sums, V - 1, res)
+
+
+@pytest.mark.parametrize("kind", ["ties", "masked"])
+def test_beam_select_ties_and_masks(kind):
+    """Equal logits and equal scores (integer logits, equal running scores:
+    lower token, then lower beam first), and masked vocabulary (-inf over half
+    the tokens and over a whole 2048-token chunk, with -0.0 and +0.0 tied)."""
+    say(f"case: beam select {kind}")
+    B, K, V = 2, 5, 9000
+    g = np.random.default_rng([24, len(kind)])
+    logits = (g.standard_normal((B, K, V)) * 2).astype(np.float32)
+    sums = (-g.random((B, K)) * 3).astype(np.float32)
+    if kind == "ties":
+        logits = np.round(logits)
+        sums[:] = -1.0
+    else:
+        logits[g.random(logits.shape) < 0.5] = -np.inf
+        logits[:, :, 2048:4096] = -np.inf
+        logits[:, :, 5000:5003] = [0.0, -0.0, 0.0]
+        logits[:, :, 6000:6003] = logits.max() + 1
+    eot = 6001
+    res = kb.beam_select(to_dev(logits, "f32"), torch.from_numpy(sums).cuda(), eot)
+    torch.cuda.synchronize()
+    _beam_check(logits, "f32", sums, eot, res)
+
+
 def test_beam_select_repeated_calls_share_workspace():
     """The workspace counters reset themselves: ten calls in a row on one
     workspace, alternating shapes."""
