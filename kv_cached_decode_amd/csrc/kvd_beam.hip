@@ -8,14 +8,14 @@
 //
 // Orders are taken on 64-bit keys whose unsigned order is the order wanted:
 // (logit, token) pairs and candidates become one integer each, so a selection
-// step is one 64-bit max over the wavefront in lane exchanges (DPP and
-// permlane swaps), with no LDS round trip and no barrier.
+// step is a max over the wavefront in lane exchanges (DPP and permlane swaps)
+// with no LDS round trip and no barrier.
 //
 // Workgroup (chunk, beam, row) reads 2048 logits (4 per thread) and publishes
 // a record: the chunk's max, its sum of exp(x - max), and its K + 1 best keys.
-// Each wavefront finds its own K + 1 best in K + 1 rounds (the lane holding a
-// round's winner drops it and rescans its items); wavefront 0 merges the eight
-// lists the same way. The last workgroup of the audio row to arrive gives each
+// Each wavefront finds its own K + 1 best in K + 1 rounds (each lane sorts its
+// keys once; the lane holding a round's winner shifts its list); wavefront 0
+// merges the eight lists the same way. The last workgroup of the audio row to arrive gives each
 // beam to a wavefront: log-sum-exp over the chunk records, then the beam's
 // K + 1 best out of every chunk's entries, again in rounds. The K (K + 1)
 // candidates are then placed in parallel: a candidate's position in the walk
@@ -75,58 +75,78 @@ __device__ __forceinline__ uint64_t cand_key(float score, int t, int tok) {
 }
 __device__ __forceinline__ int cand_token(uint64_t k) { return (int)(k & ((1u << kTokBits) - 1)); }
 
-__device__ __forceinline__ uint64_t max64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
 template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_mov64(uint64_t x) {
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, CTRL, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), CTRL, 0xF, 0xF, false);
-  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
 }
-// The pair {x[lane], x[lane ^ 16]} (resp. ^ 32) arrives in the two results in
-// the same lane-dependent order for both halves, so halves pair up by result.
-__device__ __forceinline__ uint64_t pair_max64_16(uint64_t x) {
-  const unsigned lo = (unsigned)x, hi = (unsigned)(x >> 32);
-  const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
-  const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
-  return max64(((uint64_t)(unsigned)h[0] << 32) | (unsigned)l[0],
-               ((uint64_t)(unsigned)h[1] << 32) | (unsigned)l[1]);
-}
-__device__ __forceinline__ uint64_t pair_max64_32(uint64_t x) {
-  const unsigned lo = (unsigned)x, hi = (unsigned)(x >> 32);
-  const auto l = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
-  const auto h = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
-  return max64(((uint64_t)(unsigned)h[0] << 32) | (unsigned)l[0],
-               ((uint64_t)(unsigned)h[1] << 32) | (unsigned)l[1]);
-}
-// Max over the wavefront; every lane ends with it.
-__device__ __forceinline__ uint64_t wave_max64(uint64_t x) {
-  x = max64(x, dpp_mov64<kDppQuadXor1>(x));
-  x = max64(x, dpp_mov64<kDppQuadXor2>(x));
-  x = max64(x, dpp_mov64<kDppHalfMirror>(x));
-  x = max64(x, dpp_mov64<kDppRowRor8>(x));
-  return pair_max64_32(pair_max64_16(x));
+// Unsigned max over the wavefront; every lane ends with it. (permlane swaps
+// with both operands x leave {x[lane], x[lane ^ 16]} (resp. ^ 32) in the two
+// results, and max is symmetric.)
+__device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
+  x = umax(x, dpp_u32<kDppQuadXor1>(x));
+  x = umax(x, dpp_u32<kDppQuadXor2>(x));
+  x = umax(x, dpp_u32<kDppHalfMirror>(x));
+  x = umax(x, dpp_u32<kDppRowRor8>(x));
+  const auto r16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = umax((uint32_t)r16[0], (uint32_t)r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return umax((uint32_t)r32[0], (uint32_t)r32[1]);
 }
 
-// The wavefront's n best keys among the N keys each lane holds (0 = none):
-// lane r (r < n) returns the r-th. Each round takes the wavefront max; the
-// lane holding it (keys are distinct) clears it and rescans.
+// Sorting networks (larger first) for the few keys one lane holds.
+__device__ __forceinline__ void order2(uint64_t &x, uint64_t &y) {
+  const uint64_t hi = x > y ? x : y, lo = x > y ? y : x;
+  x = hi;
+  y = lo;
+}
+template <int N>
+__device__ __forceinline__ void sort_desc(uint64_t (&k)[N]) {
+  static_assert(N == 3 || N == 4 || N == 8, "sorting network sizes");
+  if constexpr (N == 3) {
+    order2(k[0], k[1]); order2(k[0], k[2]); order2(k[1], k[2]);
+  } else if constexpr (N == 4) {
+    order2(k[0], k[1]); order2(k[2], k[3]); order2(k[0], k[2]); order2(k[1], k[3]);
+    order2(k[1], k[2]);
+  } else {  // Batcher's odd-even merge sort, 19 comparators
+    order2(k[0], k[1]); order2(k[2], k[3]); order2(k[4], k[5]); order2(k[6], k[7]);
+    order2(k[0], k[2]); order2(k[1], k[3]); order2(k[4], k[6]); order2(k[5], k[7]);
+    order2(k[1], k[2]); order2(k[5], k[6]);
+    order2(k[0], k[4]); order2(k[1], k[5]); order2(k[2], k[6]); order2(k[3], k[7]);
+    order2(k[2], k[4]); order2(k[3], k[5]);
+    order2(k[1], k[2]); order2(k[3], k[4]); order2(k[5], k[6]);
+  }
+}
+
+// The wavefront's n best keys among the N keys each lane holds (0 = none;
+// real keys are distinct): lane r (r < n) returns the r-th. With each lane's
+// keys sorted, a round reduces the high words (the value) over the wavefront;
+// when one lane holds that value its low word is read from it, otherwise a
+// second reduction over the tied lanes' low words decides. The lane holding
+// the winner then shifts its list.
 template <int N>
 __device__ __forceinline__ uint64_t wave_top(uint64_t (&k)[N], int n, int lane) {
-  uint64_t best = 0;
-#pragma unroll
-  for (int q = 0; q < N; ++q) best = max64(best, k[q]);
+  sort_desc(k);
   uint64_t mine = 0;
   for (int r = 0; r < n; ++r) {
-    const uint64_t win = wave_max64(best);
-    if (lane == r) mine = win;
-    if (best == win && win != 0) {
-      best = 0;
+    const uint32_t hi = (uint32_t)(k[0] >> 32), lo = (uint32_t)k[0];
+    const uint32_t whi = wave_umax(hi);
+    const uint64_t tied = __builtin_amdgcn_ballot_w64(hi == whi);
+    uint32_t wlo;
+    int owner;
+    if (__builtin_popcountll(tied) == 1) {
+      owner = __builtin_ctzll(tied);
+      wlo = (uint32_t)__builtin_amdgcn_readlane((int)lo, owner);
+    } else {
+      wlo = wave_umax(hi == whi ? lo : 0u);
+      owner = __builtin_ctzll(__builtin_amdgcn_ballot_w64(hi == whi && lo == wlo));
+    }
+    if (lane == r) mine = ((uint64_t)whi << 32) | wlo;
+    if (lane == owner) {
 #pragma unroll
-      for (int q = 0; q < N; ++q) {
-        if (k[q] == win) k[q] = 0;
-        best = max64(best, k[q]);
-      }
+      for (int q = 0; q + 1 < N; ++q) k[q] = k[q + 1];
+      k[N - 1] = 0;
     }
   }
   return mine;
@@ -201,7 +221,8 @@ __global__ __launch_bounds__(kThreads) void beam_kernel(BeamArgs a) {
   if (!s_last) return;
 
   // ---- last workgroup of audio row b: beam bj on wavefront bj mod 8
-  __shared__ uint64_t s_cand[kMaxCand];
+  __shared__ __align__(16) uint64_t s_cand[kMaxCand + 7];
+  __shared__ __align__(16) uint64_t s_eot[kMaxBeamWidth];
   __shared__ int s_nf;
   if (tid == 0) s_nf = 0;
   const int E = a.chunks * KP;
@@ -232,13 +253,20 @@ __global__ __launch_bounds__(kThreads) void beam_kernel(BeamArgs a) {
     S = groups_sum<1>(S);
     const float lse = M + logf(S);
     const uint64_t best = wave_top(ent, KP, lane);
+    const int tok = (int)~(uint32_t)best;
+    uint64_t ck = 0;
     if (lane < KP) {
       const float v = order_value((uint32_t)(best >> 32));
-      const int tok = (int)~(uint32_t)best;
       const int t = bj * KP + lane;
-      s_cand[t] = cand_key(sl + (v - lse), t, tok);
+      ck = cand_key(sl + (v - lse), t, tok);
+      s_cand[t] = ck;
     }
+    // a beam's tokens are distinct: at most one of its candidates is end-of-text
+    const uint64_t is_eot = __builtin_amdgcn_ballot_w64(lane < KP && tok == a.eot);
+    if (lane == (is_eot ? __builtin_ctzll(is_eot) : 0)) s_eot[bj] = is_eot ? ck : 0;
   }
+  if (tid < 7) s_cand[K * KP + tid] = 0;                   // pad to whole blocks of 8
+  if (tid >= K && tid < kMaxBeamWidth) s_eot[tid] = 0;
   __syncthreads();
 
   // ---- the walk, in parallel: candidate t ranks after `rank` others, `eots`
@@ -249,13 +277,12 @@ __global__ __launch_bounds__(kThreads) void beam_kernel(BeamArgs a) {
   if (tid < nc) {
     const uint64_t me = s_cand[tid];
     int rank = 0, eots = 0;
-#pragma unroll 8
-    for (int u = 0; u < nc; ++u) {
-      const uint64_t o = s_cand[u];
-      const int before = (o > me) ? 1 : 0;
-      rank += before;
-      eots += before & ((cand_token(o) == a.eot) ? 1 : 0);
+    for (int u = 0; u < nc; u += 8) {  // 0 (the pad) ranks after every candidate
+#pragma unroll
+      for (int v = 0; v < 8; ++v) rank += (s_cand[u + v] > me) ? 1 : 0;
     }
+#pragma unroll
+    for (int bj = 0; bj < kMaxBeamWidth; ++bj) eots += (s_eot[bj] > me) ? 1 : 0;
     const int kept = rank - eots;
     if (kept < K) {
       const int beam = tid / KP, tok = cand_token(me);
