@@ -220,6 +220,53 @@ def attainable(torch, kb, eng: Engine, reps: int = 8):
     return dur, period, curve
 
 
+def cold_numbers(torch, kb, eng: Engine, graphs, K: int, every: int = 7):
+    """The same work with the 256 MB Infinity Cache evicted first: a 512 MB
+    device write (outside the timed region) before each sampled decode step
+    (one graph replay, HIP events around it on the replay stream) and before
+    each cross-attention and read-probe launch (events at kernel begin and
+    end)."""
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    blocks = list(range(0, S_MAX // K, every))
+    pairs = []
+    for i, b in enumerate(blocks):
+        flush.fill_(i & 0xFF)
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        graphs[b].replay()
+        e.record(stream)
+        pairs.append((a, e))
+    torch.cuda.synchronize()
+    step_s = float(np.mean([a.elapsed_time(e) for a, e in pairs])) * 1e-3 / K
+    kv = float(np.mean([kv_bytes_per_step(b * K + j + 1) for b in blocks for j in range(K)]))
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    half = CROSS_BYTES // 2
+
+    def flushed(fn, i):
+        flush.fill_(i & 0xFF)
+        fn()
+    cross = _event_durations(torch, kb, [lambda l=l: flushed(lambda: eng.cross(l, l), l)
+                                         for _ in range(2) for l in range(LAYERS)])
+    probe = _event_durations(torch, kb, [lambda l=l: flushed(
+        lambda: kb.read_probe(eng.cross_c[l].k, eng.cross_c[l].v, half, sink), l)
+        for _ in range(2) for l in range(LAYERS)])
+    del flush
+    return {"what": "512 MB written before each timed unit (outside it), evicting the 256 MB "
+                    "Infinity Cache",
+            "steps_per_s": round(1 / step_s, 2), "ms_per_step": round(step_s * 1e3, 5),
+            "effective_kv_gbps": round(kv / step_s / 1e9, 1),
+            "hbm_peak_frac": round(kv / step_s / 1e9 / HBM_PEAK_GBPS, 4),
+            "sample": f"{len(blocks) * K} decode steps (every {every}th graph of the 1..448 sweep), "
+                      "each timed alone from its graph launch",
+            "cross_kernel_us": round(cross * 1e6, 3),
+            "cross_gbps": round(CROSS_BYTES / cross / 1e9, 1),
+            "cross_frac": round(CROSS_BYTES / cross / 1e9 / HBM_PEAK_GBPS, 4),
+            "probe_us": round(probe * 1e6, 3),
+            "probe_gbps": round(CROSS_BYTES / probe / 1e9, 1),
+            "cross_frac_of_attainable": round(probe / cross, 4)}
+
+
 def cpu_baseline(target_s: float = 12.0):
     """The CPU oracle (numpy, float64) on a bounded sample of the same steps:
     full 32-layer steps at lengths spread over 1..448, BLAS pinned to one
@@ -349,6 +396,7 @@ def main():
     achieved = CROSS_BYTES / k_period / 1e9
     traffic = measured_traffic()
     p_avg, p_period, curve = attainable(torch, kb, eng)
+    cold = cold_numbers(torch, kb, eng, graphs, K)
 
     cpu = None if args.no_cpu else cpu_baseline()
 
@@ -392,6 +440,7 @@ def main():
                        "alone_launch_us": round(p_avg * 1e6, 3),
                        "cross_frac_of_attainable": round(p_period / k_period, 4),
                        "probe_gbps_by_size_alone": curve},
+        "cold": cold,
         "cpu_baseline": cpu,
     }
     if eager is not None:
