@@ -29,7 +29,9 @@ theta_i = base^(-2i/D) and is applied to keys before they are cached and to
 queries at attention time; argmax ties go to the lowest index; verify row i
 is compared with draft i. The rotary variant itself is a reading (the pages
 name only the start_pos argument): parity for it is pinned to the RoFormer
-identities, not to the pages. Beam-search candidate scoring follows the
+identities, not to the pages. Logit filters set suppressed tokens to -inf
+before the argmax: one token set on every row, and one more on the first
+sampled row only. Beam-search candidate scoring follows the
 decoder's update steps on [W]; the readings there: natural-log softmax, each
 beam's K + 1 best tokens with equal values in index order, candidates with
 equal scores in the order beam then rank, and end-of-text candidates met
@@ -296,6 +298,35 @@ def verify_accept(logits: np.ndarray, draft: np.ndarray):
     for b in range(B):
         acc[b], nxt[b] = accept(am[b], draft[b])
     return am, acc, nxt
+
+
+# ---------------------------------------------------------------------------
+# Logit filters before the argmax ([W] section "LogitFilter チェーン":
+# SuppressBlank sets the blank and end-of-text logits to -inf at the first
+# sampled position only, SuppressTokens sets a fixed token list to -inf on
+# every step; section "言語検出": every token but the language tokens at -inf,
+# then argmax).
+# ---------------------------------------------------------------------------
+
+
+def apply_suppression(logits: np.ndarray, suppress=None, suppress_first=None) -> np.ndarray:
+    """Float64 copy of logits [B, R, V] with suppressed tokens at -inf:
+    `suppress` (boolean [V]) on every row, `suppress_first` (boolean [V]) on
+    row 0 of each batch row as well (the first sampled position)."""
+    x = np.array(logits, dtype=np.float64, copy=True)
+    if suppress is not None:
+        x[:, :, np.asarray(suppress, dtype=bool)] = -np.inf
+    if suppress_first is not None:
+        x[:, 0, np.asarray(suppress_first, dtype=bool)] = -np.inf
+    return x
+
+
+def verify_accept_masked(logits: np.ndarray, draft: np.ndarray, suppress=None,
+                         suppress_first=None):
+    """verify_accept on the filtered logits. With no drafts (N = 0, R = 1) it
+    is the masked argmax of one row per batch row: a greedy step, or language
+    detection with every non-language token suppressed."""
+    return verify_accept(apply_suppression(logits, suppress, suppress_first), draft)
 
 
 # ---------------------------------------------------------------------------

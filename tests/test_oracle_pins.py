@@ -462,3 +462,75 @@ def test_beam_select_row_shift_invariance():
     b = O.beam_select(logits + np.array([5.0, -3.0, 0.25])[None, :, None], sums, 7)
     for x, y in zip(a, b):
         np.testing.assert_allclose(x, y, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------- logit filters + argmax ----
+# [W] "LogitFilter チェーン" (SuppressBlank at the first sampled position,
+# SuppressTokens on every step) and "言語検出" (non-language tokens at -inf,
+# then argmax).
+
+
+def test_masked_argmax_language_detection_is_argmax_over_language_tokens():
+    g = np.random.default_rng(15)
+    V = 3000
+    lang = np.sort(g.choice(V, size=99, replace=False))     # the language tokens
+    logits = g.standard_normal((4, 1, V))
+    logits[0, 0, 5] = 50.0                                 # a non-language token is the global max
+    logits[1, 0, lang[[7, 30]]] = 40.0                     # tied best among the language tokens
+    suppress = np.ones(V, dtype=bool)
+    suppress[lang] = False
+    am, acc, nxt = O.verify_accept_masked(logits, np.zeros((4, 0), dtype=np.int32), suppress)
+    want = [lang[int(np.argmax(logits[b, 0, lang]))] for b in range(4)]   # first maximum in id order
+    assert nxt.tolist() == want and (acc == 0).all()
+    assert nxt[1] == lang[7] and nxt[0] != 5
+
+
+def test_masked_argmax_suppress_blank_only_at_first_row():
+    g = np.random.default_rng(16)
+    V, blank, eot = 800, 220, 799
+    logits = g.standard_normal((2, 3, V))
+    logits[:, :, blank] = 30.0                             # blank is every row's max
+    logits[1, 0, eot] = 31.0                               # end-of-text beats it on (1, 0)
+    first = np.zeros(V, dtype=bool)
+    first[[blank, eot]] = True
+    am, _, _ = O.verify_accept_masked(logits, np.zeros((2, 2), dtype=np.int32), None, first)
+    for b in range(2):
+        order = np.argsort(-logits[b, 0], kind="stable")
+        assert am[b, 0] == [t for t in order if t not in (blank, eot)][0]
+        assert am[b, 1] == blank and am[b, 2] == blank
+
+
+def test_masked_argmax_ignores_suppressed_values_and_all_suppressed_gives_zero():
+    g = np.random.default_rng(17)
+    V = 500
+    logits = g.standard_normal((3, 2, V))
+    sup = g.random(V) < 0.3
+    draft = g.integers(0, V, (3, 1)).astype(np.int32)
+    a = O.verify_accept_masked(logits, draft, sup)
+    changed = logits.copy()
+    changed[:, :, sup] = g.standard_normal((3, 2, int(sup.sum()))) * 1e6   # any value at all
+    b = O.verify_accept_masked(changed, draft, sup)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    for b_ in range(3):                                    # brute force over the allowed tokens
+        for r in range(2):
+            allowed = [t for t in range(V) if not sup[t]]
+            best = max(allowed, key=lambda t: (logits[b_, r, t], -t))
+            assert a[0][b_, r] == best
+    am, _, nxt = O.verify_accept_masked(logits, np.zeros((3, 0), dtype=np.int32)[:, :0],
+                                        np.ones(V, dtype=bool))
+    assert (am == 0).all()
+
+
+def test_masked_verify_rejects_a_draft_the_filter_removes():
+    V = 50
+    logits = np.zeros((1, 3, V))
+    logits[0, :, 9] = 5.0                                  # every row's unfiltered argmax is 9
+    logits[0, :, 4] = 2.0
+    draft = np.array([[9, 9]], dtype=np.int32)
+    am, acc, nxt = O.verify_accept(logits, draft)
+    assert acc[0] == 2 and nxt[0] == 9
+    sup = np.zeros(V, dtype=bool)
+    sup[9] = True                                          # SuppressTokens removes token 9
+    am, acc, nxt = O.verify_accept_masked(logits, draft, sup)
+    assert am.tolist() == [[4, 4, 4]] and acc[0] == 0 and nxt[0] == 4
