@@ -537,6 +537,13 @@ def workload_verify(torch, kb, reps):
     self_us = _kernel_us(torch, kb, lambda i: kb.decode_step_self(q[i % LAYERS], kn[i % LAYERS], vn[i % LAYERS], self_c[i % LAYERS], 448, 1 / 8, out=out[0], ws=ws))
     cross_us = _kernel_us(torch, kb, lambda i: kb.decode_attn_cross(qx[i % LAYERS], cross_c[i % LAYERS], FRAMES, 1 / 8, out=outx[0], ws=ws))
     verify_us = _kernel_us(torch, kb, lambda i: kb.verify_accept(logits, draft, ws=ws, accept_len=acc, next_token=nxt))
+    # the same with the logit filters: 90 suppressed tokens on every row, blank
+    # and end-of-text on the first row
+    V = logits.shape[-1]
+    sup = kb.token_bitmap(range(50358, 50448), V)
+    first = kb.token_bitmap([220, 50256], V)
+    masked_us = _kernel_us(torch, kb, lambda i: kb.verify_accept_masked(
+        logits, draft, sup, first, ws=ws, accept_len=acc, next_token=nxt))
     p = [0.75 ** k * 0.25 for k in range(5)] + [0.75 ** 5]
     tokens = sum(pk * t for pk, t in zip(p, [1, 2, 3, 4, 5, 5]))
     return {"metric": "speculative verify steps/s (N=5 drafts), large-v2 shape, 1 GPU",
@@ -544,7 +551,8 @@ def workload_verify(torch, kb, reps):
             "effective_kv_gbps": round(kv / sec / 1e9, 1),
             "tokens_per_s_at_p075": round(tokens / sec, 1),
             "kernels_us": {"step_self_N5_len448 (matrix-core tile)": round(self_us, 3),
-                           "cross_N5": round(cross_us, 3), "verify_accept_V51865": round(verify_us, 3)},
+                           "cross_N5": round(cross_us, 3), "verify_accept_V51865": round(verify_us, 3),
+                           "verify_accept_masked_V51865": round(masked_us, 3)},
             "config": {"workload": "whisper-large-v2 verify: 32 layers x [append 5 + self N=5, cross N=5 "
                                    "over 1500] + verify_accept [1, 5, 51865]; len before 64..443"}}
 

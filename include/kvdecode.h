@@ -172,13 +172,35 @@ int decode_attn_cross(const void *q, int32_t B, int32_t Hq, int32_t N,
  *   ws: device workspace, ws_bytes >= kvd_verify_workspace_bytes(B, R, V),
  *     zero-filled before its first use and left that way.
  * Errors: KVD_ERR_NULL, KVD_ERR_SHAPE (B, N, V < 1; N > 63; B > 4096;
- *   R * ceil(V / 4096) > 2048), KVD_ERR_ROWS,
+ *   V > 1048576), KVD_ERR_ROWS,
  *   KVD_ERR_DTYPE, KVD_ERR_WORKSPACE, KVD_ERR_ALIGN (logits not aligned to
  *   their element, other pointers to 4 bytes). */
 int verify_accept(const void *logits, int32_t logits_dtype, int32_t B, int32_t R,
                   int32_t V, const int32_t *draft, int32_t N, int32_t *argmax_out,
                   int32_t *accept_len, int32_t *next_token, void *ws,
                   size_t ws_bytes, void *stream);
+
+/* verify_accept_masked - verify_accept after the logit filters of [W]
+ * (section "LogitFilter チェーン": SuppressTokens sets a fixed token list to
+ * -inf on every step, SuppressBlank sets the blank and end-of-text tokens to
+ * -inf at the first sampled position; section "言語検出": every token but the
+ * language tokens at -inf, then argmax). A suppressed logit counts as -inf
+ * and the argmax then follows verify_accept's rules.
+ *   suppress: device bitmap of ceil(V / 32) uint32 words (bit t % 32 of word
+ *     t / 32 set: token t suppressed) applied to every row, or NULL.
+ *   suppress_first: the same, applied in addition to row 0 of each batch row
+ *     (the first sampled position), or NULL.
+ *   N may be 0 (draft may then be NULL) with R = 1: next_token[b] is the
+ *     filtered argmax of the one row, as in a greedy step or language
+ *     detection.
+ *   Other arguments, the workspace (kvd_verify_workspace_bytes(B, R, V)) and
+ *   the errors are those of verify_accept; the bitmaps must be 4-byte
+ *   aligned. */
+int verify_accept_masked(const void *logits, int32_t logits_dtype, int32_t B, int32_t R,
+                         int32_t V, const int32_t *draft, int32_t N, const uint32_t *suppress,
+                         const uint32_t *suppress_first, int32_t *argmax_out,
+                         int32_t *accept_len, int32_t *next_token, void *ws, size_t ws_bytes,
+                         void *stream);
 
 /* beam_select - one beam-search update for each audio row b, following the
  * beam-search decoder's update steps on [W] (step 4, reordering the caches

@@ -13,6 +13,7 @@ import os
 import re
 from ctypes import c_float, c_int, c_int32, c_size_t, c_void_p
 
+import numpy as np
 import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvdecode.so")
@@ -52,6 +53,9 @@ _SIGNATURES = {
     "verify_accept": (c_int, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_int32,
                               c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "kvd_attn_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32]),
+    "verify_accept_masked": (c_int, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p,
+                                     c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                     c_void_p, c_size_t, c_void_p]),
     "kvd_verify_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
     "beam_select": (c_int, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_int32,
                             c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -295,6 +299,57 @@ def verify_accept(logits: torch.Tensor, draft: torch.Tensor,
         _dev(draft, "draft", torch.int32), N, am, _dev(accept_len, "accept_len", torch.int32),
         _dev(next_token, "next_token", torch.int32), _dev(ws, "ws"),
         ws.numel() * ws.element_size(), _stream()))
+    return accept_len, next_token, argmax_out
+
+
+def token_bitmap(tokens, V: int, device="cuda") -> torch.Tensor:
+    """Suppression bitmap for verify_accept_masked: ceil(V / 32) words, bit
+    t % 32 of word t / 32 set for every token t listed (held as int32)."""
+    ids = np.asarray(list(tokens), dtype=np.int64)
+    if ids.size and (ids.min() < 0 or ids.max() >= V):
+        raise ValueError("token ids must lie in [0, V)")
+    bits = np.zeros((V + 31) // 32, dtype=np.uint32)
+    np.bitwise_or.at(bits, ids >> 5, (np.uint32(1) << (ids & 31).astype(np.uint32)))
+    return torch.from_numpy(bits.view(np.int32)).to(device)
+
+
+def verify_accept_masked(logits: torch.Tensor, draft: torch.Tensor | None,
+                         suppress: torch.Tensor | None = None,
+                         suppress_first: torch.Tensor | None = None,
+                         argmax_out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                         accept_len: torch.Tensor | None = None,
+                         next_token: torch.Tensor | None = None):
+    """verify_accept after the logit filters: `suppress` (every row) and
+    `suppress_first` (row 0 of each batch row) are token_bitmap() tensors or
+    None; draft may be None or [B, 0] (then R = 1: a masked argmax). Returns
+    (accept_len, next_token, argmax_out)."""
+    if logits.dim() != 3:
+        raise ValueError("logits must be [B, R, V]")
+    if logits.dtype not in DTYPE_CODE:
+        raise ValueError(f"unsupported logits dtype {logits.dtype}")
+    B, R, V = logits.shape
+    N = 0 if draft is None else draft.shape[1]
+    if draft is not None and (draft.dim() != 2 or draft.shape[0] != B):
+        raise ValueError("draft must be [B, N]")
+    words = (V + 31) // 32
+    for m, name in ((suppress, "suppress"), (suppress_first, "suppress_first")):
+        if m is not None and m.numel() != words:
+            raise ValueError(f"{name} must hold ceil(V / 32) = {words} words")
+    dev = logits.device
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if next_token is None:
+        next_token = torch.empty(B, dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = workspace(verify_workspace_bytes(B, R, V), dev)
+    am = _dev(argmax_out, "argmax_out", torch.int32) if argmax_out is not None else None
+    dr = _dev(draft, "draft", torch.int32) if N > 0 else None
+    sp = _dev(suppress, "suppress", torch.int32) if suppress is not None else None
+    sf = _dev(suppress_first, "suppress_first", torch.int32) if suppress_first is not None else None
+    _check("verify_accept_masked", lib().verify_accept_masked(
+        _dev(logits, "logits"), DTYPE_CODE[logits.dtype], B, R, V, dr, N, sp, sf, am,
+        _dev(accept_len, "accept_len", torch.int32), _dev(next_token, "next_token", torch.int32),
+        _dev(ws, "ws"), ws.numel() * ws.element_size(), _stream()))
     return accept_len, next_token, argmax_out
 
 

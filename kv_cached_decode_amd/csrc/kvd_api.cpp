@@ -307,16 +307,28 @@ size_t kvd_attn_workspace_bytes(int32_t B, int32_t Hq, int32_t N, int32_t len_ma
   return best;
 }
 
-int verify_accept(const void *logits, int32_t logits_dtype, int32_t B, int32_t R, int32_t V,
-                  const int32_t *draft, int32_t N, int32_t *argmax_out, int32_t *accept_len,
-                  int32_t *next_token, void *ws, size_t ws_bytes, void *stream) {
-  if (!logits || !draft || !accept_len || !next_token) return KVD_ERR_NULL;
+}  // extern "C"
+
+namespace {
+
+// verify_accept with optional suppression bitmaps; min_n is the smallest
+// draft count the entry point accepts.
+int verify_impl(const void *logits, int32_t logits_dtype, int32_t B, int32_t R, int32_t V,
+                const int32_t *draft, int32_t N, int min_n, const uint32_t *suppress,
+                const uint32_t *suppress_first, int32_t *argmax_out, int32_t *accept_len,
+                int32_t *next_token, void *ws, size_t ws_bytes, void *stream) {
+  if (!logits || (N > 0 && !draft) || !accept_len || !next_token) return KVD_ERR_NULL;
   if (!dtype_ok(logits_dtype)) return KVD_ERR_DTYPE;
-  if (B < 1 || N < 1 || V < 1 || N > 63 || B > kvd::kMaxCounters) return KVD_ERR_SHAPE;
+  if (B < 1 || N < min_n || V < 1 || N > 63 || B > kvd::kMaxCounters) return KVD_ERR_SHAPE;
   if (R != N && R != N + 1) return KVD_ERR_ROWS;
+  if (R < 1) return KVD_ERR_ROWS;
+  int chunk = 0, chunks = 0;
+  kvd::plan_verify(B, R, V, chunk, chunks);
+  if (chunks > kvd::kMaxVerifyChunks) return KVD_ERR_SHAPE;
   if (!elem_aligned(logits, logits_dtype)) return KVD_ERR_ALIGN;
-  if (!aligned4(draft) || !aligned4(accept_len) || !aligned4(next_token) ||
-      (argmax_out && !aligned4(argmax_out)))
+  if ((draft && !aligned4(draft)) || !aligned4(accept_len) || !aligned4(next_token) ||
+      (argmax_out && !aligned4(argmax_out)) || (suppress && !aligned4(suppress)) ||
+      (suppress_first && !aligned4(suppress_first)))
     return KVD_ERR_ALIGN;
   const size_t need = kvd_verify_workspace_bytes(B, R, V);
   if (!ws || ws_bytes < need) return KVD_ERR_WORKSPACE;
@@ -328,18 +340,38 @@ int verify_accept(const void *logits, int32_t logits_dtype, int32_t B, int32_t R
   a.argmax_out = argmax_out;
   a.accept_len = accept_len;
   a.next_token = next_token;
+  a.suppress = suppress;
+  a.suppress_first = suppress_first;
   a.B = B;
   a.R = R;
   a.V = V;
   a.N = N;
-  kvd::plan_verify(B, R, V, a.chunk, a.chunks);
-  if ((int64_t)R * a.chunks > kvd::kMaxVerifyPartials) return KVD_ERR_SHAPE;
-  const size_t slots = (size_t)B * R * a.chunks;
-  const size_t val_bytes = ((slots * sizeof(float) + 255) / 256) * 256;
+  a.chunk = chunk;
+  a.chunks = chunks;
   a.ws_count = static_cast<uint32_t *>(ws);
-  a.ws_val = reinterpret_cast<float *>(static_cast<char *>(ws) + kCounterBytes);
-  a.ws_idx = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + kCounterBytes + val_bytes);
+  a.ws_key = reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + kCounterBytes);
   return status_of(kvd::launch_verify(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int verify_accept(const void *logits, int32_t logits_dtype, int32_t B, int32_t R, int32_t V,
+                  const int32_t *draft, int32_t N, int32_t *argmax_out, int32_t *accept_len,
+                  int32_t *next_token, void *ws, size_t ws_bytes, void *stream) {
+  if (!draft) return KVD_ERR_NULL;
+  return verify_impl(logits, logits_dtype, B, R, V, draft, N, 1, nullptr, nullptr, argmax_out,
+                     accept_len, next_token, ws, ws_bytes, stream);
+}
+
+int verify_accept_masked(const void *logits, int32_t logits_dtype, int32_t B, int32_t R,
+                         int32_t V, const int32_t *draft, int32_t N, const uint32_t *suppress,
+                         const uint32_t *suppress_first, int32_t *argmax_out,
+                         int32_t *accept_len, int32_t *next_token, void *ws, size_t ws_bytes,
+                         void *stream) {
+  return verify_impl(logits, logits_dtype, B, R, V, draft, N, 0, suppress, suppress_first,
+                     argmax_out, accept_len, next_token, ws, ws_bytes, stream);
 }
 
 size_t kvd_beam_workspace_bytes(int32_t B, int32_t K, int32_t V) {
@@ -390,8 +422,7 @@ size_t kvd_verify_workspace_bytes(int32_t B, int32_t R, int32_t V) {
   if (B < 1 || R < 1 || V < 1) return 0;
   int chunk = 0, chunks = 0;
   kvd::plan_verify(B, R, V, chunk, chunks);
-  const size_t slots = (size_t)B * R * chunks;
-  return kCounterBytes + ((slots * sizeof(float) + 255) / 256) * 256 + slots * sizeof(int32_t);
+  return kCounterBytes + (size_t)B * R * chunks * sizeof(uint64_t);
 }
 
 }  // extern "C"

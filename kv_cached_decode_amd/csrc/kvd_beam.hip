@@ -26,6 +26,7 @@
 
 #include "kvd_device.hpp"
 #include "kvd_internal.hpp"
+#include "kvd_select.hpp"
 
 namespace kvd {
 
@@ -44,29 +45,6 @@ constexpr uint32_t kTokBits = 23;                            // tokens < 2^23 (V
 static_assert(kMaxCand <= kThreads, "one thread per candidate");
 static_assert((kMaxCand - 1) < (1 << (32 - kTokBits)), "candidate number fits its field");
 
-template <int DT>
-__device__ __forceinline__ float load_logit(const char *row, int e) {
-  if constexpr (DT == F32) return reinterpret_cast<const float *>(row)[e];
-  else if constexpr (DT == F16) return (float)reinterpret_cast<const _Float16 *>(row)[e];
-  else return __builtin_bit_cast(float, (uint32_t)reinterpret_cast<const uint16_t *>(row)[e] << 16);
-}
-
-// Unsigned integers that compare as the floats do (-0 taken as +0; NaN is
-// outside the contract), and back.
-__device__ __forceinline__ uint32_t order_bits(float v) {
-  uint32_t u = __builtin_bit_cast(uint32_t, v);
-  if (u == 0x80000000u) u = 0;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float order_value(uint32_t k) {
-  return __builtin_bit_cast(float, (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
-
-// (logit, token): larger logit first, equal logits lower token first. Every
-// such key is nonzero; 0 stands for "none" and ranks last.
-__device__ __forceinline__ uint64_t entry_key(float v, int tok) {
-  return ((uint64_t)order_bits(v) << 32) | (uint32_t)~tok;
-}
 // Candidate t = beam * (K + 1) + rank with token tok: larger score first,
 // equal scores smaller t first; the token rides in the low bits.
 __device__ __forceinline__ uint64_t cand_key(float score, int t, int tok) {
@@ -74,83 +52,6 @@ __device__ __forceinline__ uint64_t cand_key(float score, int t, int tok) {
          ((uint32_t)(kMaxCand - 1 - t) << kTokBits) | (uint32_t)tok;
 }
 __device__ __forceinline__ int cand_token(uint64_t k) { return (int)(k & ((1u << kTokBits) - 1)); }
-
-__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
-}
-// Unsigned max over the wavefront; every lane ends with it. (permlane swaps
-// with both operands x leave {x[lane], x[lane ^ 16]} (resp. ^ 32) in the two
-// results, and max is symmetric.)
-__device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
-  x = umax(x, dpp_u32<kDppQuadXor1>(x));
-  x = umax(x, dpp_u32<kDppQuadXor2>(x));
-  x = umax(x, dpp_u32<kDppHalfMirror>(x));
-  x = umax(x, dpp_u32<kDppRowRor8>(x));
-  const auto r16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-  x = umax((uint32_t)r16[0], (uint32_t)r16[1]);
-  const auto r32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-  return umax((uint32_t)r32[0], (uint32_t)r32[1]);
-}
-
-// Sorting networks (larger first) for the few keys one lane holds.
-__device__ __forceinline__ void order2(uint64_t &x, uint64_t &y) {
-  const uint64_t hi = x > y ? x : y, lo = x > y ? y : x;
-  x = hi;
-  y = lo;
-}
-template <int N>
-__device__ __forceinline__ void sort_desc(uint64_t (&k)[N]) {
-  static_assert(N == 3 || N == 4 || N == 8, "sorting network sizes");
-  if constexpr (N == 3) {
-    order2(k[0], k[1]); order2(k[0], k[2]); order2(k[1], k[2]);
-  } else if constexpr (N == 4) {
-    order2(k[0], k[1]); order2(k[2], k[3]); order2(k[0], k[2]); order2(k[1], k[3]);
-    order2(k[1], k[2]);
-  } else {  // Batcher's odd-even merge sort, 19 comparators
-    order2(k[0], k[1]); order2(k[2], k[3]); order2(k[4], k[5]); order2(k[6], k[7]);
-    order2(k[0], k[2]); order2(k[1], k[3]); order2(k[4], k[6]); order2(k[5], k[7]);
-    order2(k[1], k[2]); order2(k[5], k[6]);
-    order2(k[0], k[4]); order2(k[1], k[5]); order2(k[2], k[6]); order2(k[3], k[7]);
-    order2(k[2], k[4]); order2(k[3], k[5]);
-    order2(k[1], k[2]); order2(k[3], k[4]); order2(k[5], k[6]);
-  }
-}
-
-// The wavefront's n best keys among the N keys each lane holds (0 = none;
-// real keys are distinct): lane r (r < n) returns the r-th. With each lane's
-// keys sorted, a round reduces the high words (the value) over the wavefront;
-// when one lane holds that value its low word is read from it, otherwise a
-// second reduction over the tied lanes' low words decides. The lane holding
-// the winner then shifts its list.
-template <int N>
-__device__ __forceinline__ uint64_t wave_top(uint64_t (&k)[N], int n, int lane) {
-  sort_desc(k);
-  uint64_t mine = 0;
-  for (int r = 0; r < n; ++r) {
-    const uint32_t hi = (uint32_t)(k[0] >> 32), lo = (uint32_t)k[0];
-    const uint32_t whi = wave_umax(hi);
-    const uint64_t tied = __builtin_amdgcn_ballot_w64(hi == whi);
-    uint32_t wlo;
-    int owner;
-    if (__builtin_popcountll(tied) == 1) {
-      owner = __builtin_ctzll(tied);
-      wlo = (uint32_t)__builtin_amdgcn_readlane((int)lo, owner);
-    } else {
-      wlo = wave_umax(hi == whi ? lo : 0u);
-      owner = __builtin_ctzll(__builtin_amdgcn_ballot_w64(hi == whi && lo == wlo));
-    }
-    if (lane == r) mine = ((uint64_t)whi << 32) | wlo;
-    if (lane == owner) {
-#pragma unroll
-      for (int q = 0; q + 1 < N; ++q) k[q] = k[q + 1];
-      k[N - 1] = 0;
-    }
-  }
-  return mine;
-}
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void beam_kernel(BeamArgs a) {
@@ -181,7 +82,7 @@ __global__ __launch_bounds__(kThreads) void beam_kernel(BeamArgs a) {
 #pragma unroll
   for (int q = 0; q < kItems; ++q) {
     const int e = e0 + q * kThreads + tid;
-    k[q] = (e < a.V) ? entry_key(x[q], e) : 0;
+    k[q] = (e < a.V) ? value_key(x[q], e) : 0;
   }
   __syncthreads();
   float cmax = s_max[0];

@@ -20,7 +20,7 @@ constexpr int kMaxCounters = 4096;
 constexpr int kMaxFusedRows = 16;
 constexpr int kMaxSplits = 64;  // key splits per tile: the merge gives each split one lane
 // verify_accept: (value, index) pairs one batch row may stage for its merge.
-constexpr int kMaxVerifyPartials = 2048;
+constexpr int kMaxVerifyChunks = 512;  // 2048-logit chunks per row (8 keys per lane in the merge)
 
 struct AppendArgs {
   void *k_cache, *v_cache;       // [B][H][S_max][D]
@@ -74,8 +74,9 @@ struct VerifyArgs {
   const int32_t *draft;          // [B][N]
   int32_t *argmax_out;           // [B][R] or null
   int32_t *accept_len, *next_token;
-  float *ws_val;                 // [B][R][chunks]
-  int32_t *ws_idx;               // [B][R][chunks]
+  const uint32_t *suppress;      // [ceil(V / 32)] bit t: token t at -inf on every row, or null
+  const uint32_t *suppress_first;  // the same for row 0 of each batch row, or null
+  uint64_t *ws_key;              // [B][R][chunks]
   uint32_t *ws_count;            // [B]
   int B, R, V, N;
   int chunk, chunks;

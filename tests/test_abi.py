@@ -111,6 +111,29 @@ def test_verify_accept_validation(lib):
     assert f(FAKE + 1, 1, 1, 5, 51865, FAKE, 5, None, FAKE, FAKE, FAKE, big, None) == -7  # f16
 
 
+def test_verify_accept_masked_validation(lib):
+    f = lib.verify_accept_masked
+    big = 1 << 30
+    ok = [FAKE, 0, 1, 5, 51865, FAKE, 5, FAKE, FAKE, None, FAKE, FAKE, FAKE, big, None]
+
+    def call(**kw):
+        args = list(ok)
+        names = ["logits", "dt", "B", "R", "V", "draft", "N", "sup", "first", "am", "acc", "nxt",
+                 "ws", "wsb", "stream"]
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return f(*args)
+    assert call(logits=None) == -1
+    assert call(draft=None) == -1                   # drafts needed when N > 0
+    assert call(draft=None, N=0, R=1, ws=None) == -6   # N = 0 takes no drafts (stops at the workspace)
+    assert call(N=0, R=2) == -5 and call(N=0, R=0) == -5
+    assert call(V=(1 << 20) + 1) == -2 and call(N=64, R=64) == -2
+    assert call(sup=FAKE + 2) == -7 and call(first=FAKE + 1) == -7
+    assert call(ws=None) == -6
+    assert lib.verify_accept(FAKE, 0, 1, 5, (1 << 20) + 1, FAKE, 5, None, FAKE, FAKE, FAKE, big,
+                             None) == -2
+
+
 def test_workspace_sizes(lib):
     # a 1500-key cache is split, a 40-key one is not (the counter block only)
     assert kb.attn_workspace_bytes(1, 20, 1, 1500) > 16384

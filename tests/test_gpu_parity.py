@@ -265,7 +265,7 @@ def test_verify_accept_edges(dtype):
         assert acc[0] == N and nxt[0] == (ref_am[0, N] if R == N + 1 else -1)
 
 
-@pytest.mark.parametrize("V", [1, 7, 4096, 4097, 12289])
+@pytest.mark.parametrize("V", [1, 7, 2048, 2049, 4096, 4097, 12289])
 def test_verify_accept_small_vocab(V):
     say(f"case: verify V={V}")
     g = np.random.default_rng(V)
@@ -274,6 +274,86 @@ def test_verify_accept_small_vocab(V):
     acc, nxt, am = _verify_gpu(logits, draft)
     ram, racc, rnxt = O.verify_accept(logits, draft)
     assert np.array_equal(am, ram) and np.array_equal(acc, racc) and np.array_equal(nxt, rnxt)
+
+
+def _masked_gpu(logits, draft, sup, first, dtype="f32"):
+    lt = to_dev(logits if dtype == "f32" else O.narrow(logits.astype(np.float64), dtype), dtype)
+    B, R, V = logits.shape
+    dt = torch.from_numpy(draft).to("cuda") if draft is not None and draft.shape[1] else None
+    sp = kb.token_bitmap(np.flatnonzero(sup), V) if sup is not None else None
+    sf = kb.token_bitmap(np.flatnonzero(first), V) if first is not None else None
+    am = torch.empty((B, R), dtype=torch.int32, device="cuda")
+    acc, nxt, _ = kb.verify_accept_masked(lt, dt, sp, sf, argmax_out=am)
+    return acc.cpu().numpy(), nxt.cpu().numpy(), am.cpu().numpy()
+
+
+def _masked_ref(logits, draft, sup, first, dtype="f32"):
+    x = logits if dtype == "f32" else O.widen(O.narrow(logits.astype(np.float64), dtype), dtype)
+    d = draft if draft is not None else np.zeros((logits.shape[0], 0), dtype=np.int32)
+    return O.verify_accept_masked(x, d, sup, first)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("R_extra", [0, 1])
+def test_verify_accept_masked_filters(dtype, R_extra):
+    """SuppressTokens (30% of the vocabulary, every row) and SuppressBlank
+    (blank and end-of-text, first row only) before the argmax, at the
+    whisper-large-v2 vocabulary, drafts agreeing with the filtered argmax
+    except where planted."""
+    say(f"case: verify masked {dtype} R=N+{R_extra}")
+    g = np.random.default_rng([25, R_extra, len(dtype)])
+    B, N, V, blank, eot = 3, 5, 51865, 220, 50256
+    R = N + R_extra
+    logits = (g.standard_normal((B, R, V)) * 2).astype(np.float32)
+    sup = g.random(V) < 0.3
+    sup[[blank, eot]] = False
+    first = np.zeros(V, dtype=bool)
+    first[[blank, eot]] = True
+    logits[:, :, blank] = 40.0                       # blank wins every row but the first
+    logits[0, 0, eot] = 41.0                         # end-of-text would win (0, 0)
+    top = np.flatnonzero(sup)[:3]
+    logits[1, :, top] = 50.0                         # suppressed tokens would win row 1
+    ram, _, _ = _masked_ref(logits, np.zeros((B, N), np.int32), sup, first, dtype)
+    draft = ram[:, :N].astype(np.int32).copy()
+    draft[2, 3] = top[0]                             # a draft the filter removed
+    acc, nxt, am = _masked_gpu(logits, draft, sup, first, dtype)
+    ram, racc, rnxt = _masked_ref(logits, draft, sup, first, dtype)
+    assert np.array_equal(am, ram) and np.array_equal(acc, racc) and np.array_equal(nxt, rnxt)
+    assert (am[:, 0] != blank).all() and (am[:, 1:] == blank).all() and acc[2] == 3
+
+
+@pytest.mark.parametrize("B,V", [(4, 51865), (2, 7), (1, 2049), (1, 1 << 20)])
+def test_verify_accept_masked_language_detection(B, V):
+    """No drafts, one row: the argmax over an allowed token set (every other
+    token suppressed), with ties among the allowed tokens and a suppressed
+    global maximum; one batch row has every token suppressed (gives 0)."""
+    say(f"case: masked argmax B={B} V={V}")
+    g = np.random.default_rng([26, B, V])
+    logits = (g.standard_normal((B, 1, V)) * 2).astype(np.float32)
+    lang = np.sort(g.choice(V, size=min(V, 99), replace=False))
+    sup = np.ones(V, dtype=bool)
+    sup[lang] = False
+    logits[0, 0, lang[:2]] = 60.0                    # tie: the lower token wins
+    big = np.flatnonzero(sup)
+    if big.size:
+        logits[-1, 0, big[0]] = 70.0                 # suppressed, must not win
+    acc, nxt, am = _masked_gpu(logits, None, sup, None)
+    ram, racc, rnxt = _masked_ref(logits, None, sup, None)
+    assert np.array_equal(am, ram) and np.array_equal(nxt, rnxt) and (acc == 0).all()
+    assert nxt[0] == lang[0]
+    acc, nxt, am = _masked_gpu(logits, None, np.ones(V, dtype=bool), None)
+    assert (nxt == 0).all() and (am == 0).all()
+
+
+def test_verify_accept_masked_without_bitmaps_equals_verify_accept():
+    say("case: masked verify with no bitmaps")
+    w = I.WHISPER_VERIFY
+    for t in range(20):
+        logits, draft = I.verify_logits(w, 1000 + t, plant=True)
+        a = _verify_gpu(logits, draft)
+        b = _masked_gpu(logits, draft, None, None)
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)
 
 
 # ------------------------------------------------------------------ beam ----
