@@ -219,6 +219,15 @@ def attend_self(q_store: np.ndarray, cache: ConcatCache, scale: float,
                   scale, causal_offset=L - N)
 
 
+def attend_self_ragged(q_store: np.ndarray, caches, scale: float,
+                       rope_base: float = 0.0) -> np.ndarray:
+    """A ragged batch ([S] over a batch of sequences): batch row b has its own
+    cache caches[b] (B = 1) with its own length, and its N queries sit at the
+    last N positions of its own sequence. Rows are independent."""
+    return np.concatenate([attend_self(q_store[b:b + 1], caches[b], scale, rope_base)
+                           for b in range(len(caches))], axis=0)
+
+
 def attend_cross(q_store: np.ndarray, cache: ConcatCache, scale: float) -> np.ndarray:
     """Cross attention: every query sees every encoder frame, no mask."""
     return attend(widen(q_store, cache.dtype), widen(cache.k, cache.dtype),

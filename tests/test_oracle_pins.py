@@ -252,6 +252,63 @@ def test_prefill_then_decode_with_rope_equals_recompute():
             assert np.max(np.abs(inc[b, h] - full)) < 1e-12
 
 
+def test_ragged_batch_rows_equal_full_recompute_with_rollback():
+    """A ragged batch of speculative steps: each row appends N = 4 drafts at
+    its own length, keeps its own accepted count (the rest rolled back), and
+    the next step appends again from there. Every query's output equals full
+    causal recomputation over that row's kept sequence alone."""
+    g = np.random.default_rng(18)
+    B, H, D, N = 3, 2, 64, 4
+    dt = "f32"
+    lens0 = [3, 9, 1]
+    seqK = [O.narrow(g.standard_normal((H, lens0[b], D)), dt) for b in range(B)]
+    seqV = [O.narrow(g.standard_normal((H, lens0[b], D)), dt) for b in range(B)]
+    caches = []
+    for b in range(B):
+        c = O.ConcatCache(1, H, D, dt)
+        c.append(seqK[b][None], seqV[b][None])
+        caches.append(c)
+    for step in range(4):
+        q = O.narrow(g.standard_normal((B, H, N, D)), dt)
+        kn = O.narrow(g.standard_normal((B, H, N, D)), dt)
+        vn = O.narrow(g.standard_normal((B, H, N, D)), dt)
+        for b in range(B):
+            caches[b].append(kn[b:b + 1], vn[b:b + 1])
+        out = O.attend_self_ragged(q, caches, 0.125)
+        for b in range(B):
+            K = O.widen(np.concatenate([seqK[b], kn[b]], axis=1), dt)
+            V = O.widen(np.concatenate([seqV[b], vn[b]], axis=1), dt)
+            L = K.shape[1]
+            Q = np.zeros((H, L, D))
+            Q[:, L - N:] = O.widen(q[b], dt)
+            full = O.full_causal_attention(Q, K, V, 0.125)[:, L - N:]
+            assert np.max(np.abs(out[b] - full)) < 1e-12
+        for b in range(B):   # each row keeps its own accepted prefix of the drafts
+            keep = int(g.integers(0, N + 1))
+            seqK[b] = np.concatenate([seqK[b], kn[b][:, :keep]], axis=1)
+            seqV[b] = np.concatenate([seqV[b], vn[b][:, :keep]], axis=1)
+            caches[b].truncate(seqK[b].shape[1])
+
+
+def test_ragged_batch_with_equal_lengths_is_the_batched_call():
+    g = np.random.default_rng(19)
+    B, Hq, Hk, D, L, N = 3, 6, 2, 64, 11, 3
+    dt = "bf16"
+    K = O.narrow(g.standard_normal((B, Hk, L, D)), dt)
+    V = O.narrow(g.standard_normal((B, Hk, L, D)), dt)
+    q = O.narrow(g.standard_normal((B, Hq, N, D)), dt)
+    batched = O.ConcatCache(B, Hk, D, dt)
+    batched.append(K, V, rope_base=1e4)
+    rows = []
+    for b in range(B):
+        c = O.ConcatCache(1, Hk, D, dt)
+        c.append(K[b:b + 1], V[b:b + 1], rope_base=1e4)
+        rows.append(c)
+    a = O.attend_self(q, batched, 0.125, rope_base=1e4)
+    r = O.attend_self_ragged(q, rows, 0.125, rope_base=1e4)
+    assert np.array_equal(a, r)
+
+
 # --------------------------------------------------------------- reorder ----
 
 def test_reorder_brute_force_and_composition():
