@@ -140,6 +140,47 @@ int decode_step_self(const void *q, const void *k_new, const void *v_new, int32_
                      const kvd_cache *cache, int32_t len, float scale, float rope_base,
                      float *out, void *ws, size_t ws_bytes, void *stream);
 
+/* Ragged batches ([S] applied to a batch of sequences: each batch row
+ * accepts its own number of drafts, so its cache length moves on its own).
+ * The calls below take per-row positions or lengths in a device array, so a
+ * decode loop never reads them back to the host; a rolled-back row simply
+ * gets a shorter length (rows past it are overwritten later).
+ *
+ * kv_append_ragged - kv_append with row b written at [pos[b], pos[b] + T).
+ *   pos: device int32 [cache->B]. A row whose pos[b] < 0 or
+ *     pos[b] + T > S_max is not written and KVD_ERR_CAPACITY is stored in
+ *     dev_status (device int32, or NULL); other rows are written.
+ *   Other arguments and errors as kv_append. */
+int kv_append_ragged(const kvd_cache *cache, const void *k_new, const void *v_new,
+                     const int32_t *pos, int32_t T, float rope_base, int32_t *dev_status,
+                     void *stream);
+
+/* decode_attn_self_ragged - decode_attn_self with row b's length lens[b]:
+ * its query i sits at position lens[b] - N + i and sees keys
+ * 0 .. lens[b] - N + i.
+ *   lens: device int32 [cache->B]; len_max: a host bound, N <= len_max <=
+ *     S_max, that the split plan and the workspace are sized for
+ *     (kvd_attn_workspace_bytes(B, Hq, N, len_max)). A lens[b] outside
+ *     [N, len_max] is clamped into it and KVD_ERR_CAPACITY is stored in
+ *     dev_status (device int32, or NULL).
+ *   Other arguments, results and errors as decode_attn_self with
+ *   len = len_max. */
+int decode_attn_self_ragged(const void *q, int32_t Hq, int32_t N, const kvd_cache *cache,
+                            const int32_t *lens, int32_t len_max, float scale, float rope_base,
+                            float *out, void *ws, size_t ws_bytes, int32_t *dev_status,
+                            void *stream);
+
+/* decode_step_self_ragged - decode_step_self with per-row lengths, in one
+ * launch (N <= 16): row b's N new K/V rows are written at
+ * [lens[b] - N, lens[b]) and its queries attend as in
+ * decode_attn_self_ragged. After the call the cache holds exactly what
+ * kv_append_ragged at positions lens[b] - N would have written.
+ * Errors as decode_attn_self_ragged, and KVD_ERR_SHAPE for N > 16. */
+int decode_step_self_ragged(const void *q, const void *k_new, const void *v_new, int32_t Hq,
+                            int32_t N, const kvd_cache *cache, const int32_t *lens,
+                            int32_t len_max, float scale, float rope_base, float *out, void *ws,
+                            size_t ws_bytes, int32_t *dev_status, void *stream);
+
 /* decode_attn_cross - attention of N queries per row over all `frames`
  * rows of a cross-attention cache, with no mask ([W]: cross-attention K/V
  * computed once from the encoder and reused every step).

@@ -43,6 +43,15 @@ _SIGNATURES = {
     "kv_append": (c_int, [ctypes.POINTER(KvdCache), c_void_p, c_void_p, c_int32, c_int32,
                           c_float, c_void_p]),
     "kv_reorder": (c_int, [ctypes.POINTER(KvdCache), c_void_p, c_int32, c_void_p, c_void_p]),
+    "kv_append_ragged": (c_int, [ctypes.POINTER(KvdCache), c_void_p, c_void_p, c_void_p, c_int32,
+                                 c_float, c_void_p, c_void_p]),
+    "decode_attn_self_ragged": (c_int, [c_void_p, c_int32, c_int32, ctypes.POINTER(KvdCache),
+                                        c_void_p, c_int32, c_float, c_float, c_void_p, c_void_p,
+                                        c_size_t, c_void_p, c_void_p]),
+    "decode_step_self_ragged": (c_int, [c_void_p, c_void_p, c_void_p, c_int32, c_int32,
+                                        ctypes.POINTER(KvdCache), c_void_p, c_int32, c_float,
+                                        c_float, c_void_p, c_void_p, c_size_t, c_void_p,
+                                        c_void_p]),
     "decode_attn_self": (c_int, [c_void_p, c_int32, c_int32, ctypes.POINTER(KvdCache), c_int32,
                                  c_float, c_float, c_void_p, c_void_p, c_size_t, c_void_p]),
     "decode_step_self": (c_int, [c_void_p, c_void_p, c_void_p, c_int32, c_int32,
@@ -255,6 +264,73 @@ def decode_step_self(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, 
         _dev(v_new, "v_new", cache.dtype), Hq, N, ctypes.byref(d), length, scale, rope_base,
         _dev(out, "out", torch.float32), _dev(ws, "ws"), ws.numel() * ws.element_size(),
         _stream()))
+    return out
+
+
+def _rows(t: torch.Tensor, B: int, name: str):
+    if t.numel() != B:
+        raise ValueError(f"{name} must hold one int32 per batch row ({B})")
+    return _dev(t, name, torch.int32)
+
+
+def kv_append_ragged(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor, pos: torch.Tensor,
+                     rope_base: float = 0.0, dev_status: torch.Tensor | None = None):
+    """kv_append with batch row b written at [pos[b], pos[b] + T) (pos: device
+    int32 [B])."""
+    d = cache.desc()
+    if k_new.dim() != 4 or k_new.shape != v_new.shape:
+        raise ValueError("k_new and v_new must be [B, H, T, D] of one shape")
+    if (k_new.shape[0], k_new.shape[1], k_new.shape[3]) != (d.B, d.H, d.D):
+        raise ValueError(f"k_new shape {tuple(k_new.shape)} does not match the cache")
+    st = _dev(dev_status, "dev_status", torch.int32) if dev_status is not None else None
+    _check("kv_append_ragged", lib().kv_append_ragged(
+        ctypes.byref(d), _dev(k_new, "k_new", cache.dtype), _dev(v_new, "v_new", cache.dtype),
+        _rows(pos, d.B, "pos"), k_new.shape[2], rope_base, st, _stream()))
+
+
+def decode_attn_self_ragged(q: torch.Tensor, cache: Cache, lens: torch.Tensor, len_max: int,
+                            scale: float, rope_base: float = 0.0, out: torch.Tensor | None = None,
+                            ws: torch.Tensor | None = None,
+                            dev_status: torch.Tensor | None = None) -> torch.Tensor:
+    """decode_attn_self with per-row lengths (lens: device int32 [B], each in
+    [N, len_max])."""
+    d = cache.desc()
+    if q.dim() != 4 or q.shape[0] != d.B or q.shape[3] != d.D:
+        raise ValueError(f"q must be [B={d.B}, Hq, N, {d.D}], got {tuple(q.shape)}")
+    Hq, N = q.shape[1], q.shape[2]
+    out = _attn_out(q, out)
+    if ws is None:
+        ws = workspace(attn_workspace_bytes(d.B, Hq, N, len_max), q.device)
+    st = _dev(dev_status, "dev_status", torch.int32) if dev_status is not None else None
+    _check("decode_attn_self_ragged", lib().decode_attn_self_ragged(
+        _dev(q, "q", cache.dtype), Hq, N, ctypes.byref(d), _rows(lens, d.B, "lens"), len_max,
+        scale, rope_base, _dev(out, "out", torch.float32), _dev(ws, "ws"),
+        ws.numel() * ws.element_size(), st, _stream()))
+    return out
+
+
+def decode_step_self_ragged(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                            cache: Cache, lens: torch.Tensor, len_max: int, scale: float,
+                            rope_base: float = 0.0, out: torch.Tensor | None = None,
+                            ws: torch.Tensor | None = None,
+                            dev_status: torch.Tensor | None = None) -> torch.Tensor:
+    """kv_append_ragged of the N new rows at [lens[b] - N, lens[b]) plus
+    decode_attn_self_ragged, one launch (N <= 16)."""
+    d = cache.desc()
+    if q.dim() != 4 or q.shape[0] != d.B or q.shape[3] != d.D:
+        raise ValueError(f"q must be [B={d.B}, Hq, N, {d.D}], got {tuple(q.shape)}")
+    Hq, N = q.shape[1], q.shape[2]
+    if tuple(k_new.shape) != (d.B, d.H, N, d.D) or k_new.shape != v_new.shape:
+        raise ValueError(f"k_new/v_new must be [{d.B}, {d.H}, {N}, {d.D}]")
+    out = _attn_out(q, out)
+    if ws is None:
+        ws = workspace(attn_workspace_bytes(d.B, Hq, N, len_max), q.device)
+    st = _dev(dev_status, "dev_status", torch.int32) if dev_status is not None else None
+    _check("decode_step_self_ragged", lib().decode_step_self_ragged(
+        _dev(q, "q", cache.dtype), _dev(k_new, "k_new", cache.dtype),
+        _dev(v_new, "v_new", cache.dtype), Hq, N, ctypes.byref(d), _rows(lens, d.B, "lens"),
+        len_max, scale, rope_base, _dev(out, "out", torch.float32), _dev(ws, "ws"),
+        ws.numel() * ws.element_size(), st, _stream()))
     return out
 
 

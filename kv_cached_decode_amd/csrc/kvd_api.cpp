@@ -117,15 +117,26 @@ const char *kvd_status_string(int status) {
   }
 }
 
-int kv_append(const kvd_cache *cache, const void *k_new, const void *v_new, int32_t pos,
-              int32_t T, float rope_base, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by kv_append and kv_append_ragged (pos_rows non-null: per-row
+// positions on the device, checked there).
+int append_impl(const kvd_cache *cache, const void *k_new, const void *v_new, int32_t pos,
+                const int32_t *pos_rows, int32_t *dev_status, int32_t T, float rope_base,
+                void *stream) {
   int st = check_cache(cache);
   if (st) return st;
   if (!k_new || !v_new) return KVD_ERR_NULL;
   if (T < 1 || pos < 0 || !(rope_base >= 0.f) || isinf(rope_base)) return KVD_ERR_SHAPE;
   if ((int64_t)pos + T > cache->S_max) return KVD_ERR_CAPACITY;
   if (!aligned16(k_new) || !aligned16(v_new)) return KVD_ERR_ALIGN;
-  kvd::AppendArgs a;
+  if ((pos_rows && !aligned4(pos_rows)) || (dev_status && !aligned4(dev_status)))
+    return KVD_ERR_ALIGN;
+  kvd::AppendArgs a{};
+  a.pos_rows = pos_rows;
+  a.dev_status = dev_status;
   a.k_cache = cache->k;
   a.v_cache = cache->v;
   a.k_new = k_new;
@@ -141,6 +152,22 @@ int kv_append(const kvd_cache *cache, const void *k_new, const void *v_new, int3
   return status_of(kvd::launch_append(cache->dtype, a, static_cast<hipStream_t>(stream)));
 }
 
+}  // namespace
+
+extern "C" {
+
+int kv_append(const kvd_cache *cache, const void *k_new, const void *v_new, int32_t pos,
+              int32_t T, float rope_base, void *stream) {
+  return append_impl(cache, k_new, v_new, pos, nullptr, nullptr, T, rope_base, stream);
+}
+
+int kv_append_ragged(const kvd_cache *cache, const void *k_new, const void *v_new,
+                     const int32_t *pos, int32_t T, float rope_base, int32_t *dev_status,
+                     void *stream) {
+  if (!pos) return KVD_ERR_NULL;
+  return append_impl(cache, k_new, v_new, 0, pos, dev_status, T, rope_base, stream);
+}
+
 int kv_reorder(const kvd_cache *cache, const int32_t *parent, int32_t len, int32_t *dev_status,
                void *stream) {
   int st = check_cache(cache);
@@ -149,7 +176,7 @@ int kv_reorder(const kvd_cache *cache, const int32_t *parent, int32_t len, int32
   if (len < 0 || cache->B > 16) return KVD_ERR_SHAPE;
   if (len > cache->S_max) return KVD_ERR_CAPACITY;
   if (!aligned4(parent) || (dev_status && !aligned4(dev_status))) return KVD_ERR_ALIGN;
-  kvd::ReorderArgs a;
+  kvd::ReorderArgs a{};
   a.k_cache = cache->k;
   a.v_cache = cache->v;
   a.parent = parent;
@@ -165,9 +192,12 @@ namespace {
 
 // Shared by decode_attn_self and decode_step_self: validate and plan (no HIP
 // call). k_new/v_new non-null: the N new rows are appended in the same launch.
+// lens non-null: per-row lengths on the device (a ragged batch), with len
+// their planned maximum.
 int prepare_self(AttnArgs &a, const void *q, const void *k_new, const void *v_new, int32_t Hq,
                  int32_t N, const kvd_cache *cache, int32_t len, float scale, float rope_base,
-                 float *out, void *ws, size_t ws_bytes) {
+                 float *out, void *ws, size_t ws_bytes, const int32_t *lens = nullptr,
+                 int32_t *dev_status = nullptr) {
   int st = check_cache(cache);
   if (st) return st;
   if (!q || !out) return KVD_ERR_NULL;
@@ -177,7 +207,10 @@ int prepare_self(AttnArgs &a, const void *q, const void *k_new, const void *v_ne
   if (len > cache->S_max || len < N) return KVD_ERR_CAPACITY;
   if (!aligned16(q) || !aligned16(out)) return KVD_ERR_ALIGN;
   if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return KVD_ERR_ALIGN;
+  if ((lens && !aligned4(lens)) || (dev_status && !aligned4(dev_status))) return KVD_ERR_ALIGN;
   a = AttnArgs{};
+  a.lens = lens;
+  a.dev_status = dev_status;
   a.q = q;
   a.k = cache->k;
   a.v = cache->v;
@@ -208,7 +241,7 @@ int prepare_self(AttnArgs &a, const void *q, const void *k_new, const void *v_ne
 int decode_attn_self(const void *q, int32_t Hq, int32_t N, const kvd_cache *cache, int32_t len,
                      float scale, float rope_base, float *out, void *ws, size_t ws_bytes,
                      void *stream) {
-  AttnArgs a;
+  AttnArgs a{};
   const int st = prepare_self(a, q, nullptr, nullptr, Hq, N, cache, len, scale, rope_base, out,
                               ws, ws_bytes);
   if (st) return st;
@@ -220,7 +253,7 @@ int decode_step_self(const void *q, const void *k_new, const void *v_new, int32_
                      float *out, void *ws, size_t ws_bytes, void *stream) {
   if (!k_new || !v_new) return KVD_ERR_NULL;
   const bool fused = N <= kvd::kMaxFusedRows;
-  AttnArgs a;
+  AttnArgs a{};
   const int st = prepare_self(a, q, fused ? k_new : nullptr, fused ? v_new : nullptr, Hq, N, cache,
                               len, scale, rope_base, out, ws, ws_bytes);
   if (st) return st;
@@ -228,7 +261,7 @@ int decode_step_self(const void *q, const void *k_new, const void *v_new, int32_
   if (!fused) {
     // a long block of new rows (prefill): append first, then attend
     if (!aligned16(k_new) || !aligned16(v_new)) return KVD_ERR_ALIGN;
-    kvd::AppendArgs ap;
+    kvd::AppendArgs ap{};
     ap.k_cache = cache->k;
     ap.v_cache = cache->v;
     ap.k_new = k_new;
@@ -245,6 +278,31 @@ int decode_step_self(const void *q, const void *k_new, const void *v_new, int32_
     if (sa) return sa;
   }
   return status_of(kvd::launch_attn(cache->dtype, a, s));
+}
+
+int decode_attn_self_ragged(const void *q, int32_t Hq, int32_t N, const kvd_cache *cache,
+                            const int32_t *lens, int32_t len_max, float scale, float rope_base,
+                            float *out, void *ws, size_t ws_bytes, int32_t *dev_status,
+                            void *stream) {
+  if (!lens) return KVD_ERR_NULL;
+  AttnArgs a{};
+  const int st = prepare_self(a, q, nullptr, nullptr, Hq, N, cache, len_max, scale, rope_base,
+                              out, ws, ws_bytes, lens, dev_status);
+  if (st) return st;
+  return status_of(kvd::launch_attn(cache->dtype, a, static_cast<hipStream_t>(stream)));
+}
+
+int decode_step_self_ragged(const void *q, const void *k_new, const void *v_new, int32_t Hq,
+                            int32_t N, const kvd_cache *cache, const int32_t *lens,
+                            int32_t len_max, float scale, float rope_base, float *out, void *ws,
+                            size_t ws_bytes, int32_t *dev_status, void *stream) {
+  if (!k_new || !v_new || !lens) return KVD_ERR_NULL;
+  if (N > kvd::kMaxFusedRows) return KVD_ERR_SHAPE;
+  AttnArgs a{};
+  const int st = prepare_self(a, q, k_new, v_new, Hq, N, cache, len_max, scale, rope_base, out,
+                              ws, ws_bytes, lens, dev_status);
+  if (st) return st;
+  return status_of(kvd::launch_attn(cache->dtype, a, static_cast<hipStream_t>(stream)));
 }
 
 int decode_attn_cross(const void *q, int32_t B, int32_t Hq, int32_t N, const kvd_cache *xcache,
@@ -333,7 +391,7 @@ int verify_impl(const void *logits, int32_t logits_dtype, int32_t B, int32_t R, 
   const size_t need = kvd_verify_workspace_bytes(B, R, V);
   if (!ws || ws_bytes < need) return KVD_ERR_WORKSPACE;
   if (!aligned16(ws)) return KVD_ERR_ALIGN;
-  kvd::VerifyArgs a;
+  kvd::VerifyArgs a{};
   a.logits = logits;
   a.dtype = logits_dtype;
   a.draft = draft;
@@ -398,7 +456,7 @@ int beam_select(const void *logits, int32_t logits_dtype, int32_t B, int32_t K, 
     return KVD_ERR_ALIGN;
   if (!ws || ws_bytes < kvd_beam_workspace_bytes(B, K, V)) return KVD_ERR_WORKSPACE;
   if (!aligned16(ws)) return KVD_ERR_ALIGN;
-  kvd::BeamArgs a;
+  kvd::BeamArgs a{};
   a.logits = logits;
   a.dtype = logits_dtype;
   a.sum_logprobs = sum_logprobs;

@@ -38,7 +38,7 @@ struct AttnGeom {
   static constexpr int ROWB = kHeadDim * Storage<DT>::bytes;
 };
 
-template <int DT, int GM, bool FUSED, int NWMAX, bool ROPE>
+template <int DT, int GM, bool FUSED, int NWMAX, bool ROPE, bool RAGGED>
 __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
   using Geo = AttnGeom<DT>;
   constexpr int D = kHeadDim;
@@ -58,12 +58,13 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
   const int g0 = rt * GM;
   const int gcount = min(GM, a.G - g0);
   const int k0 = split * a.chunk;
-  const int kspan = min(k0 + a.chunk, a.L);
+  const RowSpan sp = row_span<RAGGED>(a, bkv);
+  const int kspan = min(k0 + a.chunk, sp.L);
 
   const size_t head = (size_t)bkv * a.Hkv + hk;
   char *kc = static_cast<char *>(a.k) + head * a.S_max * ROWB;
   char *vc = static_cast<char *>(a.v) + head * a.S_max * ROWB;
-  const int nb0 = max(k0, a.new_base);  // first new row of this key range
+  const int nb0 = max(k0, sp.new_base);  // first new row of this key range
 
   // ---- which keys each query row sees (indices only, no memory access)
   int lim[GM];
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
     lim[g] = 0;
     if (g < gcount) {
       const RowId r = row_id(a, bkv, hk, g0 + g);
-      lim[g] = (a.causal_base < 0) ? a.L : a.causal_base + r.i + 1;
+      lim[g] = (sp.causal_base < 0) ? sp.L : sp.causal_base + r.i + 1;
       kvis = max(kvis, lim[g]);
     }
   }
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
   float rc[ROPE ? VE : 1], rs[ROPE ? VE : 1];  // cos / sin at position rpos
   int rpos = -1;
   if constexpr (ROPE) {
-    rpos = a.causal_base + row_id(a, bkv, hk, g0).i;
+    rpos = sp.causal_base + row_id(a, bkv, hk, g0).i;
     rope_slice_cs<DT>(ds, rpos, RopeStep{a.rope_step, a.rope_ratio}, rc, rs);
   }
 
@@ -154,7 +155,7 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
     for (int t = threadIdx.x; t < n; t += blockDim.x) {
       const int r = t / HALF_VECS, j = t % HALF_VECS;
       const int pos = nb0 + r;
-      const size_t src = (size_t)(pos - a.new_base) * ROWB;
+      const size_t src = (size_t)(pos - sp.new_base) * ROWB;
       const PairChunks c = load_pair<DT>(kn + src, vn + src, j, pos, RopeStep{ROPE ? a.rope_step : 0.0, a.rope_ratio});
       s_new[r * VPR + j] = c.klo;
       s_new[r * VPR + j + VPR / 2] = c.khi;
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
     if (g < gcount) {
       if constexpr (ROPE) {
         const RowId r = row_id(a, bkv, hk, g0 + g);
-        const int pos = a.causal_base + r.i;
+        const int pos = sp.causal_base + r.i;
         if (pos != rpos) {  // rows of one position share their cos / sin
           rope_slice_cs<DT>(ds, pos, RopeStep{a.rope_step, a.rope_ratio}, rc, rs);
           rpos = pos;
@@ -392,28 +393,34 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
   merge_splits<GM>(a, tile_id, g0, gcount, bkv, hk);
 }
 
-template <int DT, bool FUSED, bool ROPE>
+template <int DT, bool FUSED, bool ROPE, bool RAGGED>
 void launch_gm(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
   switch (a.gm) {
-    case 1: launch_kernel(attn_kernel<DT, 1, FUSED, 4, ROPE>, grid, block, s, a); break;
-    case 2: launch_kernel(attn_kernel<DT, 2, FUSED, 4, ROPE>, grid, block, s, a); break;
-    case 4: launch_kernel(attn_kernel<DT, 4, FUSED, 4, ROPE>, grid, block, s, a); break;
-    default: launch_kernel(attn_kernel<DT, 8, FUSED, 4, ROPE>, grid, block, s, a); break;
+    case 1: launch_kernel(attn_kernel<DT, 1, FUSED, 4, ROPE, RAGGED>, grid, block, s, a); break;
+    case 2: launch_kernel(attn_kernel<DT, 2, FUSED, 4, ROPE, RAGGED>, grid, block, s, a); break;
+    case 4: launch_kernel(attn_kernel<DT, 4, FUSED, 4, ROPE, RAGGED>, grid, block, s, a); break;
+    default: launch_kernel(attn_kernel<DT, 8, FUSED, 4, ROPE, RAGGED>, grid, block, s, a); break;
   }
 }
 
 // The 16-wave variant (one wide workgroup per unit): one query row and no
 // rotary work, so that it fits 128 registers without spilling.
-template <int DT, bool FUSED>
+template <int DT, bool FUSED, bool RAGGED>
 void launch_wide(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
-  launch_kernel(attn_kernel<DT, 1, FUSED, kMaxWaves, false>, grid, block, s, a);
+  launch_kernel(attn_kernel<DT, 1, FUSED, kMaxWaves, false, RAGGED>, grid, block, s, a);
+}
+
+template <int DT, bool FUSED, bool RAGGED>
+void launch_rg(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
+  if (a.waves > 4) launch_wide<DT, FUSED, RAGGED>(a, grid, block, s);
+  else if (a.rope_base > 0.f) launch_gm<DT, FUSED, true, RAGGED>(a, grid, block, s);
+  else launch_gm<DT, FUSED, false, RAGGED>(a, grid, block, s);
 }
 
 template <int DT, bool FUSED>
 void launch_dt(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
-  if (a.waves > 4) launch_wide<DT, FUSED>(a, grid, block, s);
-  else if (a.rope_base > 0.f) launch_gm<DT, FUSED, true>(a, grid, block, s);
-  else launch_gm<DT, FUSED, false>(a, grid, block, s);
+  if (a.lens) launch_rg<DT, FUSED, true>(a, grid, block, s);
+  else launch_rg<DT, FUSED, false>(a, grid, block, s);
 }
 
 int env_int(const char *name, int dflt) {

@@ -31,6 +31,29 @@ __device__ __forceinline__ size_t out_row(const AttnArgs &a, const RowId &r) {
   return ((size_t)(r.b * a.Hq + r.h) * a.N + r.i) * kHeadDim;
 }
 
+// The key range of unit row bkv: the call's L, causal base and new-row base,
+// or, with per-row lengths (RAGGED: a ragged batch), that row's len clamped
+// into [N, L] (L is the planned maximum; a clamped len is flagged in
+// dev_status, so no access ever leaves the planned range). RAGGED is a
+// template flag so that kernels without per-row lengths carry no trace of
+// them.
+struct RowSpan {
+  int L, causal_base, new_base;
+};
+template <bool RAGGED>
+__device__ __forceinline__ RowSpan row_span(const AttnArgs &a, int bkv) {
+  RowSpan s{a.L, a.causal_base, a.new_base};
+  if constexpr (RAGGED) {
+    const int len = a.lens[bkv];
+    const int c = min(max(len, a.N), a.L);
+    if (c != len && a.dev_status && threadIdx.x == 0) *a.dev_status = -4;  // KVD_ERR_CAPACITY
+    s.L = c;
+    s.causal_base = c - a.N;
+    if (a.new_base != INT_MAX) s.new_base = c - a.T_new;
+  }
+  return s;
+}
+
 // Every kernel argument the first loads depend on, fetched in one go: the
 // empty asm keeps the compiler from sinking a fetch into a later branch,
 // which would add a serial round trip before the first key load.

@@ -69,7 +69,7 @@ __device__ __forceinline__ uint32_t elem16(u32x2 c, int t) {
   return (t & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
-template <int DT, int RW, bool FUSED, bool ROPE>
+template <int DT, int RW, bool FUSED, bool ROPE, bool RAGGED>
 __global__ __launch_bounds__(64 * kWaves) void attn_mfma_kernel(AttnArgs a) {
   constexpr int D = kHeadDim;
   constexpr int ROWB = kHeadDim * 2;
@@ -85,18 +85,19 @@ __global__ __launch_bounds__(64 * kWaves) void attn_mfma_kernel(AttnArgs a) {
   const int phase = wave / RW;
   const int bkv = unit / a.Hkv, hk = unit % a.Hkv;
   const int k0 = split * a.chunk;
-  const int kspan = min(k0 + a.chunk, a.L);
+  const RowSpan sp = row_span<RAGGED>(a, bkv);
+  const int kspan = min(k0 + a.chunk, sp.L);
   const size_t head = (size_t)bkv * a.Hkv + hk;
   char *kc = static_cast<char *>(a.k) + head * a.S_max * ROWB;
   char *vc = static_cast<char *>(a.v) + head * a.S_max * ROWB;
-  const int nb0 = max(k0, a.new_base);
+  const int nb0 = max(k0, sp.new_base);
 
   // ---- this lane's query row and the keys it sees
   const int grow = rt * kRows + c;
   const bool active = grow < a.G;
   RowId r{0, 0, 0};
   if (active) r = row_id(a, bkv, hk, grow);
-  const int lim = active ? ((a.causal_base < 0) ? a.L : a.causal_base + r.i + 1) : 0;
+  const int lim = active ? ((sp.causal_base < 0) ? sp.L : sp.causal_base + r.i + 1) : 0;
   const int kend = min(kspan, (int)groups_max<1>((float)lim));  // wave-uniform
 
   // ---- query operand: dims [8gq, +8) and [32 + 8gq, +8) of the row; a rotary
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_mfma_kernel(AttnArgs a) {
   // they are computed while the loads above are in flight
   float qc[ROPE ? 8 : 1], qs[ROPE ? 8 : 1];
   if constexpr (ROPE)
-    rope_cos_sin_run<8>(a.causal_base + r.i, gq * 8, RopeStep{a.rope_step, a.rope_ratio}, qc, qs);
+    rope_cos_sin_run<8>(sp.causal_base + r.i, gq * 8, RopeStep{a.rope_step, a.rope_ratio}, qc, qs);
 
   // ---- fused append (as in the streaming kernel)
   __shared__ u32x4 s_new[FUSED ? 2 * kMaxFusedRows * VPR : 1];
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_mfma_kernel(AttnArgs a) {
     for (int t = threadIdx.x; t < n; t += blockDim.x) {
       const int rr = t / HALF_VECS, j = t % HALF_VECS;
       const int pos = nb0 + rr;
-      const size_t src = (size_t)(pos - a.new_base) * ROWB;
+      const size_t src = (size_t)(pos - sp.new_base) * ROWB;
       const PairChunks ch = load_pair<DT>(kn + src, vn + src, j, pos, RopeStep{ROPE ? a.rope_step : 0.0, a.rope_ratio});
       s_new[rr * VPR + j] = ch.klo;
       s_new[rr * VPR + j + VPR / 2] = ch.khi;
@@ -303,16 +304,22 @@ __global__ __launch_bounds__(64 * kWaves) void attn_mfma_kernel(AttnArgs a) {
   }
 }
 
-template <int DT, int RW>
-void launch_rw(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
+template <int DT, int RW, bool RAGGED>
+void launch_rwr(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
   const bool fused = a.k_new != nullptr, rope = a.rope_base > 0.f;
   if (fused) {
-    if (rope) launch_kernel(attn_mfma_kernel<DT, RW, true, true>, grid, block, s, a);
-    else launch_kernel(attn_mfma_kernel<DT, RW, true, false>, grid, block, s, a);
+    if (rope) launch_kernel(attn_mfma_kernel<DT, RW, true, true, RAGGED>, grid, block, s, a);
+    else launch_kernel(attn_mfma_kernel<DT, RW, true, false, RAGGED>, grid, block, s, a);
   } else {
-    if (rope) launch_kernel(attn_mfma_kernel<DT, RW, false, true>, grid, block, s, a);
-    else launch_kernel(attn_mfma_kernel<DT, RW, false, false>, grid, block, s, a);
+    if (rope) launch_kernel(attn_mfma_kernel<DT, RW, false, true, RAGGED>, grid, block, s, a);
+    else launch_kernel(attn_mfma_kernel<DT, RW, false, false, RAGGED>, grid, block, s, a);
   }
+}
+
+template <int DT, int RW>
+void launch_rw(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
+  if (a.lens) launch_rwr<DT, RW, true>(a, grid, block, s);
+  else launch_rwr<DT, RW, false>(a, grid, block, s);
 }
 
 }  // namespace

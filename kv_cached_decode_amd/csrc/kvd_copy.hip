@@ -9,6 +9,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kStatusBadShape = -2;  // KVD_ERR_SHAPE
+constexpr int kStatusCapacity = -4;  // KVD_ERR_CAPACITY
 constexpr int kMaxBeams = 16;
 
 // Thread (row, j) moves rotary pair j of one new row; rows are ordered
@@ -24,10 +25,18 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
   const long row = tid / HALF_VECS;
   const int t = (int)(row % a.T);
   const long bh = row / a.T;
+  int pos = a.pos;
+  if (a.pos_rows) {  // ragged batch: row b writes at its own position
+    pos = a.pos_rows[bh / a.H];
+    if (pos < 0 || pos > a.S_max - a.T) {  // outside the cache: skipped, never written
+      if (a.dev_status && t == 0 && j == 0) *a.dev_status = kStatusCapacity;
+      return;
+    }
+  }
   const size_t src = (size_t)row * ROWB;
-  const size_t dst = ((size_t)bh * a.S_max + a.pos + t) * ROWB;
+  const size_t dst = ((size_t)bh * a.S_max + pos + t) * ROWB;
   const PairChunks c = load_pair<DT>(static_cast<const char *>(a.k_new) + src,
-                                     static_cast<const char *>(a.v_new) + src, j, a.pos + t,
+                                     static_cast<const char *>(a.v_new) + src, j, pos + t,
                                      RopeStep{a.rope_step, a.rope_ratio});
   store_pair<DT>(static_cast<char *>(a.k_cache) + dst, static_cast<char *>(a.v_cache) + dst, j, c);
 }

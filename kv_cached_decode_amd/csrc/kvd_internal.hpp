@@ -26,6 +26,8 @@ struct AppendArgs {
   void *k_cache, *v_cache;       // [B][H][S_max][D]
   const void *k_new, *v_new;     // [B][H][T][D]
   int B, H, S_max, T, pos;
+  const int32_t *pos_rows;       // [B] per-row positions (ragged batch), or null: pos for all
+  int32_t *dev_status;           // a row outside the cache is skipped and flagged here, or null
   float rope_base;               // > 0: rotate keys at pos + t
   double rope_step;              // 2 log2(rope_base) / D (0: no rotation)
   double rope_ratio;             // 2^(-rope_step)
@@ -54,6 +56,9 @@ struct AttnArgs {
   int L;                         // keys: len (self) or frames (cross)
   int causal_base;               // self: len - N; cross: -1 (no mask)
   int new_base, T_new;           // new rows sit at [new_base, new_base + T_new); INT_MAX: none
+  const int32_t *lens;           // [Bkv] per-row len (ragged self attention; L is then the
+                                 // planned maximum), or null
+  int32_t *dev_status;           // a len outside [N, L] is clamped and flagged here, or null
   float scale_log2;              // scale * log2(e)
   float rope_base;               // > 0: rotate q at causal_base + i (and new keys)
   double rope_step;              // 2 log2(rope_base) / D (0: no rotation)

@@ -58,6 +58,29 @@ def test_kv_append_validation(lib):
     assert f(ctypes.byref(_cache(k=MIS)), FAKE, FAKE, 0, 1, 0.0, None) == -7
 
 
+def test_ragged_validation(lib):
+    c = ctypes.byref(_cache(B=4))
+    big = 1 << 30
+    a = lib.kv_append_ragged
+    assert a(c, FAKE, FAKE, None, 5, 0.0, None, None) == -1
+    assert a(c, FAKE, FAKE, FAKE, 0, 0.0, None, None) == -2              # T < 1
+    assert a(c, FAKE, FAKE, FAKE, 449, 0.0, None, None) == -4            # T > S_max
+    assert a(c, FAKE, FAKE, FAKE + 2, 5, 0.0, None, None) == -7          # pos misaligned
+    assert a(c, FAKE, FAKE, FAKE, 5, 0.0, FAKE + 1, None) == -7          # dev_status misaligned
+    s = lib.decode_attn_self_ragged
+    assert s(FAKE, 20, 5, c, None, 448, 0.125, 0.0, FAKE, FAKE, big, None, None) == -1
+    assert s(FAKE, 20, 5, c, FAKE, 449, 0.125, 0.0, FAKE, FAKE, big, None, None) == -4
+    assert s(FAKE, 20, 5, c, FAKE, 4, 0.125, 0.0, FAKE, FAKE, big, None, None) == -4
+    assert s(FAKE, 20, 5, c, FAKE + 2, 448, 0.125, 0.0, FAKE, FAKE, big, None, None) == -7
+    assert s(FAKE, 20, 5, c, FAKE, 448, 0.125, 0.0, FAKE, FAKE, big, FAKE + 2, None) == -7
+    t = lib.decode_step_self_ragged
+    assert t(FAKE, FAKE, None, 20, 5, c, FAKE, 448, 0.125, 0.0, FAKE, FAKE, big, None, None) == -1
+    assert t(FAKE, FAKE, FAKE, 20, 5, c, None, 448, 0.125, 0.0, FAKE, FAKE, big, None, None) == -1
+    assert t(FAKE, FAKE, FAKE, 20, 17, c, FAKE, 448, 0.125, 0.0, FAKE, FAKE, big, None, None) == -2
+    assert t(FAKE, FAKE, FAKE, 20, 5, c, FAKE, 3, 0.125, 0.0, FAKE, FAKE, big, None, None) == -4
+    assert t(FAKE, MIS, FAKE, 20, 5, c, FAKE, 448, 0.125, 0.0, FAKE, FAKE, big, None, None) == -7
+
+
 def test_kv_reorder_validation(lib):
     f = lib.kv_reorder
     assert f(ctypes.byref(_cache(B=5)), None, 10, None, None) == -1

@@ -179,6 +179,171 @@ def test_large_scores_online_rescale(dtype, plan):
     assert e <= TOL[dtype]
 
 
+# ------------------------------------------------------- ragged batches ----
+# Each batch row has its own length ([S] over a batch of sequences). Rows past
+# a row's length hold large "poison" keys and values: reading any of them
+# would move that row's output far outside the tolerance.
+
+def _ragged_setup(dtype, group, N, lens, S_max, g):
+    B, Hkv = len(lens), 2
+    Hq = Hkv * group
+    k = g.standard_normal((B, Hkv, S_max, 64)) * 0.5
+    v = g.standard_normal((B, Hkv, S_max, 64))
+    for b, L in enumerate(lens):
+        k[b, :, L:] = g.standard_normal((Hkv, S_max - L, 64)) * 8.0
+        v[b, :, L:] = 100.0
+    q = g.standard_normal((B, Hq, N, 64))
+    return tuple(O.narrow(a, dtype) for a in (k, v, q))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("N", [1, 5])
+@pytest.mark.parametrize("group,rope", [(1, 0.0), (3, 1e4)])
+def test_ragged_self_attention(dtype, N, group, rope, plan):
+    say(f"case: ragged self {dtype} N={N} group={group} rope={rope} plan={plan}")
+    g = np.random.default_rng([40, N, group, len(dtype)])
+    S_max, len_max = 448, 448
+    lens = [448, 441, 65, N]
+    ks, vs, qs = _ragged_setup(dtype, group, N, lens, S_max, g)
+    cache = kb.Cache.wrap(to_dev(ks, dtype), to_dev(vs, dtype))
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lt = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out = kb.decode_attn_self_ragged(to_dev(qs, dtype), cache, lt, len_max, 0.125, rope_base=rope,
+                                     ws=_ws(), dev_status=st)
+    rows = []
+    for b, L in enumerate(lens):
+        c = O.ConcatCache(1, ks.shape[1], 64, dtype)
+        c.append(ks[b:b + 1, :, :L], vs[b:b + 1, :, :L])
+        rows.append(c)
+    e = max_err(out, O.attend_self_ragged(qs, rows, 0.125, rope_base=rope))
+    assert e <= TOL[dtype], e
+    assert int(st.item()) == 0
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("N", [1, 5, 16])
+def test_ragged_step_self_equals_append_then_attend(dtype, N, plan):
+    """The fused ragged step writes each row's N new rows at lens[b] - N
+    (rotated for bf16) exactly as kv_append_ragged does, returns what
+    decode_attn_self_ragged returns afterwards, and matches the oracle."""
+    say(f"case: ragged step {dtype} N={N} plan={plan}")
+    g = np.random.default_rng([41, N, len(dtype)])
+    rope = 1e4 if dtype == "bf16" else 0.0
+    S_max, len_max = 448, 448
+    lens = [448, 300, N + 2, N]
+    ks, vs, qs = _ragged_setup(dtype, 3 if dtype == "bf16" else 1, N, lens, S_max, g)
+    kn = O.narrow(g.standard_normal((4, 2, N, 64)) * 0.5, dtype)
+    vn = O.narrow(g.standard_normal((4, 2, N, 64)), dtype)
+    lt = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    pt = torch.tensor([L - N for L in lens], dtype=torch.int32, device="cuda")
+    fused = kb.Cache.wrap(to_dev(ks, dtype), to_dev(vs, dtype))
+    split = kb.Cache.wrap(to_dev(ks, dtype), to_dev(vs, dtype))
+    ws = _ws()
+    out_f = kb.decode_step_self_ragged(to_dev(qs, dtype), to_dev(kn, dtype), to_dev(vn, dtype),
+                                       fused, lt, len_max, 0.125, rope_base=rope, ws=ws)
+    kb.kv_append_ragged(split, to_dev(kn, dtype), to_dev(vn, dtype), pt, rope_base=rope)
+    out_s = kb.decode_attn_self_ragged(to_dev(qs, dtype), split, lt, len_max, 0.125,
+                                       rope_base=rope, ws=ws)
+    assert np.array_equal(bits(from_dev(fused.k, dtype)), bits(from_dev(split.k, dtype)))
+    assert np.array_equal(bits(from_dev(fused.v, dtype)), bits(from_dev(split.v, dtype)))
+    assert torch.equal(out_f, out_s)
+    rows = []
+    for b, L in enumerate(lens):
+        c = O.ConcatCache(1, 2, 64, dtype)
+        c.append(ks[b:b + 1, :, :L - N], vs[b:b + 1, :, :L - N])
+        c.append(kn[b:b + 1], vn[b:b + 1], rope_base=rope)
+        rows.append(c)
+    e = max_err(out_f, O.attend_self_ragged(qs, rows, 0.125, rope_base=rope))
+    assert e <= TOL[dtype], e
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_kv_append_ragged_bit_exact_and_skips_rows_outside(dtype):
+    say(f"case: append ragged {dtype}")
+    g = np.random.default_rng(42)
+    B, H, S_max, T = 4, 3, 448, 5
+    base_k = O.narrow(g.standard_normal((B, H, S_max, 64)), dtype)
+    base_v = O.narrow(g.standard_normal((B, H, S_max, 64)), dtype)
+    kn = O.narrow(g.standard_normal((B, H, T, 64)), dtype)
+    vn = O.narrow(g.standard_normal((B, H, T, 64)), dtype)
+    pos = [0, 100, 443, 444]                       # row 3 would end at 449 > S_max
+    cache = kb.Cache.wrap(to_dev(base_k, dtype), to_dev(base_v, dtype))
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kb.kv_append_ragged(cache, to_dev(kn, dtype), to_dev(vn, dtype),
+                        torch.tensor(pos, dtype=torch.int32, device="cuda"), dev_status=st)
+    want_k, want_v = base_k.copy(), base_v.copy()
+    for b in range(3):
+        want_k[b, :, pos[b]:pos[b] + T] = kn[b]
+        want_v[b, :, pos[b]:pos[b] + T] = vn[b]
+    assert np.array_equal(bits(from_dev(cache.k, dtype)), bits(want_k))
+    assert np.array_equal(bits(from_dev(cache.v, dtype)), bits(want_v))
+    assert int(st.item()) == -4
+
+
+def test_ragged_lengths_outside_the_plan_are_clamped_and_flagged():
+    say("case: ragged clamp")
+    g = np.random.default_rng(43)
+    N, len_max = 5, 448
+    given = [500, 3, 100, 448]
+    used = [448, 5, 100, 448]
+    ks, vs, qs = _ragged_setup("f16", 1, N, used, 448, g)
+    cache = kb.Cache.wrap(to_dev(ks, "f16"), to_dev(vs, "f16"))
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = kb.decode_attn_self_ragged(to_dev(qs, "f16"), cache,
+                                     torch.tensor(given, dtype=torch.int32, device="cuda"),
+                                     len_max, 0.125, ws=_ws(), dev_status=st)
+    rows = []
+    for b, L in enumerate(used):
+        c = O.ConcatCache(1, 2, 64, "f16")
+        c.append(ks[b:b + 1, :, :L], vs[b:b + 1, :, :L])
+        rows.append(c)
+    assert max_err(out, O.attend_self_ragged(qs, rows, 0.125)) <= TOL["f16"]
+    assert int(st.item()) == -4
+
+
+def test_ragged_speculative_loop_with_rollback():
+    """Whisper self-attention shape, 4 sequences: every iteration appends 5
+    drafts to each row at its own length (one fused launch), and each row then
+    keeps its own number of them; the next iteration writes over the rest.
+    Outputs match the oracle every iteration, and the kept cache rows match
+    the oracle's cache bit for bit at the end."""
+    say("case: ragged speculative loop")
+    g = np.random.default_rng(44)
+    B, H, N, S_max = 4, 20, 5, 448
+    pos = [10, 57, 200, 390]
+    cache = kb.Cache(B, H, S_max, torch.float16)
+    rows = []
+    for b in range(B):
+        k0 = O.narrow(g.standard_normal((1, H, pos[b], 64)) * 0.5, "f16")
+        v0 = O.narrow(g.standard_normal((1, H, pos[b], 64)), "f16")
+        cache.k[b:b + 1, :, :pos[b]].copy_(to_dev(k0, "f16"))
+        cache.v[b:b + 1, :, :pos[b]].copy_(to_dev(v0, "f16"))
+        c = O.ConcatCache(1, H, 64, "f16")
+        c.append(k0, v0)
+        rows.append(c)
+    ws = _ws()
+    for it in range(8):
+        lens = [p + N for p in pos]
+        q = O.narrow(g.standard_normal((B, H, N, 64)), "f16")
+        kn = O.narrow(g.standard_normal((B, H, N, 64)) * 0.5, "f16")
+        vn = O.narrow(g.standard_normal((B, H, N, 64)), "f16")
+        out = kb.decode_step_self_ragged(to_dev(q, "f16"), to_dev(kn, "f16"), to_dev(vn, "f16"),
+                                         cache, torch.tensor(lens, dtype=torch.int32, device="cuda"),
+                                         S_max, 0.125, ws=ws)
+        for b in range(B):
+            rows[b].append(kn[b:b + 1], vn[b:b + 1])
+        e = max_err(out, O.attend_self_ragged(q, rows, 0.125))
+        assert e <= TOL["f16"], (it, e)
+        for b in range(B):
+            keep = int(g.integers(0, N + 1))
+            pos[b] = min(pos[b] + keep, S_max - N)
+            rows[b].truncate(pos[b])
+    got_k, got_v = from_dev(cache.k, "f16"), from_dev(cache.v, "f16")
+    for b in range(B):
+        assert np.array_equal(bits(got_k[b, :, :pos[b]]), bits(rows[b].k[0]))
+        assert np.array_equal(bits(got_v[b, :, :pos[b]]), bits(rows[b].v[0]))
+
+
 # ------------------------------------------------------ speculative verify ----
 
 @pytest.mark.parametrize("L_before", [64, 128, 443])
