@@ -324,7 +324,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="also time eager (no graph) launches")
     ap.add_argument("--graph-steps", type=int, default=1,
                     help="decode steps captured per graph (1: one graph per step)")
-    ap.add_argument("--workload", default="greedy", choices=["greedy", "verify", "beam", "gqa"],
+    ap.add_argument("--workload", default="greedy",
+                    choices=["greedy", "verify", "beam", "gqa", "ragged"],
                     help="greedy (the headline line) or a further workload")
     ap.add_argument("--unfused", action="store_true",
                     help="separate kv_append and decode_attn_self launches (96 per step)")
@@ -340,7 +341,8 @@ def main():
             print("bench.py needs a GPU", file=sys.stderr)
             sys.exit(1)
         kb.lib()
-        fn = {"verify": workload_verify, "beam": workload_beam, "gqa": workload_gqa}[args.workload]
+        fn = {"verify": workload_verify, "beam": workload_beam, "gqa": workload_gqa,
+              "ragged": workload_ragged}[args.workload]
         line = fn(torch, kb, max(1, args.steps // 448) * 4)
         line.update({"n_gpus": 1, "dtype": "bf16" if args.workload == "gqa" else "f16",
                      "data": "synthetic", "higher_is_better": True})
@@ -555,6 +557,67 @@ def workload_verify(torch, kb, reps):
                            "verify_accept_masked_V51865": round(masked_us, 3)},
             "config": {"workload": "whisper-large-v2 verify: 32 layers x [append 5 + self N=5, cross N=5 "
                                    "over 1500] + verify_accept [1, 5, 51865]; len before 64..443"}}
+
+
+def workload_ragged(torch, kb, reps):
+    """Batched speculative verification with ragged rows at the large-v2
+    shape: 4 sequences, each with its own self and cross caches and its own
+    length (drawn per step in [32, 443]); per step, 32 layers of [append 5
+    draft rows per sequence at its own length + self attention of its 5 causal
+    queries (one ragged launch), cross attention of 5 queries per sequence over
+    its 1500 frames], then verify_accept over [4, 5, 51865]."""
+    g = torch.Generator(device="cuda").manual_seed(6)
+    rn = lambda *sh: (torch.randn(*sh, generator=g, device="cuda") / 8).half()
+    B, N, V, steps = 4, 5, 51865, 7
+    self_c, cross_c = [], []
+    for _ in range(LAYERS):
+        c = kb.Cache(B, H, S_MAX, torch.float16)
+        c.k.copy_(rn(B, H, S_MAX, D)); c.v.copy_(rn(B, H, S_MAX, D))
+        self_c.append(c)
+        x = kb.Cache(B, H, FRAMES, torch.float16)
+        x.k.copy_(rn(B, H, FRAMES, D)); x.v.copy_(rn(B, H, FRAMES, D))
+        cross_c.append(x)
+    q, qx = rn(LAYERS, B, H, N, D), rn(LAYERS, B, H, N, D)
+    kn, vn = rn(LAYERS, B, H, N, D), rn(LAYERS, B, H, N, D)
+    out = torch.empty((LAYERS, B, H, N, D), dtype=torch.float32, device="cuda")
+    outx = torch.empty_like(out)
+    logits = torch.randn(B, N, V, generator=g, device="cuda") * 2
+    draft = torch.randint(0, V, (B, N), generator=g, device="cuda", dtype=torch.int32)
+    acc = torch.empty(B, dtype=torch.int32, device="cuda")
+    nxt = torch.empty(B, dtype=torch.int32, device="cuda")
+    ws = kb.workspace(max(kb.attn_workspace_bytes(B, H, N, FRAMES), kb.verify_workspace_bytes(B, N, V)))
+    before = np.random.default_rng(6).integers(32, 444, size=(steps, B))
+    lens = [torch.tensor(before[i] + N, dtype=torch.int32, device="cuda") for i in range(steps)]
+
+    def step(i):
+        for l in range(LAYERS):
+            kb.decode_step_self_ragged(q[l], kn[l], vn[l], self_c[l], lens[i], S_MAX, 1 / 8,
+                                       out=out[l], ws=ws)
+            kb.decode_attn_cross(qx[l], cross_c[l], FRAMES, 1 / 8, out=outx[l], ws=ws)
+        kb.verify_accept(logits, draft, ws=ws, accept_len=acc, next_token=nxt)
+
+    graphs = _graph_steps(torch, step, range(steps))
+    sec = _time_graphs(torch, graphs, reps)
+    kv = sum(LAYERS * (2 * (int(L) + N) * ROW_BYTES + CROSS_BYTES + 2 * N * ROW_BYTES)
+             for row in before for L in row) / steps
+    self_us = _kernel_us(torch, kb, lambda i: kb.decode_step_self_ragged(
+        q[i % LAYERS], kn[i % LAYERS], vn[i % LAYERS], self_c[i % LAYERS], lens[i % steps], S_MAX,
+        1 / 8, out=out[0], ws=ws))
+    cross_us = _kernel_us(torch, kb, lambda i: kb.decode_attn_cross(
+        qx[i % LAYERS], cross_c[i % LAYERS], FRAMES, 1 / 8, out=outx[0], ws=ws))
+    verify_us = _kernel_us(torch, kb, lambda i: kb.verify_accept(
+        logits, draft, ws=ws, accept_len=acc, next_token=nxt))
+    return {"metric": "ragged batched verify steps/s (4 sequences x N=5 drafts), large-v2 shape, 1 GPU",
+            "value": round(1 / sec, 2), "unit": "verify steps/s", "ms_per_step": round(sec * 1e3, 4),
+            "sequence_steps_per_s": round(B / sec, 1),
+            "effective_kv_gbps": round(kv / sec / 1e9, 1),
+            "kernels_us": {"step_self_ragged_B4_N5": round(self_us, 3),
+                           "cross_B4_N5": round(cross_us, 3),
+                           "verify_accept_B4_V51865": round(verify_us, 3)},
+            "config": {"workload": "whisper-large-v2 ragged verify: 4 sequences, lengths before the "
+                                   "step drawn in [32, 443] per step and sequence; 32 layers x "
+                                   "[append 5 + self N=5 (one ragged launch), cross N=5 over each "
+                                   "sequence's 1500 frames] + verify_accept [4, 5, 51865]"}}
 
 
 def workload_beam(torch, kb, reps):

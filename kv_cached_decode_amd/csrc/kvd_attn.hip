@@ -443,7 +443,10 @@ AttnPlan plan_attn_mfma(int units, int G, int L) {
   const int tiles16 = (G + kRows - 1) / kRows;
   const long unit_bytes = (long)L * 2 * kHeadDim * 2;
   const int forced = env_int("KVD_ATTN_CHUNK", 0);
-  if ((long)units * tiles16 >= 64 && forced <= 0) {
+  // one 16-row tile per wave (prefill) needs 4 tiles per unit to keep the
+  // workgroup's waves busy, and enough units to fill the chip; fewer rows
+  // (verification) share one tile across the 4 waves and split the keys
+  if ((long)units * tiles16 >= 64 && tiles16 >= 4 && forced <= 0) {
     p.rw = 4;
     p.row_tiles = (tiles16 + 3) / 4;
     p.chunk = ((L + kStep - 1) / kStep) * kStep;
