@@ -52,8 +52,10 @@ class SpecLoop:
         self.R = N + 1
         T = c.s_max + self.R
         self.T = T
-        # per-position tables: [layers, T, H, D]
-        self.mq, self.mk, self.mv, self.mx = (rn(c.main_layers, T, H, D) for _ in range(4))
+        # per-position tables: main [layers, H, T, D] (a gather of R positions
+        # is the [layers, H, R, D] operand itself), assistant [layers, T, H, D]
+        # (one position of one layer is a contiguous [H, D] row)
+        self.mq, self.mk, self.mv, self.mx = (rn(c.main_layers, H, T, D) for _ in range(4))
         self.aq, self.ak, self.av, self.ax = (rn(c.asst_layers, T, H, D) for _ in range(4))
         self.LM = torch.randn(T, c.vocab, generator=g, device=device) * 2
         greedy = self.LM.argmax(-1)
@@ -100,33 +102,29 @@ class SpecLoop:
     # -- one iteration, as launched (and captured) ------------------------
     def _assistant(self):
         c = self.cfg
+        rows = (self.P + self.ar).long()                      # positions P .. P + N
+        lens = self.P + 1 + self.ar                           # after each step's append
+        # every step's inputs in one gather per table: [layers, R, H, D], [R, V]
+        q, k, v, x = (t.index_select(1, rows) for t in (self.aq, self.ak, self.av, self.ax))
+        logits = self.LA.index_select(0, rows)
         for j in range(self.R):
-            pos = self.P + j                                  # int32 [1]
-            lens = pos + 1
-            rows = pos.long()
             for l in range(c.asst_layers):
-                q = self.aq[l].index_select(0, rows).view(1, c.heads, 1, 64)
-                k = self.ak[l].index_select(0, rows).view(1, c.heads, 1, 64)
-                v = self.av[l].index_select(0, rows).view(1, c.heads, 1, 64)
-                x = self.ax[l].index_select(0, rows).view(1, c.heads, 1, 64)
-                kb.decode_step_self_ragged(q, k, v, self.a_self[l], lens, c.s_max, 0.125,
-                                           out=self.a_out[l], ws=self.ws)
-                kb.decode_attn_cross(x, self.a_cross[l], c.frames, 0.125, out=self.a_outx[l],
-                                     ws=self.ws)
-            if j < c.drafts:   # greedy draft for position pos + 1
-                logits = self.LA.index_select(0, rows).view(1, 1, c.vocab)
-                kb.verify_accept_masked(logits, None, accept_len=self.scratch[0:1],
+                one = lambda t: t[l, j].view(1, c.heads, 1, 64)
+                kb.decode_step_self_ragged(one(q), one(k), one(v), self.a_self[l], lens[j:j + 1],
+                                           c.s_max, 0.125, out=self.a_out[l], ws=self.ws)
+                kb.decode_attn_cross(one(x), self.a_cross[l], c.frames, 0.125,
+                                     out=self.a_outx[l], ws=self.ws)
+            if j < c.drafts:   # greedy draft for position P + j + 1
+                kb.verify_accept_masked(logits[j].view(1, 1, c.vocab), None,
+                                        accept_len=self.scratch[0:1],
                                         next_token=self.draft[0, j:j + 1], ws=self.ws)
 
     def _main(self):
         c = self.cfg
         rows = (self.P + self.ar).long()                      # positions P .. P + N
         lens = self.P + self.R
-        q = self.mq.index_select(1, rows).transpose(1, 2).contiguous()   # [layers, H, R, D]
-        k = self.mk.index_select(1, rows).transpose(1, 2).contiguous()
-        v = self.mv.index_select(1, rows).transpose(1, 2).contiguous()
-        x = self.mx.index_select(1, rows).transpose(1, 2).contiguous()
-        for l in range(c.main_layers):
+        q, k, v, x = (t.index_select(2, rows) for t in (self.mq, self.mk, self.mv, self.mx))
+        for l in range(c.main_layers):                        # [layers, H, R, D]
             kb.decode_step_self_ragged(q[l:l + 1], k[l:l + 1], v[l:l + 1], self.m_self[l], lens,
                                        c.s_max, 0.125, out=self.m_out[l], ws=self.ws)
             kb.decode_attn_cross(x[l:l + 1], self.m_cross[l], c.frames, 0.125,
@@ -149,11 +147,8 @@ class SpecLoop:
         c = self.cfg
         rows = self.P.long()
         lens = self.P + 1
-        q = self.mq.index_select(1, rows).transpose(1, 2).contiguous()   # [layers, H, 1, D]
-        k = self.mk.index_select(1, rows).transpose(1, 2).contiguous()
-        v = self.mv.index_select(1, rows).transpose(1, 2).contiguous()
-        x = self.mx.index_select(1, rows).transpose(1, 2).contiguous()
-        for l in range(c.main_layers):
+        q, k, v, x = (t.index_select(2, rows) for t in (self.mq, self.mk, self.mv, self.mx))
+        for l in range(c.main_layers):                        # [layers, H, 1, D]
             kb.decode_step_self_ragged(q[l:l + 1], k[l:l + 1], v[l:l + 1], self.m_self[l], lens,
                                        c.s_max, 0.125, out=self.g_out[l], ws=self.ws)
             kb.decode_attn_cross(x[l:l + 1], self.m_cross[l], c.frames, 0.125,
@@ -170,10 +165,12 @@ class SpecLoop:
         """Both caches hold the prompt (positions [0, prompt)); P = prompt."""
         c = self.cfg
         p = c.prompt
-        for caches, tk, tv in ((self.m_self, self.mk, self.mv), (self.a_self, self.ak, self.av)):
-            for l, cache in enumerate(caches):
-                kb.kv_append(cache, tk[l, :p].transpose(0, 1).unsqueeze(0).contiguous(),
-                             tv[l, :p].transpose(0, 1).unsqueeze(0).contiguous(), 0)
+        for l, cache in enumerate(self.m_self):
+            kb.kv_append(cache, self.mk[l, :, :p].unsqueeze(0).contiguous(),
+                         self.mv[l, :, :p].unsqueeze(0).contiguous(), 0)
+        for l, cache in enumerate(self.a_self):
+            kb.kv_append(cache, self.ak[l, :p].transpose(0, 1).unsqueeze(0).contiguous(),
+                         self.av[l, :p].transpose(0, 1).unsqueeze(0).contiguous(), 0)
         self.P.fill_(p)
         self.it.zero_()
         self.log.zero_()

@@ -49,14 +49,13 @@ def test_speculative_stream_equals_greedy(loop, graphs):
     # every kept row sits at its position: K / V of position p are table rows p
     L = P[-1] + loop.R
     for l in range(CFG.main_layers):
-        assert torch.equal(loop.m_self[l].k[0, :, :L], loop.mk[l, :L].transpose(0, 1))
-        assert torch.equal(loop.m_self[l].v[0, :, :L], loop.mv[l, :L].transpose(0, 1))
+        assert torch.equal(loop.m_self[l].k[0, :, :L], loop.mk[l, :, :L])
+        assert torch.equal(loop.m_self[l].v[0, :, :L], loop.mv[l, :, :L])
     # the last verification pass against the oracle
     for l in range(CFG.main_layers):
         c = O.ConcatCache(1, CFG.heads, 64, "f16")
-        c.append(loop.mk[l, :L].transpose(0, 1)[None].cpu().numpy(),
-                 loop.mv[l, :L].transpose(0, 1)[None].cpu().numpy())
-        q = loop.mq[l, P[-1]:L].transpose(0, 1)[None].cpu().numpy()
+        c.append(loop.mk[l, :, :L][None].cpu().numpy(), loop.mv[l, :, :L][None].cpu().numpy())
+        q = loop.mq[l, :, P[-1]:L][None].cpu().numpy()
         assert max_err(loop.m_out[l], O.attend_self(q, c, 0.125)) <= TOL["f16"]
 
 
