@@ -52,21 +52,40 @@ __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Eight floats rounded to nearest-even into the storage type (bf16 through
+// the hardware conversion, v_cvt_pk_bf16_f32).
+template <int DT>
+__device__ __forceinline__ u32x4 round8(const float *x) {
+  if constexpr (DT == BF16) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      v[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x[2 * i], x[2 * i + 1]}, bf16x2));
+    return v;
+  } else {
+    return pack16<DT>(x);
+  }
+}
+
 // x as a high and a low part in the storage type: hi = round(x), lo = round(x - hi).
 template <int DT>
 __device__ __forceinline__ void split_hi_lo(const float *x, u32x4 &hi, u32x4 &lo) {
   float h[8], r[8];
-  hi = pack16<DT>(x);
+  hi = round8<DT>(x);
   unpack16<DT>(hi, h);
 #pragma unroll
   for (int e = 0; e < 8; ++e) r[e] = x[e] - h[e];
-  lo = pack16<DT>(r);
+  lo = round8<DT>(r);
 }
 
-// 16-bit element t (0..3) of an 8-byte chunk.
-__device__ __forceinline__ uint32_t elem16(u32x2 c, int t) {
-  const uint32_t w = (t < 2) ? c[0] : c[1];
-  return (t & 1) ? (w >> 16) : (w & 0xffffu);
+// Element t (0..3) of two 8-byte chunks as one dword: (c0's, c1's << 16).
+template <int t>
+__device__ __forceinline__ uint32_t pair16(u32x2 c0, u32x2 c1) {
+  constexpr uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;
+  return __builtin_amdgcn_perm(c1[t >> 1], c0[t >> 1], sel);
 }
 
 template <int DT, int RW, bool FUSED, bool ROPE, bool RAGGED>
@@ -78,7 +97,8 @@ __global__ __launch_bounds__(64 * kWaves) void attn_mfma_kernel(AttnArgs a) {
   static_assert(DT != F32, "matrix-core tiles take 16-bit storage");
 
   hoist_args(a);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar addressing
   const int c = lane & 15, gq = lane >> 4;
   const int split = blockIdx.x, unit = blockIdx.z;
   const int rt = blockIdx.y * RW + wave % RW;  // 16-row tile of this wave
@@ -98,7 +118,10 @@ __global__ __launch_bounds__(64 * kWaves) void attn_mfma_kernel(AttnArgs a) {
   RowId r{0, 0, 0};
   if (active) r = row_id(a, bkv, hk, grow);
   const int lim = active ? ((sp.causal_base < 0) ? sp.L : sp.causal_base + r.i + 1) : 0;
-  const int kend = min(kspan, (int)groups_max<1>((float)lim));  // wave-uniform
+  const int kend = __builtin_amdgcn_readfirstlane(min(kspan, (int)groups_max<1>((float)lim)));
+  // below lim_lo every row of the wave sees every key
+  const int lim_lo =
+      __builtin_amdgcn_readfirstlane(-(int)groups_max<1>(-(float)(active ? lim : INT_MAX / 2)));
 
   // ---- query operand: dims [8gq, +8) and [32 + 8gq, +8) of the row; a rotary
   // pair (i, i + 32) sits in one lane
@@ -156,11 +179,26 @@ __global__ __launch_bounds__(64 * kWaves) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int s0 = k0 + phase * kStep; s0 < kend; s0 += NPH * kStep) {
+  // One 32-key step: its loads, then its scores, softmax update and P.V.
+  auto load_step = [&](int s0, u32x4 (&ka)[2][2], u32x2 (&vv)[8]) {
     // K: tile t, dims chunk kk -> key s0 + 16t + c, 16 bytes at dims 8gq + 32kk
-    u32x4 ka[2][2];
     // V: lane's 8 keys s0 + {4gq + j (j < 4), 16 + 4gq + j - 4}, bytes [8c, 8c + 8)
-    u32x2 vv[8];
+    if (s0 + kStep <= kend && (!FUSED || s0 + kStep <= nb0)) {  // whole step cached
+      // a uniform base plus a per-lane 32-bit offset: scalar address math
+      const char *kb = kc + (size_t)s0 * ROWB;
+      const char *vb = vc + (size_t)s0 * ROWB;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+          ka[t][kk] = load16(kb + (uint32_t)((16 * t + c) * ROWB + gq * 16 + kk * 64));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int kr = (j < 4) ? 4 * gq + j : 16 + 4 * gq + j - 4;
+        vv[j] = *reinterpret_cast<const u32x2 *>(vb + (uint32_t)(kr * ROWB + c * 8));
+      }
+      return;
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int key = s0 + 16 * t + c;
@@ -186,6 +224,8 @@ __global__ __launch_bounds__(64 * kWaves) void attn_mfma_kernel(AttnArgs a) {
         }
       }
     }
+  };
+  auto compute_step = [&](int s0, const u32x4 (&ka)[2][2], const u32x2 (&vv)[8]) {
     // scores S^T: st[t][i] = q_row . k_(s0 + 16t + 4gq + i)
     f32x4 st[2];
 #pragma unroll
@@ -199,12 +239,20 @@ __global__ __launch_bounds__(64 * kWaves) void attn_mfma_kernel(AttnArgs a) {
     }
     float sc[8];
     float mt = -INFINITY;
+    if (s0 + kStep <= lim_lo && s0 + kStep <= kend) {  // every row sees every key
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int t = j >> 2, i = j & 3;
-      const int key = s0 + 16 * t + 4 * gq + i;
-      sc[j] = (key < lim && key < kend) ? st[t][i] * a.scale_log2 : -INFINITY;
-      mt = fmaxf(mt, sc[j]);
+      for (int j = 0; j < 8; ++j) {
+        sc[j] = st[j >> 2][j & 3] * a.scale_log2;
+        mt = fmaxf(mt, sc[j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int t = j >> 2, i = j & 3;
+        const int key = s0 + 16 * t + 4 * gq + i;
+        sc[j] = (key < lim && key < kend) ? st[t][i] * a.scale_log2 : -INFINITY;
+        mt = fmaxf(mt, sc[j]);
+      }
     }
     mt = groups_max<16>(mt);  // the row's 32 keys sit in lanes c, c+16, c+32, c+48
     const float mn = fmaxf(m, mt);
@@ -224,14 +272,43 @@ __global__ __launch_bounds__(64 * kWaves) void attn_mfma_kernel(AttnArgs a) {
     lsum = lsum * alpha + ps;
     u32x4 phi, plo;
     split_hi_lo<DT>(p, phi, plo);
+    // V^T rows 4c + t: element t of each of the 8 key chunks
+    const u32x4 va[4] = {
+        u32x4{pair16<0>(vv[0], vv[1]), pair16<0>(vv[2], vv[3]), pair16<0>(vv[4], vv[5]), pair16<0>(vv[6], vv[7])},
+        u32x4{pair16<1>(vv[0], vv[1]), pair16<1>(vv[2], vv[3]), pair16<1>(vv[4], vv[5]), pair16<1>(vv[6], vv[7])},
+        u32x4{pair16<2>(vv[0], vv[1]), pair16<2>(vv[2], vv[3]), pair16<2>(vv[4], vv[5]), pair16<2>(vv[6], vv[7])},
+        u32x4{pair16<3>(vv[0], vv[1]), pair16<3>(vv[2], vv[3]), pair16<3>(vv[4], vv[5]), pair16<3>(vv[6], vv[7])}};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      u32x4 va;  // V^T rows 4c + t: element t of each of the 8 key chunks
-#pragma unroll
-      for (int w = 0; w < 4; ++w) va[w] = elem16(vv[2 * w], t) | (elem16(vv[2 * w + 1], t) << 16);
       o[t] *= alpha;
-      o[t] = mfma<DT>(va, phi, o[t]);
-      o[t] = mfma<DT>(va, plo, o[t]);
+      o[t] = mfma<DT>(va[t], phi, o[t]);
+      o[t] = mfma<DT>(va[t], plo, o[t]);
+    }
+  };
+  const int kstride = NPH * kStep;
+  int s0 = k0 + phase * kStep;
+  if constexpr (RW == kWaves) {
+    // prefill: a wave walks many steps, so the next step's loads go out
+    // before this step's math (two register buffers in turn)
+    u32x4 kA[2][2], kB[2][2];
+    u32x2 vA[8], vB[8];
+    if (s0 < kend) load_step(s0, kA, vA);
+    while (s0 < kend) {
+      if (s0 + kstride < kend) load_step(s0 + kstride, kB, vB);
+      compute_step(s0, kA, vA);
+      s0 += kstride;
+      if (s0 >= kend) break;
+      if (s0 + kstride < kend) load_step(s0 + kstride, kA, vA);
+      compute_step(s0, kB, vB);
+      s0 += kstride;
+    }
+  } else {
+    // verification: one or two steps per wave (prefetching measured slower)
+    for (; s0 < kend; s0 += kstride) {
+      u32x4 ka[2][2];
+      u32x2 vv[8];
+      load_step(s0, ka, vv);
+      compute_step(s0, ka, vv);
     }
   }
   lsum = groups_sum<16>(lsum);  // the row's keys were spread over the 4 lane groups
