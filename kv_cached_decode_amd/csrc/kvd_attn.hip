@@ -239,22 +239,10 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
       float mt = sc[0][g];
 #pragma unroll
       for (int s = 1; s < kSteps; ++s) mt = fmaxf(mt, sc[s][g]);
-      const float mn = fmaxf(m[g], mt);
-      if (mn != -INFINITY) {
-        const float alpha = exp2f(m[g] - mn);
-        float ls = l[g] * alpha;
+      online_update(m[g], l[g], o[g], mt, [&](auto &&fn) {
 #pragma unroll
-        for (int e = 0; e < VE; ++e) o[g][e] *= alpha;
-#pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-          const float p = exp2f(sc[s][g] - mn);
-          ls += p;
-#pragma unroll
-          for (int e = 0; e < VE; ++e) o[g][e] = fmaf(p, vf[s][e], o[g][e]);
-        }
-        l[g] = ls;
-        m[g] = mn;
-      }
+        for (int s = 0; s < kSteps; ++s) fn(sc[s][g], vf[s]);
+      });
     }
     t0 += stride;
   };
@@ -306,22 +294,10 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
         float mt = sc[0][g];
 #pragma unroll
         for (int s = 1; s < kSteps; ++s) mt = fmaxf(mt, sc[s][g]);
-        const float mn = fmaxf(m[g], mt);
-        if (mn != -INFINITY) {
-          const float alpha = exp2f(m[g] - mn);
-          float ls = l[g] * alpha;
+        online_update(m[g], l[g], o[g], mt, [&](auto &&fn) {
 #pragma unroll
-          for (int e = 0; e < VE; ++e) o[g][e] *= alpha;
-#pragma unroll
-          for (int s = 0; s < kSteps; ++s) {
-            const float p = exp2f(sc[s][g] - mn);
-            ls += p;
-#pragma unroll
-            for (int e = 0; e < VE; ++e) o[g][e] = fmaf(p, vf[s][e], o[g][e]);
-          }
-          l[g] = ls;
-          m[g] = mn;
-        }
+          for (int s = 0; s < kSteps; ++s) fn(sc[s][g], vf[s]);
+        });
       }
     }
   }

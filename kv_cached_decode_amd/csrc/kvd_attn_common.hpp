@@ -54,6 +54,35 @@ __device__ __forceinline__ RowSpan row_span(const AttnArgs &a, int bkv) {
   return s;
 }
 
+// Online softmax (log2 domain), one row, one step of keys: mt is the step's
+// largest score and each(fn) calls fn(score, v) for every key of the step.
+// The row's reference m moves only when a score passes it by more than
+// kLazySoftmax, so p = 2^(score - m) stays below 2^kLazySoftmax and o and l
+// are rescaled only when some lane of the wavefront moved (exact: o and l
+// always share the reference m; the merges weigh partials by their m).
+constexpr float kLazySoftmax = 8.f;
+template <int VE, typename Each>
+__device__ __forceinline__ void online_update(float &m, float &l, float (&o)[VE], float mt,
+                                              Each each) {
+  const bool move = mt > m + kLazySoftmax;
+  if (__builtin_amdgcn_ballot_w64(move)) {
+    const float mn = move ? mt : m;
+    const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+#pragma unroll
+    for (int e = 0; e < VE; ++e) o[e] *= alpha;
+    l *= alpha;
+    m = mn;
+  }
+  if (m != -INFINITY) {
+    each([&](float sc, const float (&v)[VE]) {
+      const float p = __builtin_amdgcn_exp2f(sc - m);
+      l += p;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) o[e] = fmaf(p, v[e], o[e]);
+    });
+  }
+}
+
 // Every kernel argument the first loads depend on, fetched in one go: the
 // empty asm keeps the compiler from sinking a fetch into a later branch,
 // which would add a serial round trip before the first key load.

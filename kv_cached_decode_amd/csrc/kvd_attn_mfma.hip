@@ -255,21 +255,25 @@ __global__ __launch_bounds__(64 * kWaves) void attn_mfma_kernel(AttnArgs a) {
       }
     }
     mt = groups_max<16>(mt);  // the row's 32 keys sit in lanes c, c+16, c+32, c+48
-    const float mn = fmaxf(m, mt);
-    float p[8];
-    float alpha = 1.f, ps = 0.f;
+    // lazy reference, as online_update: m moves only when a score passes it
+    // by more than kLazySoftmax; o and l are rescaled only when a row moved
+    const bool move = mt > m + kLazySoftmax;
+    if (__builtin_amdgcn_ballot_w64(move)) {
+      const float mn = move ? mt : m;
+      const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mn);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) p[j] = 0.f;
-    if (mn != -INFINITY) {
-      alpha = exp2f(m - mn);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        p[j] = exp2f(sc[j] - mn);
-        ps += p[j];
-      }
+      for (int t = 0; t < 4; ++t) o[t] *= alpha;
+      lsum *= alpha;
       m = mn;
     }
-    lsum = lsum * alpha + ps;
+    float p[8];
+    float ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      p[j] = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc[j] - m);
+      ps += p[j];
+    }
+    lsum += ps;
     u32x4 phi, plo;
     split_hi_lo<DT>(p, phi, plo);
     // V^T rows 4c + t: element t of each of the 8 key chunks
@@ -280,7 +284,6 @@ __global__ __launch_bounds__(64 * kWaves) void attn_mfma_kernel(AttnArgs a) {
         u32x4{pair16<3>(vv[0], vv[1]), pair16<3>(vv[2], vv[3]), pair16<3>(vv[4], vv[5]), pair16<3>(vv[6], vv[7])}};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      o[t] *= alpha;
       o[t] = mfma<DT>(va[t], phi, o[t]);
       o[t] = mfma<DT>(va[t], plo, o[t]);
     }
