@@ -310,7 +310,14 @@ def cpu_baseline(target_s: float = 12.0):
     if limiter is not None:
         limiter.unregister()
     mean = float(np.mean(times))
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": 1.0 / mean, "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "cpu_model": model, "host_cpus": os.cpu_count(),
             "sample": f"{len(times)} full 32-layer decode steps at self lengths {sorted(set(used))} "
                       f"(oracle: numpy float64, BLAS limited to 1 thread), {spent:.1f} s total"}
 

@@ -129,7 +129,7 @@ def plan(request, monkeypatch):
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("N", [1, 5])
-@pytest.mark.parametrize("L", [5, 64, 129, 130, 133, 257, 448, 1100])
+@pytest.mark.parametrize("L", [1, 2, 5, 64, 129, 130, 133, 257, 448, 1100])
 def test_sentinel_mask(dtype, N, L, plan):
     """Query i's own key and the next key (one it must not see) both align
     with it; one-hot values name every key that got weight."""
