@@ -332,7 +332,7 @@ def main():
     ap.add_argument("--graph-steps", type=int, default=1,
                     help="decode steps captured per graph (1: one graph per step)")
     ap.add_argument("--workload", default="greedy",
-                    choices=["greedy", "verify", "beam", "gqa", "ragged", "specloop"],
+                    choices=["greedy", "verify", "beam", "gqa", "ragged", "specloop", "prefill"],
                     help="greedy (the headline line) or a further workload")
     ap.add_argument("--unfused", action="store_true",
                     help="separate kv_append and decode_attn_self launches (96 per step)")
@@ -349,7 +349,8 @@ def main():
             sys.exit(1)
         kb.lib()
         fn = {"verify": workload_verify, "beam": workload_beam, "gqa": workload_gqa,
-              "ragged": workload_ragged, "specloop": workload_specloop}[args.workload]
+              "ragged": workload_ragged, "specloop": workload_specloop,
+              "prefill": workload_prefill}[args.workload]
         line = fn(torch, kb, max(1, args.steps // 448) * 4)
         line.update({"n_gpus": 1, "dtype": "bf16" if args.workload == "gqa" else "f16",
                      "data": "synthetic", "higher_is_better": True})
@@ -676,6 +677,35 @@ def workload_specloop(torch, kb, reps):
                                    "(assistant argmax agrees with the main model's w.p. 0.75); "
                                    f"{loop.max_iters} iterations from a {p0}-token prompt; greedy: "
                                    f"{loop.max_greedy} steps"}}
+
+
+def workload_prefill(torch, kb, reps):
+    """The GQA prefill attention alone (the matrix-core tile with one 16-row
+    tile per wave): B8, 9 query / 3 KV heads x 64, bf16, rotary base 1e4,
+    512 causal queries over 512 cached keys, one layer's cache per launch."""
+    g = torch.Generator(device="cuda").manual_seed(8)
+    B, Hq, Hkv, P, S = 8, 9, 3, 512, 1024
+    layers = 4
+    caches = []
+    for _ in range(layers):
+        c = kb.Cache(B, Hkv, S, torch.bfloat16)
+        c.k.copy_(torch.randn(B, Hkv, S, D, generator=g, device="cuda").bfloat16())
+        c.v.copy_(torch.randn(B, Hkv, S, D, generator=g, device="cuda").bfloat16())
+        caches.append(c)
+    q = torch.randn(layers, B, Hq, P, D, generator=g, device="cuda").bfloat16()
+    out = torch.empty((B, Hq, P, D), dtype=torch.float32, device="cuda")
+    ws = kb.workspace(kb.attn_workspace_bytes(B, Hq, P, P))
+    us = _kernel_us(torch, kb, lambda i: kb.decode_attn_self(q[i % layers], caches[i % layers], P,
+                                                             0.125, rope_base=1e4, out=out, ws=ws),
+                    n=32 * max(1, reps))
+    flops = 4 * D * B * Hq * (P * (P + 1) // 2)   # QK^T and PV over the causal pairs
+    tflops = flops / (us * 1e-6) / 1e12
+    return {"metric": "GQA prefill attention TFLOP/s (512 causal queries), 1 GPU", "value": round(tflops, 2),
+            "unit": "TFLOP/s", "kernel_us": round(us, 3), "algorithmic_gflop": round(flops / 1e9, 3),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": 2500.0, "unit": "TFLOP/s",
+                         "frac": round(tflops / 2500.0, 4)},
+            "config": {"workload": "GQA prefill attention: B8, Hq9/Hkv3 x 64, bf16, RoPE 1e4, 512 causal "
+                                   "queries over 512 keys (one launch per layer's cache)"}}
 
 
 def workload_beam(torch, kb, reps):
