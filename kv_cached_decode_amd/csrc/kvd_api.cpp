@@ -62,6 +62,16 @@ int prepare_attn(AttnArgs &a, int dtype, void *ws, size_t ws_bytes) {
   a.gm = p.gm;
   a.mfma = p.mfma;
   a.rw = p.rw;
+  // Causal prefill on one tile per wave: the tiles late in a sequence walk
+  // many more keys than the early ones, so each wave takes a complementary
+  // pair (tile t, tile T - 1 - t; rows are ordered by head, then position),
+  // which evens the waves' work and halves their number.
+  a.pair = 0;
+  if (p.mfma && p.rw == 4 && a.causal_base >= 0 && !a.k_new) {
+    const int tiles16 = (a.G + 15) / 16;
+    a.pair = 1;
+    a.row_tiles = ((tiles16 + 1) / 2 + 3) / 4;
+  }
   if (p.splits > 1) {
     const size_t need = attn_bytes(p);
     if (!ws) return KVD_ERR_WORKSPACE;

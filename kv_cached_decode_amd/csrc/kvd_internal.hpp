@@ -71,6 +71,7 @@ struct AttnArgs {
   int gm;                        // rows per tile (template bucket)
   int mfma;                      // 1: matrix-core tile kernel (blocks of queries)
   int rw;                        // matrix-core kernel: 16-row tiles per workgroup (1 or 4)
+  int pair;                      // rw = 4, causal: each wave takes tiles t and T - 1 - t
 };
 
 struct VerifyArgs {

@@ -344,6 +344,37 @@ def test_ragged_speculative_loop_with_rollback():
         assert np.array_equal(bits(got_v[b, :, :pos[b]]), bits(rows[b].v[0]))
 
 
+@pytest.mark.parametrize("dtype,rope", [("f16", 0.0), ("bf16", 1e4)])
+@pytest.mark.parametrize("N", [80, 72, 100])
+@pytest.mark.parametrize("ragged", [False, True])
+def test_prefill_tiles_paired(dtype, rope, N, ragged):
+    """Causal blocks on one 16-row tile per wave, each wave taking a tile and
+    its complement (4 rows x 2 KV heads x 4 query heads: 20, 18 and 25 tiles
+    per unit, the odd count leaving the middle tile alone)."""
+    say(f"case: paired prefill {dtype} N={N} ragged={ragged}")
+    g = np.random.default_rng([45, N, len(dtype), int(ragged)])
+    B, Hq, Hkv, S = 4, 8, 2, 256
+    lens = [N + 30, N + 30, N + 30, N + 30] if not ragged else [N + 30, N + 3, N + 100, N]
+    k = O.narrow(g.standard_normal((B, Hkv, S, 64)), dtype)
+    v = O.narrow(g.standard_normal((B, Hkv, S, 64)), dtype)
+    q = O.narrow(g.standard_normal((B, Hq, N, 64)), dtype)
+    cache = kb.Cache.wrap(to_dev(k, dtype), to_dev(v, dtype))
+    ws = _ws()
+    if ragged:
+        out = kb.decode_attn_self_ragged(to_dev(q, dtype), cache,
+                                         torch.tensor(lens, dtype=torch.int32, device="cuda"),
+                                         max(lens), 0.125, rope_base=rope, ws=ws)
+    else:
+        out = kb.decode_attn_self(to_dev(q, dtype), cache, lens[0], 0.125, rope_base=rope, ws=ws)
+    rows = []
+    for b, L in enumerate(lens):
+        c = O.ConcatCache(1, Hkv, 64, dtype)
+        c.append(k[b:b + 1, :, :L], v[b:b + 1, :, :L])
+        rows.append(c)
+    e = max_err(out, O.attend_self_ragged(q, rows, 0.125, rope_base=rope))
+    assert e <= TOL[dtype], e
+
+
 # ------------------------------------------------------ speculative verify ----
 
 @pytest.mark.parametrize("L_before", [64, 128, 443])
