@@ -711,17 +711,21 @@ def workload_prefill(torch, kb, reps):
 def workload_beam(torch, kb, reps):
     """Beam search with 5 beams at the large-v2 shape: per step, beam_select
     over [1, 5, 51865] fp32 logits (N(0, 4)) with the running scores the step
-    before produced, then 32 layers of [kv_reorder by the selected parents,
-    append + self attention, cross attention over a cross cache shared by the
-    beams]; 224 steps."""
+    before produced, then 32 layers of [the beam step: each beam's parent rows
+    read from one of the layer's two caches and written into the other with
+    the new row, plus self attention, in one launch; cross attention over a
+    cross cache shared by the beams]; 224 steps. The same steps with an
+    in-place kv_reorder before the fused append + attention (one cache per
+    layer) are timed beside it."""
     g = torch.Generator(device="cuda").manual_seed(4)
     rn = lambda *sh: (torch.randn(*sh, generator=g, device="cuda") / 8).half()
     B, steps, V, eot = 5, 224, 51865, 50256
-    self_c, cross_c = [], []
+    pairs, cross_c = [], []
     for _ in range(LAYERS):
-        c = kb.Cache(B, H, S_MAX, torch.float16)
-        c.k.copy_(rn(B, H, S_MAX, D)); c.v.copy_(rn(B, H, S_MAX, D))
-        self_c.append(c)
+        pr = [kb.Cache(B, H, S_MAX, torch.float16) for _ in range(2)]
+        for c in pr:
+            c.k.copy_(rn(B, H, S_MAX, D)); c.v.copy_(rn(B, H, S_MAX, D))
+        pairs.append(pr)
         x = kb.Cache(1, H, FRAMES, torch.float16)
         x.k.copy_(rn(1, H, FRAMES, D)); x.v.copy_(rn(1, H, FRAMES, D))
         cross_c.append(x)
@@ -741,9 +745,19 @@ def workload_beam(torch, kb, reps):
         kb.beam_select(logits[s], prev["score"], eot, ws=wsb, out=cur)
         parent = cur["parent"][0]
         for l in range(LAYERS):
+            src, dst = pairs[l][s % 2], pairs[l][(s + 1) % 2]
+            kb.decode_step_self_beams(q[l], kn[l], vn[l], src, dst, parent, s + 1, 1 / 8,
+                                      out=out[l], ws=ws)
+            kb.decode_attn_cross(qx[l], cross_c[l], FRAMES, 1 / 8, out=outx[l], ws=ws)
+
+    def step_inplace(s):
+        cur, prev = outs[s % 2], outs[(s + 1) % 2]
+        kb.beam_select(logits[s], prev["score"], eot, ws=wsb, out=cur)
+        parent = cur["parent"][0]
+        for l in range(LAYERS):
             if s > 0:
-                kb.kv_reorder(self_c[l], parent, s)
-            kb.decode_step_self(q[l], kn[l], vn[l], self_c[l], s + 1, 1 / 8, out=out[l], ws=ws)
+                kb.kv_reorder(pairs[l][0], parent, s)
+            kb.decode_step_self(q[l], kn[l], vn[l], pairs[l][0], s + 1, 1 / 8, out=out[l], ws=ws)
             kb.decode_attn_cross(qx[l], cross_c[l], FRAMES, 1 / 8, out=outx[l], ws=ws)
 
     graphs = _graph_steps(torch, step, range(steps))
@@ -754,22 +768,31 @@ def workload_beam(torch, kb, reps):
         changed += int((outs[s % 2]["parent"][0].cpu() != torch.arange(B, dtype=torch.int32)).sum())
     changed /= steps
     sec = _time_graphs(torch, graphs, reps)
-    # reorder moves (reads and writes) the rows of the beams whose parent differs
-    kv = sum(LAYERS * (B * 2 * (s + 1) * ROW_BYTES + CROSS_BYTES + B * 2 * ROW_BYTES
-                       + 2 * changed * 2 * s * ROW_BYTES) + B * V * 4 for s in range(steps)) / steps
+    del graphs
+    sec_inplace = _time_graphs(torch, _graph_steps(torch, step_inplace, range(steps)), reps)
+    # the beam step reads each beam's s parent rows once (for the copy and the
+    # attention) and writes them and the new row; cross attention reads the
+    # shared cache; scoring reads the logits
+    kv = sum(LAYERS * (B * 2 * s * ROW_BYTES * 2 + B * 2 * ROW_BYTES + CROSS_BYTES) + B * V * 4
+             for s in range(steps)) / steps
     parent = outs[0]["parent"][0]
-    reorder_us = _kernel_us(torch, kb, lambda i: kb.kv_reorder(self_c[i % LAYERS], parent, 200))
+    beam_us = _kernel_us(torch, kb, lambda i: kb.decode_step_self_beams(
+        q[i % LAYERS], kn[i % LAYERS], vn[i % LAYERS], pairs[i % LAYERS][0], pairs[i % LAYERS][1],
+        parent, 201, 1 / 8, out=out[0], ws=ws))
+    reorder_us = _kernel_us(torch, kb, lambda i: kb.kv_reorder(pairs[i % LAYERS][0], parent, 200))
     select_us = _kernel_us(torch, kb, lambda i: kb.beam_select(logits[i % steps], outs[1]["score"], eot,
                                                               ws=wsb, out=outs[0]))
     return {"metric": "beam-search decode steps/s (5 beams), large-v2 shape, 1 GPU",
             "value": round(1 / sec, 2), "unit": "steps/s", "ms_per_step": round(sec * 1e3, 4),
             "effective_kv_gbps": round(kv / sec / 1e9, 1),
             "beams_changed_per_step": round(changed, 2),
-            "kernels_us": {"kv_reorder_len200": round(reorder_us, 3),
+            "inplace_reorder_steps_per_s": round(1 / sec_inplace, 2),
+            "kernels_us": {"beam_step_len201": round(beam_us, 3),
+                           "kv_reorder_len200": round(reorder_us, 3),
                            "beam_select_5x51865": round(select_us, 3)},
             "config": {"workload": "whisper-large-v2 beam 5: beam_select [1, 5, 51865] + 32 layers x "
-                                   "[kv_reorder by its parents, append + self, cross shared by beams]; "
-                                   "224 steps"}}
+                                   "[beam step: parent rows copied between two caches + append + "
+                                   "self attention, one launch; cross shared by beams]; 224 steps"}}
 
 
 def workload_gqa(torch, kb, reps):

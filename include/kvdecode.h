@@ -181,6 +181,33 @@ int decode_step_self_ragged(const void *q, const void *k_new, const void *v_new,
                             int32_t len_max, float scale, float rope_base, float *out, void *ws,
                             size_t ws_bytes, int32_t *dev_status, void *stream);
 
+/* decode_step_self_beams - one beam-search decode step on two caches used in
+ * turn: kv_reorder, then decode_step_self, in one launch (N <= 16), with the
+ * reordered rows written into a second cache instead of in place ([W] beam
+ * search update, step 4, rearrange_kv_cache, followed by the next step's
+ * append and attention). For every beam b, rows [0, len - N) of every head
+ * of dst become rows [0, len - N) of beam parent[b] in src; the N new K/V
+ * rows go to [len - N, len) of dst; the queries attend over dst as
+ * decode_step_self does. Each cached row is read once, for both the copy and
+ * the attention. The caller swaps src and dst for the next step.
+ *   src, dst: caches of equal dtype, B, H and S_max whose storage does not
+ *     overlap (src is only read); rows of dst from len on are not touched.
+ *   parent: device int32 [B], repeats allowed. A parent outside [0, B)
+ *     makes beam b read its own rows of src and stores KVD_ERR_SHAPE in
+ *     dev_status (device int32, or NULL).
+ *   ws: kvd_attn_workspace_bytes(B, Hq, N, len).
+ *   Other arguments and results as decode_step_self on dst. After the call
+ *   dst holds exactly what the copy and kv_append(dst, k_new, v_new, len - N,
+ *   N, rope_base) would have written, and `out` equals decode_attn_self's.
+ * Errors: as decode_step_self; KVD_ERR_DTYPE when the dtypes differ;
+ *   KVD_ERR_SHAPE when B, H or S_max differ, the storage overlaps, or
+ *   N > 16. */
+int decode_step_self_beams(const void *q, const void *k_new, const void *v_new, int32_t Hq,
+                           int32_t N, const kvd_cache *src, const kvd_cache *dst,
+                           const int32_t *parent, int32_t len, float scale, float rope_base,
+                           float *out, void *ws, size_t ws_bytes, int32_t *dev_status,
+                           void *stream);
+
 /* decode_attn_cross - attention of N queries per row over all `frames`
  * rows of a cross-attention cache, with no mask ([W]: cross-attention K/V
  * computed once from the encoder and reused every step).

@@ -57,6 +57,10 @@ _SIGNATURES = {
     "decode_step_self": (c_int, [c_void_p, c_void_p, c_void_p, c_int32, c_int32,
                                  ctypes.POINTER(KvdCache), c_int32, c_float, c_float, c_void_p,
                                  c_void_p, c_size_t, c_void_p]),
+    "decode_step_self_beams": (c_int, [c_void_p, c_void_p, c_void_p, c_int32, c_int32,
+                                       ctypes.POINTER(KvdCache), ctypes.POINTER(KvdCache),
+                                       c_void_p, c_int32, c_float, c_float, c_void_p, c_void_p,
+                                       c_size_t, c_void_p, c_void_p]),
     "decode_attn_cross": (c_int, [c_void_p, c_int32, c_int32, c_int32, ctypes.POINTER(KvdCache),
                                   c_int32, c_float, c_void_p, c_void_p, c_size_t, c_void_p]),
     "verify_accept": (c_int, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_int32,
@@ -331,6 +335,34 @@ def decode_step_self_ragged(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.T
         _dev(v_new, "v_new", cache.dtype), Hq, N, ctypes.byref(d), _rows(lens, d.B, "lens"),
         len_max, scale, rope_base, _dev(out, "out", torch.float32), _dev(ws, "ws"),
         ws.numel() * ws.element_size(), st, _stream()))
+    return out
+
+
+def decode_step_self_beams(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                           src: Cache, dst: Cache, parent: torch.Tensor, length: int,
+                           scale: float, rope_base: float = 0.0,
+                           out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                           dev_status: torch.Tensor | None = None) -> torch.Tensor:
+    """One beam step on two caches used in turn: dst rows [0, length - N) of
+    beam b become src rows of beam parent[b], the N new rows are appended at
+    [length - N, length) of dst and the queries attend over dst; one launch
+    (N <= 16)."""
+    d, s = dst.desc(), src.desc()
+    if q.dim() != 4 or q.shape[0] != d.B or q.shape[3] != d.D:
+        raise ValueError(f"q must be [B={d.B}, Hq, N, {d.D}], got {tuple(q.shape)}")
+    Hq, N = q.shape[1], q.shape[2]
+    if tuple(k_new.shape) != (d.B, d.H, N, d.D) or k_new.shape != v_new.shape:
+        raise ValueError(f"k_new/v_new must be [{d.B}, {d.H}, {N}, {d.D}]")
+    out = _attn_out(q, out)
+    if ws is None:
+        ws = workspace(attn_workspace_bytes(d.B, Hq, N, length), q.device)
+    st = _dev(dev_status, "dev_status", torch.int32) if dev_status is not None else None
+    _check("decode_step_self_beams", lib().decode_step_self_beams(
+        _dev(q, "q", dst.dtype), _dev(k_new, "k_new", dst.dtype),
+        _dev(v_new, "v_new", dst.dtype), Hq, N, ctypes.byref(s), ctypes.byref(d),
+        _rows(parent, d.B, "parent"), length, scale, rope_base,
+        _dev(out, "out", torch.float32), _dev(ws, "ws"), ws.numel() * ws.element_size(), st,
+        _stream()))
     return out
 
 

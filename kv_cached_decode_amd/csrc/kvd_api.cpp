@@ -14,6 +14,9 @@
 using kvd::AttnArgs;
 using kvd::AttnPlan;
 
+static_assert(kvd::kStatusBadShape == KVD_ERR_SHAPE, "kernel status values");
+static_assert(kvd::kStatusCapacity == KVD_ERR_CAPACITY, "kernel status values");
+
 namespace {
 
 bool dtype_ok(int dt) { return dt == KVD_F32 || dt == KVD_F16 || dt == KVD_BF16; }
@@ -52,7 +55,8 @@ size_t attn_bytes(const AttnPlan &p) { return kCounterBytes + p.part_floats * si
 // Fill the plan-dependent fields and the workspace pointers.
 int prepare_attn(AttnArgs &a, int dtype, void *ws, size_t ws_bytes) {
   const int units = a.Bkv * a.Hkv;
-  const AttnPlan p = kvd::plan_attn(dtype, units, a.G, a.N, a.L, a.rope_base > 0.f);
+  // the beam step runs on the streaming kernel (it alone copies parent rows)
+  const AttnPlan p = kvd::plan_attn(dtype, units, a.G, a.N, a.L, a.rope_base > 0.f, !a.parent);
   if (p.row_tiles > 65535 || units > 65535) return KVD_ERR_SHAPE;  // grid limits
   if (p.splits > kvd::kMaxSplits) return KVD_ERR_SHAPE;  // the merge gives each split one lane
   a.chunk = p.chunk;
@@ -207,7 +211,8 @@ namespace {
 int prepare_self(AttnArgs &a, const void *q, const void *k_new, const void *v_new, int32_t Hq,
                  int32_t N, const kvd_cache *cache, int32_t len, float scale, float rope_base,
                  float *out, void *ws, size_t ws_bytes, const int32_t *lens = nullptr,
-                 int32_t *dev_status = nullptr) {
+                 int32_t *dev_status = nullptr, const kvd_cache *src = nullptr,
+                 const int32_t *parent = nullptr) {
   int st = check_cache(cache);
   if (st) return st;
   if (!q || !out) return KVD_ERR_NULL;
@@ -221,6 +226,11 @@ int prepare_self(AttnArgs &a, const void *q, const void *k_new, const void *v_ne
   a = AttnArgs{};
   a.lens = lens;
   a.dev_status = dev_status;
+  if (parent) {
+    a.parent = parent;
+    a.k_src = src->k;
+    a.v_src = src->v;
+  }
   a.q = q;
   a.k = cache->k;
   a.v = cache->v;
@@ -315,6 +325,37 @@ int decode_step_self_ragged(const void *q, const void *k_new, const void *v_new,
   return status_of(kvd::launch_attn(cache->dtype, a, static_cast<hipStream_t>(stream)));
 }
 
+int decode_step_self_beams(const void *q, const void *k_new, const void *v_new, int32_t Hq,
+                           int32_t N, const kvd_cache *src, const kvd_cache *dst,
+                           const int32_t *parent, int32_t len, float scale, float rope_base,
+                           float *out, void *ws, size_t ws_bytes, int32_t *dev_status,
+                           void *stream) {
+  int st = check_cache(src);
+  if (st) return st;
+  st = check_cache(dst);
+  if (st) return st;
+  if (!k_new || !v_new || !parent) return KVD_ERR_NULL;
+  if (src->dtype != dst->dtype) return KVD_ERR_DTYPE;
+  if (src->B != dst->B || src->H != dst->H || src->S_max != dst->S_max || N > kvd::kMaxFusedRows)
+    return KVD_ERR_SHAPE;
+  // beams read parents' rows of src while writing their own rows of dst:
+  // the two caches' storage must not overlap
+  const uintptr_t bytes = (uintptr_t)src->B * src->H * src->S_max * kvd::kHeadDim *
+                          (src->dtype == KVD_F32 ? 4 : 2);
+  const void *sp[2] = {src->k, src->v}, *dp[2] = {dst->k, dst->v};
+  for (const void *x : sp)
+    for (const void *y : dp) {
+      const uintptr_t u = reinterpret_cast<uintptr_t>(x), w = reinterpret_cast<uintptr_t>(y);
+      if (u < w + bytes && w < u + bytes) return KVD_ERR_SHAPE;
+    }
+  if (!aligned4(parent)) return KVD_ERR_ALIGN;
+  AttnArgs a{};
+  st = prepare_self(a, q, k_new, v_new, Hq, N, dst, len, scale, rope_base, out, ws, ws_bytes,
+                    nullptr, dev_status, src, parent);
+  if (st) return st;
+  return status_of(kvd::launch_attn(dst->dtype, a, static_cast<hipStream_t>(stream)));
+}
+
 int decode_attn_cross(const void *q, int32_t B, int32_t Hq, int32_t N, const kvd_cache *xcache,
                       int32_t frames, float scale, float *out, void *ws, size_t ws_bytes,
                       void *stream) {
@@ -361,9 +402,11 @@ size_t kvd_attn_workspace_bytes(int32_t B, int32_t Hq, int32_t N, int32_t len_ma
       if (shared && B == 1) continue;
       const int units = shared ? hkv : B * hkv;
       const int G = (shared ? B : 1) * group * N;
-      for (int dt = 0; dt < 2; ++dt) {
+      // fp32, 16-bit on matrix-core tiles, 16-bit streaming (the beam step)
+      for (int dt = 0; dt < 3; ++dt) {
         for (int L = 1; L <= len_max; ++L) {
-          const AttnPlan p = kvd::plan_attn(dt == 0 ? kvd::F32 : kvd::F16, units, G, N, L, false);
+          const AttnPlan p =
+              kvd::plan_attn(dt == 0 ? kvd::F32 : kvd::F16, units, G, N, L, false, dt != 2);
           if (p.splits > 1) {
             const size_t b = attn_bytes(p);
             if (b > best) best = b;

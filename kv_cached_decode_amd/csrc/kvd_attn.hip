@@ -38,7 +38,7 @@ struct AttnGeom {
   static constexpr int ROWB = kHeadDim * Storage<DT>::bytes;
 };
 
-template <int DT, int GM, bool FUSED, int NWMAX, bool ROPE, bool RAGGED>
+template <int DT, int GM, bool FUSED, int NWMAX, bool ROPE, bool RAGGED, bool BEAM>
 __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
   using Geo = AttnGeom<DT>;
   constexpr int D = kHeadDim;
@@ -65,6 +65,21 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
   char *kc = static_cast<char *>(a.k) + head * a.S_max * ROWB;
   char *vc = static_cast<char *>(a.v) + head * a.S_max * ROWB;
   const int nb0 = max(k0, sp.new_base);  // first new row of this key range
+  // Where the cached rows are read: this unit's own rows, or (beam step:
+  // reorder + append + attend) the rows of beam parent[b] in the source
+  // cache, which row tile 0 also writes into this beam's rows of k / v.
+  const char *ks = kc, *vs = vc;
+  static_assert(!BEAM || FUSED, "the beam step appends its new rows");
+  if constexpr (BEAM) {
+    int p = a.parent[bkv];
+    if (p < 0 || p >= a.Bkv) {  // outside the contract: keep this beam's own rows
+      if (a.dev_status && threadIdx.x == 0) *a.dev_status = kStatusBadShape;
+      p = bkv;
+    }
+    const size_t src = ((size_t)p * a.Hkv + hk) * a.S_max * ROWB;
+    ks = static_cast<const char *>(a.k_src) + src;
+    vs = static_cast<const char *>(a.v_src) + src;
+  }
 
   // ---- which keys each query row sees (indices only, no memory access)
   int lim[GM];
@@ -93,8 +108,8 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
       kd[s] = u32x4{0, 0, 0, 0};
       vd[s] = u32x4{0, 0, 0, 0};
       if (key < kend && (!FUSED || key < nb0)) {
-        kd[s] = load16(kc + (size_t)key * ROWB + ds * 16);
-        vd[s] = load16(vc + (size_t)key * ROWB + ds * 16);
+        kd[s] = load16(ks + (size_t)key * ROWB + ds * 16);
+        vd[s] = load16(vs + (size_t)key * ROWB + ds * 16);
       }
     }
   };
@@ -105,8 +120,8 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
       kA[s] = u32x4{0, 0, 0, 0};
       vA[s] = u32x4{0, 0, 0, 0};
       if (key < kend && (!FUSED || key < nb0)) {
-        kA[s] = load16(kc + (size_t)key * ROWB + ds * 16);
-        vA[s] = load16(vc + (size_t)key * ROWB + ds * 16);
+        kA[s] = load16(ks + (size_t)key * ROWB + ds * 16);
+        vA[s] = load16(vs + (size_t)key * ROWB + ds * 16);
       }
     }
   };
@@ -256,6 +271,18 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
     // the same tile step written out on the one buffer (the compiler
     // schedules this form better than the step above called through pointers)
     while (t0 < kend) {
+      if constexpr (BEAM) {  // the parent's cached rows into this beam's rows
+        if (rt == 0) {
+#pragma unroll
+          for (int s = 0; s < kSteps; ++s) {
+            const int key = t0 + s * RPL + kr;
+            if (key < kend && key < nb0) {
+              store16(kc + (size_t)key * ROWB + ds * 16, kA[s]);
+              store16(vc + (size_t)key * ROWB + ds * 16, vA[s]);
+            }
+          }
+        }
+      }
       if constexpr (FUSED) {
 #pragma unroll
         for (int s = 0; s < kSteps; ++s) {
@@ -369,32 +396,38 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
   merge_splits<GM>(a, tile_id, g0, gcount, bkv, hk);
 }
 
-template <int DT, bool FUSED, bool ROPE, bool RAGGED>
+template <int DT, bool FUSED, bool ROPE, bool RAGGED, bool BEAM>
 void launch_gm(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
   switch (a.gm) {
-    case 1: launch_kernel(attn_kernel<DT, 1, FUSED, 4, ROPE, RAGGED>, grid, block, s, a); break;
-    case 2: launch_kernel(attn_kernel<DT, 2, FUSED, 4, ROPE, RAGGED>, grid, block, s, a); break;
-    case 4: launch_kernel(attn_kernel<DT, 4, FUSED, 4, ROPE, RAGGED>, grid, block, s, a); break;
-    default: launch_kernel(attn_kernel<DT, 8, FUSED, 4, ROPE, RAGGED>, grid, block, s, a); break;
+    case 1: launch_kernel(attn_kernel<DT, 1, FUSED, 4, ROPE, RAGGED, BEAM>, grid, block, s, a); break;
+    case 2: launch_kernel(attn_kernel<DT, 2, FUSED, 4, ROPE, RAGGED, BEAM>, grid, block, s, a); break;
+    case 4: launch_kernel(attn_kernel<DT, 4, FUSED, 4, ROPE, RAGGED, BEAM>, grid, block, s, a); break;
+    default: launch_kernel(attn_kernel<DT, 8, FUSED, 4, ROPE, RAGGED, BEAM>, grid, block, s, a); break;
   }
 }
 
 // The 16-wave variant (one wide workgroup per unit): one query row and no
 // rotary work, so that it fits 128 registers without spilling.
-template <int DT, bool FUSED, bool RAGGED>
+template <int DT, bool FUSED, bool RAGGED, bool BEAM>
 void launch_wide(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
-  launch_kernel(attn_kernel<DT, 1, FUSED, kMaxWaves, false, RAGGED>, grid, block, s, a);
+  launch_kernel(attn_kernel<DT, 1, FUSED, kMaxWaves, false, RAGGED, BEAM>, grid, block, s, a);
 }
 
-template <int DT, bool FUSED, bool RAGGED>
+template <int DT, bool FUSED, bool RAGGED, bool BEAM = false>
 void launch_rg(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
-  if (a.waves > 4) launch_wide<DT, FUSED, RAGGED>(a, grid, block, s);
-  else if (a.rope_base > 0.f) launch_gm<DT, FUSED, true, RAGGED>(a, grid, block, s);
-  else launch_gm<DT, FUSED, false, RAGGED>(a, grid, block, s);
+  if (a.waves > 4) launch_wide<DT, FUSED, RAGGED, BEAM>(a, grid, block, s);
+  else if (a.rope_base > 0.f) launch_gm<DT, FUSED, true, RAGGED, BEAM>(a, grid, block, s);
+  else launch_gm<DT, FUSED, false, RAGGED, BEAM>(a, grid, block, s);
 }
 
 template <int DT, bool FUSED>
 void launch_dt(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
+  if constexpr (FUSED) {
+    if (a.parent) {  // beam step (equal lengths)
+      launch_rg<DT, true, false, true>(a, grid, block, s);
+      return;
+    }
+  }
   if (a.lens) launch_rg<DT, FUSED, true>(a, grid, block, s);
   else launch_rg<DT, FUSED, false>(a, grid, block, s);
 }
@@ -475,13 +508,14 @@ hipError_t launch_attn(int dtype, const AttnArgs &a, hipStream_t s) {
 // 64 KB), which avoids the cross-workgroup merge (two memory round trips:
 // the arrival count, then the partials); beyond that the keys are split into
 // chunks of at least 32 KB and at most 8 splits.
-AttnPlan plan_attn(int dtype, int units, int G, int N, int L, bool rope) {
+AttnPlan plan_attn(int dtype, int units, int G, int N, int L, bool rope, bool allow_mfma) {
   AttnPlan p{};
   // Matrix-core tiles for several query rows per KV head: N > 1 queries, or
   // G >= 3 rows from grouped heads or beams sharing one cache (measured: 3
   // GQA rows 12% and 5 beam rows 31% faster per decode step than 4- and 8-row
   // streaming tiles; 2 rows stay on the streaming kernel).
-  const bool use_mfma = dtype != F32 && (N > 1 || G >= 3) && env_int("KVD_ATTN_MFMA", 1) != 0;
+  const bool use_mfma =
+      allow_mfma && dtype != F32 && (N > 1 || G >= 3) && env_int("KVD_ATTN_MFMA", 1) != 0;
   if (use_mfma) return plan_attn_mfma(units, G, L);
   p.gm = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
   p.row_tiles = (G + p.gm - 1) / p.gm;

@@ -46,7 +46,7 @@ __device__ __forceinline__ RowSpan row_span(const AttnArgs &a, int bkv) {
   if constexpr (RAGGED) {
     const int len = a.lens[bkv];
     const int c = min(max(len, a.N), a.L);
-    if (c != len && a.dev_status && threadIdx.x == 0) *a.dev_status = -4;  // KVD_ERR_CAPACITY
+    if (c != len && a.dev_status && threadIdx.x == 0) *a.dev_status = kStatusCapacity;
     s.L = c;
     s.causal_base = c - a.N;
     if (a.new_base != INT_MAX) s.new_base = c - a.T_new;

@@ -8,8 +8,6 @@ namespace kvd {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kStatusBadShape = -2;  // KVD_ERR_SHAPE
-constexpr int kStatusCapacity = -4;  // KVD_ERR_CAPACITY
 constexpr int kMaxBeams = 16;
 
 // Thread (row, j) moves rotary pair j of one new row; rows are ordered

@@ -13,6 +13,11 @@ enum DType { F32 = 0, F16 = 1, BF16 = 2 };  // same values as enum kvd_dtype
 
 constexpr int kHeadDim = 64;
 
+// Status values kernels store in a caller's dev_status word (the values of
+// KVD_ERR_SHAPE and KVD_ERR_CAPACITY).
+constexpr int kStatusBadShape = -2;
+constexpr int kStatusCapacity = -4;
+
 // Arrival counters at the start of every workspace (one per merged tile).
 constexpr int kMaxCounters = 4096;
 // decode_step_self: new rows appended inside the attention launch (more are
@@ -59,6 +64,8 @@ struct AttnArgs {
   const int32_t *lens;           // [Bkv] per-row len (ragged self attention; L is then the
                                  // planned maximum), or null
   int32_t *dev_status;           // a len outside [N, L] is clamped and flagged here, or null
+  const void *k_src, *v_src;     // beam step: cached rows are read from beam parent[b] here
+  const int32_t *parent;         // [Bkv] beam step parents (k, v are then the destination), or null
   float scale_log2;              // scale * log2(e)
   float rope_base;               // > 0: rotate q at causal_base + i (and new keys)
   double rope_step;              // 2 log2(rope_base) / D (0: no rotation)
@@ -93,7 +100,7 @@ struct AttnPlan {
   int gm, row_tiles, chunk, splits, waves, mfma, rw;
   size_t part_floats, counters;
 };
-AttnPlan plan_attn(int dtype, int units, int G, int N, int L, bool rope);
+AttnPlan plan_attn(int dtype, int units, int G, int N, int L, bool rope, bool allow_mfma = true);
 
 void plan_verify(int B, int R, int V, int &chunk, int &chunks);
 

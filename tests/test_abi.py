@@ -58,6 +58,38 @@ def test_kv_append_validation(lib):
     assert f(ctypes.byref(_cache(k=MIS)), FAKE, FAKE, 0, 1, 0.0, None) == -7
 
 
+def test_beam_step_validation(lib):
+    big = 1 << 30
+    src = _cache(B=5)
+    dst = _cache(B=5, k=0x1000000, v=0x2000000)   # storage 5*20*448*128 B = 5.7 MB apart
+    far = _cache(B=5, k=0x4000000, v=0x5000000)
+    f = lib.decode_step_self_beams
+
+    def call(q=FAKE, kn=FAKE, vn=FAKE, Hq=20, N=1, s=src, d=dst, par=FAKE, L=100, ws_bytes=big,
+             st=None):
+        return f(q, kn, vn, Hq, N, ctypes.byref(s), ctypes.byref(d), par, L, 0.125, 0.0, FAKE,
+                 FAKE, ws_bytes, st, None)
+    assert f(FAKE, FAKE, FAKE, 20, 1, None, ctypes.byref(dst), FAKE, 100, 0.125, 0.0, FAKE, FAKE,
+             big, None, None) == -1
+    assert call(par=None) == -1
+    assert call(kn=None) == -1
+    assert call(q=None) == -1
+    assert call(d=_cache(B=5, k=0x1000000, v=0x2000000, dtype=kb.BF16)) == -3   # dtypes differ
+    assert call(d=_cache(B=4, k=0x1000000, v=0x2000000)) == -2                 # B differs
+    assert call(d=_cache(B=5, S=447, k=0x1000000, v=0x2000000)) == -2          # S_max differs
+    assert call(N=17) == -2
+    assert call(d=src) == -2                                                   # same storage
+    assert call(s=dst, d=_cache(B=5, k=0x1000000 + 5 * 20 * 448 * 128 - 16, v=0x6000000)) == -2
+    assert call(s=far, d=_cache(B=5, k=0x6000000, v=0x4000000 + 4096)) == -2  # dst.v inside src.k
+    assert call(par=FAKE + 2) == -7
+    assert call(st=FAKE + 1) == -7
+    assert call(L=0) == -4
+    assert call(L=449) == -4
+    assert call(N=5, L=4) == -4
+    assert call(Hq=21) == -2
+    assert call(L=448, ws_bytes=0) == -6      # 5 x 20 heads of 448 rows: split keys
+
+
 def test_ragged_validation(lib):
     c = ctypes.byref(_cache(B=4))
     big = 1 << 30

@@ -747,6 +747,153 @@ def test_step_self_equals_append_then_attend(dtype, B, Hq, Hkv, N, L, rope, plan
     assert max_err(o2, O.attend_self(q, oc, 0.125, rope_base=rope)) <= TOL[dtype]
 
 
+# ------------------------------------------ fused beam step (two caches) ----
+
+@pytest.mark.parametrize("dtype,B,Hq,Hkv,N,L,rope", [
+    ("f16", 5, 20, 20, 1, 1, 0.0),          # first token: nothing to copy
+    ("f16", 5, 20, 20, 1, 2, 0.0),
+    ("f16", 5, 20, 20, 1, 300, 0.0),        # whisper beam step (split keys)
+    ("f16", 5, 20, 20, 1, 448, 0.0),        # full cache
+    ("bf16", 16, 20, 20, 1, 77, 0.0),       # 16 beams
+    ("bf16", 4, 9, 3, 1, 700, 10000.0),     # grouped heads, rotary keys
+    ("bf16", 3, 9, 3, 16, 530, 10000.0),    # largest fused block
+    ("f16", 2, 8, 2, 5, 133, 0.0),          # draft block across a split boundary
+    ("f32", 3, 4, 4, 3, 70, 10000.0),
+    ("f32", 2, 4, 2, 1, 1100, 0.0),
+])
+def test_beam_step_equals_reorder_then_step(dtype, B, Hq, Hkv, N, L, rope, plan, monkeypatch):
+    """decode_step_self_beams(src -> dst) leaves dst exactly as a copy of
+    src, kv_reorder and decode_step_self would (rows from L on untouched),
+    leaves src as it was, returns the same output bit for bit on the same
+    (streaming) plan, and matches the oracle."""
+    say(f"case: beam step {dtype} B={B} Hq={Hq} Hkv={Hkv} N={N} L={L} rope={rope} plan={plan}")
+    monkeypatch.setenv("KVD_ATTN_MFMA", "0")   # the composition on the beam step's kernel
+    g = np.random.default_rng(L * 11 + N + B)
+    S = L + 5
+    old, new = slice(0, L - N), slice(L - N, L)
+    src_k = O.narrow(g.standard_normal((B, Hkv, S, 64)), dtype)
+    src_v = O.narrow(g.standard_normal((B, Hkv, S, 64)), dtype)
+    dst_k = O.narrow(g.standard_normal((B, Hkv, S, 64)), dtype)   # stale rows of an older step
+    dst_v = O.narrow(g.standard_normal((B, Hkv, S, 64)), dtype)
+    k_new = O.narrow(g.standard_normal((B, Hkv, N, 64)), dtype)
+    v_new = O.narrow(g.standard_normal((B, Hkv, N, 64)), dtype)
+    q = O.narrow(g.standard_normal((B, Hq, N, 64)), dtype)
+    par = g.integers(0, B, size=B).astype(np.int32)
+    par[0] = B - 1
+    pd = torch.from_numpy(par).cuda()
+    src = kb.Cache.wrap(to_dev(src_k, dtype), to_dev(src_v, dtype))
+    dst = kb.Cache.wrap(to_dev(dst_k, dtype), to_dev(dst_v, dtype))
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    o_beam = kb.decode_step_self_beams(to_dev(q, dtype), to_dev(k_new, dtype), to_dev(v_new, dtype),
+                                       src, dst, pd, L, 0.125, rope_base=rope,
+                                       dev_status=status)
+    # the same step as reorder in place + fused step on a copy of src
+    ref = kb.Cache.wrap(to_dev(src_k, dtype), to_dev(src_v, dtype))
+    kb.kv_reorder(ref, pd, L - N)
+    o_ref = kb.decode_step_self(to_dev(q, dtype), to_dev(k_new, dtype), to_dev(v_new, dtype), ref,
+                                L, 0.125, rope_base=rope)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    gk, gv = from_dev(dst.k, dtype), from_dev(dst.v, dtype)
+    rk, rv = from_dev(ref.k, dtype), from_dev(ref.v, dtype)
+    assert np.array_equal(bits(gk[:, :, :L]), bits(rk[:, :, :L]))
+    assert np.array_equal(bits(gv[:, :, :L]), bits(rv[:, :, :L]))
+    assert np.array_equal(bits(gk[:, :, L:]), bits(dst_k[:, :, L:]))     # rows past L untouched
+    assert np.array_equal(bits(gv[:, :, L:]), bits(dst_v[:, :, L:]))
+    assert np.array_equal(bits(from_dev(src.k, dtype)), bits(src_k))     # src only read
+    assert np.array_equal(bits(from_dev(src.v, dtype)), bits(src_v))
+    assert torch.equal(o_beam, o_ref)
+    # the oracle: the parents' rows, then the append, then attention
+    oc = O.ConcatCache(B, Hkv, 64, dtype)
+    if L > N:
+        oc.set_once(O.reorder(src_k[:, :, old], par), O.reorder(src_v[:, :, old], par))
+    oc.append(k_new, v_new, rope)
+    assert np.array_equal(bits(gk[:, :, old]), bits(oc.k[:, :, old]))   # copied rows
+    assert np.array_equal(bits(gv[:, :, :L]), bits(oc.v))
+    if rope > 0:   # rotated in fp32 by the kernel, in fp64 by the oracle
+        assert _rotated_rows_close(gk[:, :, new], oc.k[:, :, new], k_new, dtype)
+    else:
+        assert np.array_equal(bits(gk[:, :, new]), bits(oc.k[:, :, new]))
+    assert max_err(o_beam, O.attend_self(q, oc, 0.125, rope_base=rope)) <= TOL[dtype]
+
+
+def _rotated_rows_close(gpu, ref, raw, dtype):
+    """Keys rotated by the kernel (fp32 rotation, rounded to nearest) against
+    the oracle's (fp64, rounded): one step of the storage type apart at most,
+    plus the fp32 error of lo*c - hi*s where the two terms cancel."""
+    mant = {"f32": 23, "f16": 10, "bf16": 7}[dtype]
+    g, r, x = O.widen(gpu, dtype), O.widen(ref, dtype), np.abs(O.widen(raw, dtype))
+    half = x.shape[-1] // 2
+    pair = np.concatenate([x[..., :half] + x[..., half:]] * 2, axis=-1)
+    ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(r), 1e-38))[1] - 1 - mant)
+    return bool(np.all(np.abs(g - r) <= ulp + pair * 2.0 ** -20))
+
+
+def test_beam_step_bad_parent_reads_own_rows():
+    say("case: beam step with parents outside [0, B)")
+    dtype, B, H, S, L = "f16", 4, 20, 64, 40
+    g = np.random.default_rng(5)
+    src_k = O.narrow(g.standard_normal((B, H, S, 64)), dtype)
+    src_v = O.narrow(g.standard_normal((B, H, S, 64)), dtype)
+    k_new = O.narrow(g.standard_normal((B, H, 1, 64)), dtype)
+    v_new = O.narrow(g.standard_normal((B, H, 1, 64)), dtype)
+    q = O.narrow(g.standard_normal((B, H, 1, 64)), dtype)
+    par = np.array([2, -1, 4, 0], dtype=np.int32)
+    src = kb.Cache.wrap(to_dev(src_k, dtype), to_dev(src_v, dtype))
+    dst = kb.Cache(B, H, S, torch.float16)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = kb.decode_step_self_beams(to_dev(q, dtype), to_dev(k_new, dtype), to_dev(v_new, dtype),
+                                    src, dst, torch.from_numpy(par).cuda(), L, 0.125,
+                                    dev_status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == -2
+    eff = np.array([2, 1, 2, 0], dtype=np.int32)   # invalid parents: the beam's own rows
+    oc = O.ConcatCache(B, H, 64, dtype)
+    oc.set_once(O.reorder(src_k[:, :, :L - 1], eff), O.reorder(src_v[:, :, :L - 1], eff))
+    oc.append(k_new, v_new)
+    assert np.array_equal(bits(from_dev(dst.k, dtype)[:, :, :L]), bits(oc.k))
+    assert np.array_equal(bits(from_dev(dst.v, dtype)[:, :, :L]), bits(oc.v))
+    assert max_err(out, O.attend_self(q, oc, 0.125)) <= TOL[dtype]
+
+
+def test_beam_step_ping_pong_whisper():
+    """Beam search over 96 steps of two whisper layers (5 beams, 20 heads,
+    fp16) with the caches used in turn: at each step the parents of the
+    step's beams are read from one cache and written into the other with the
+    new row. Caches and attention are checked against the oracle's reorder +
+    append + attention along the way."""
+    w = I.WHISPER_BEAM
+    say("case: beam step ping-pong, 5 beams, 96 steps, two layers")
+    steps = 96
+    ws = _ws()
+    worst = 0.0
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for l in (0, 1):
+        pair = [kb.Cache(5, 20, 448, torch.float16), kb.Cache(5, 20, 448, torch.float16)]
+        oc = O.ConcatCache(5, 20, 64, "f16")
+        k_all, v_all = I.self_kv(w, l)
+        kd, vd = to_dev(k_all, "f16"), to_dev(v_all, "f16")
+        for s in range(steps):
+            par = I.parents(w, s) if s > 0 else np.arange(5, dtype=np.int32)
+            src, dst = pair[s % 2], pair[(s + 1) % 2]
+            q = I.queries(w, l, s)
+            o = kb.decode_step_self_beams(to_dev(q, "f16"), kd[:, :, s:s + 1].contiguous(),
+                                          vd[:, :, s:s + 1].contiguous(), src, dst,
+                                          torch.from_numpy(par).cuda(), s + 1, w.attn_scale,
+                                          ws=ws, dev_status=status)
+            if s > 0:
+                oc.reorder(par)
+            oc.append(k_all[:, :, s:s + 1], v_all[:, :, s:s + 1])
+            if s % 8 == 7 or s < 3:
+                e = max_err(o, O.attend_self(q, oc, w.attn_scale))
+                worst = max(worst, e)
+                assert e <= TOL["f16"], (l, s, e)
+                assert np.array_equal(bits(from_dev(dst.k, "f16")[:, :, :s + 1]), bits(oc.k))
+                assert np.array_equal(bits(from_dev(dst.v, "f16")[:, :, :s + 1]), bits(oc.v))
+    assert int(status.item()) == 0
+    say(f"beam ping-pong: worst max|err| {worst:.2e}")
+
+
 def test_read_probe_reads_every_vector():
     """kvd_read_probe: a buffer whose only nonzero 16-byte vector folds to the
     probe's marker makes it store that word; an all-zero buffer stores nothing."""
