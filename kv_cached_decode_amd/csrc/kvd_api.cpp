@@ -48,7 +48,7 @@ double rope_step_of(float rope_base) {
 // (each kernel that counts arrivals sets its counters back to zero), so one
 // workspace can serve calls with different plans: partial results of one call
 // never land where another call keeps a counter.
-constexpr size_t kCounterBytes = kvd::kMaxCounters * sizeof(uint32_t);
+constexpr size_t kCounterBytes = (size_t)kvd::kMaxCounters * kvd::kCounterStride * sizeof(uint32_t);
 
 size_t attn_bytes(const AttnPlan &p) { return kCounterBytes + p.part_floats * sizeof(float); }
 

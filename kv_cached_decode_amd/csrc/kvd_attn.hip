@@ -47,7 +47,9 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
   constexpr int VPR = ROWB / 16;  // 16-byte vectors per row
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave-uniform values kept in scalar registers, so that the key loop and
+  // its tests are scalar branches and not per-lane masks
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
   const int kr = lane / LPR;  // key row within a wave load
   const int ds = lane % LPR;  // dims [ds*VE, ds*VE + VE)
@@ -93,7 +95,7 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
       kvis = max(kvis, lim[g]);
     }
   }
-  const int kend = min(kspan, kvis);
+  const int kend = __builtin_amdgcn_readfirstlane(min(kspan, kvis));
 
   // ---- first tiles of cached keys: in flight before anything else waits.
   // Without new rows, with few query rows and 4 waves (registers to spare;
@@ -101,30 +103,32 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
   // i + 2 is loaded into the buffer tile i just freed.
   constexpr int PF = (!FUSED && GM <= 2 && NWMAX <= 4) ? 2 : 1;
   u32x4 kA[kSteps], vA[kSteps], kB[PF == 2 ? kSteps : 1], vB[PF == 2 ? kSteps : 1];
+  // A whole tile of cached keys: plain loads from a uniform base plus 32-bit
+  // lane offsets. A tile reaching past kend or into the new rows loads its
+  // keys clamped to the last cached one (row 0 if there is none), again with
+  // no branch and no zeroed register in front of a load (either would cost
+  // instructions and make the compiler wait for earlier loads). Past kend the
+  // scores are masked; the values there are rows below kend, so finite,
+  // except with new rows (see the fused loop).
+  const int kcap = max((FUSED ? min(kend, nb0) : kend) - 1, 0);
+  auto whole = [&](int t) { return t + TILE <= kend && (!FUSED || t + TILE <= nb0); };
   auto load_tile = [&](u32x4 *kd, u32x4 *vd, int t) {
+    // one code path for both kinds of tile (a branch between two sets of
+    // loads makes the compiler wait on the other set's registers); the base
+    // and the clamp are scalar selects
+    const bool full = whole(t);
+    const int kbase = full ? t : min(t, kcap);
+    const int klast = full ? t + TILE - 1 : kcap;
+    const char *kb = ks + (size_t)kbase * ROWB;
+    const char *vb = vs + (size_t)kbase * ROWB;
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
-      const int key = t + s * RPL + kr;
-      kd[s] = u32x4{0, 0, 0, 0};
-      vd[s] = u32x4{0, 0, 0, 0};
-      if (key < kend && (!FUSED || key < nb0)) {
-        kd[s] = load16(ks + (size_t)key * ROWB + ds * 16);
-        vd[s] = load16(vs + (size_t)key * ROWB + ds * 16);
-      }
+      const uint32_t off = (uint32_t)(min(t + s * RPL + kr, klast) - kbase) * ROWB + ds * 16;
+      kd[s] = load16(kb + off);
+      vd[s] = load16(vb + off);
     }
   };
-  auto load_a = [&](int t) {  // the same into (kA, vA), written out
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      const int key = t + s * RPL + kr;
-      kA[s] = u32x4{0, 0, 0, 0};
-      vA[s] = u32x4{0, 0, 0, 0};
-      if (key < kend && (!FUSED || key < nb0)) {
-        kA[s] = load16(ks + (size_t)key * ROWB + ds * 16);
-        vA[s] = load16(vs + (size_t)key * ROWB + ds * 16);
-      }
-    }
-  };
+  auto load_a = [&](int t) { load_tile(kA, vA, t); };
   const int stride = nw * TILE;
   int t0 = k0 + wave * TILE;
   if constexpr (PF == 2) {  // (each form measured fastest for its kernels)
@@ -213,18 +217,29 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
     for (int e = 0; e < VE; ++e) o[g][e] = 0.f;
   }
 
-  // one tile: the keys [t0, t0 + TILE) of this wave, held in (kv, vv)
-  auto step = [&](u32x4 *kv, u32x4 *vv) {
-    if constexpr (FUSED) {  // new rows of this tile come from LDS
+  // The new rows of the tile at t0 replace its loaded chunks, from LDS: a
+  // uniform test per tile, then reads at clamped rows and a select per lane
+  // (no branch around a read)
+  auto overlay_new = [&](u32x4 *kv, u32x4 *vv) {
+    if (t0 + TILE > nb0) {
 #pragma unroll
       for (int s = 0; s < kSteps; ++s) {
         const int key = t0 + s * RPL + kr;
-        if (key < kend && key >= nb0) {
-          kv[s] = s_new[(key - nb0) * VPR + ds];
-          vv[s] = s_new[(kMaxFusedRows + key - nb0) * VPR + ds];
+        const int r = min(max(key - nb0, 0), kMaxFusedRows - 1);
+        const u32x4 kn = s_new[r * VPR + ds], vn = s_new[(kMaxFusedRows + r) * VPR + ds];
+        const bool fresh = key < kend && key >= nb0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          kv[s][i] = fresh ? kn[i] : kv[s][i];
+          vv[s][i] = fresh ? vn[i] : vv[s][i];
         }
       }
     }
+  };
+
+  // one tile: the keys [t0, t0 + TILE) of this wave, held in (kv, vv)
+  auto step = [&](u32x4 *kv, u32x4 *vv) {
+    if constexpr (FUSED) overlay_new(kv, vv);
     float sc[kSteps][GM];
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
@@ -246,9 +261,6 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
     float vf[kSteps][VE];
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) unpack16<DT>(vv[s], vf[s]);
-    // the buffer is free: the tile PF strides ahead goes in flight during
-    // this one's math
-    if (t0 + PF * stride < kend) load_tile(kv, vv, t0 + PF * stride);
 #pragma unroll
     for (int g = 0; g < GM; ++g) {
       float mt = sc[0][g];
@@ -259,6 +271,10 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
         for (int s = 0; s < kSteps; ++s) fn(sc[s][g], vf[s]);
       });
     }
+    // the buffer is free now (the conversions of the values fold into the
+    // P.V instructions, so it is read until here): the tile PF strides ahead
+    // goes out, PF - 1 tiles of math ahead of its use
+    if (t0 + PF * stride < kend) load_tile(kv, vv, t0 + PF * stride);
     t0 += stride;
   };
   if constexpr (PF == 2) {
@@ -271,6 +287,17 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
     // the same tile step written out on the one buffer (the compiler
     // schedules this form better than the step above called through pointers)
     while (t0 < kend) {
+      if constexpr (FUSED) {
+        // values past kend: p = 0 there must meet no Inf or NaN, and with
+        // new rows the clamped row may be one not written yet (a select per
+        // lane, no branch: a branch would cost register copies)
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+          const bool in = t0 + s * RPL + kr < kend;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vA[s][i] = in ? vA[s][i] : 0u;
+        }
+      }
       if constexpr (BEAM) {  // the parent's cached rows into this beam's rows
         if (rt == 0) {
 #pragma unroll
@@ -283,16 +310,7 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
           }
         }
       }
-      if constexpr (FUSED) {
-#pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-          const int key = t0 + s * RPL + kr;
-          if (key < kend && key >= nb0) {
-            kA[s] = s_new[(key - nb0) * VPR + ds];
-            vA[s] = s_new[(kMaxFusedRows + key - nb0) * VPR + ds];
-          }
-        }
-      }
+      if constexpr (FUSED) overlay_new(kA, vA);
       float sc[kSteps][GM];
 #pragma unroll
       for (int s = 0; s < kSteps; ++s) {
@@ -314,8 +332,6 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
       float vf[kSteps][VE];
 #pragma unroll
       for (int s = 0; s < kSteps; ++s) unpack16<DT>(vA[s], vf[s]);
-      t0 += stride;
-      if (t0 < kend) load_a(t0);
 #pragma unroll
       for (int g = 0; g < GM; ++g) {
         float mt = sc[0][g];
@@ -326,6 +342,9 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
           for (int s = 0; s < kSteps; ++s) fn(sc[s][g], vf[s]);
         });
       }
+      // the buffer is free now (see the two-tile form above)
+      t0 += stride;
+      if (t0 < kend) load_a(t0);
     }
   }
 

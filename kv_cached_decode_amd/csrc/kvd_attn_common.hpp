@@ -155,8 +155,9 @@ __device__ void merge_splits(const AttnArgs &a, size_t tile_id, int g0, int gcou
   wait_stores();
   __syncthreads();
   if (threadIdx.x == 0) {
-    const bool last = arrive(&a.ws_count[tile_id]) == (uint32_t)(a.splits - 1);
-    if (last) reset_counter(&a.ws_count[tile_id]);  // every split has arrived
+    uint32_t *counter = a.ws_count + tile_id * kCounterStride;
+    const bool last = arrive(counter) == (uint32_t)(a.splits - 1);
+    if (last) reset_counter(counter);  // every split has arrived
     s_last = last;
   }
   __syncthreads();

@@ -112,6 +112,42 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
   char *vc = static_cast<char *>(a.v) + head * a.S_max * ROWB;
   const int nb0 = max(k0, sp.new_base);
 
+  // ---- the wave's first step goes out before anything else is computed
+  // when every row of the tile sees all its keys (a causal row sees at least
+  // keys 0 .. causal_base) and none of them is new
+  const int kstride = NPH * kStep;
+  int s0 = k0 + phase * kStep;
+  u32x4 kA[2][2];
+  u32x2 vA[8];
+  // K: tile t, dims chunk kk -> key s + 16t + c, 16 bytes at dims 8gq + 32kk
+  // V: lane's 8 keys s + {4gq + j (j < 4), 16 + 4gq + j - 4}, bytes [8c, 8c + 8)
+  auto load_whole = [&](int s, u32x4 (&ka)[2][2], u32x2 (&vv)[8]) {
+    // a uniform base plus a per-lane 32-bit offset: scalar address math
+    const char *kb = kc + (size_t)s * ROWB;
+    const char *vb = vc + (size_t)s * ROWB;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        ka[t][kk] = load16(kb + (uint32_t)((16 * t + c) * ROWB + gq * 16 + kk * 64));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int kr = (j < 4) ? 4 * gq + j : 16 + 4 * gq + j - 4;
+      vv[j] = *reinterpret_cast<const u32x2 *>(vb + (uint32_t)(kr * ROWB + c * 8));
+    }
+  };
+  // only the waves whose steps hold new rows take them; the one holding the
+  // first of them writes them into the cache
+  bool takes_new = false, store_new = false;
+  if (FUSED && kspan > nb0) {
+    const int st0 = (nb0 - k0) / kStep, st1 = (kspan - 1 - k0) / kStep;
+    takes_new = st0 % NPH == phase || st1 % NPH == phase;
+    store_new = rt == 0 && st0 % NPH == phase;
+  }
+  const int kend_lo = min(kspan, (sp.causal_base < 0) ? sp.L : sp.causal_base + 1);
+  const bool early = s0 + kStep <= kend_lo && (!FUSED || s0 + kStep <= nb0);  // uniform
+  if (early) load_whole(s0, kA, vA);
+
   // ---- this lane's query row and the keys it sees
   const int grow = rt * kRows + c;
   const bool active = grow < a.G;
@@ -132,100 +168,92 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
     qraw[1] = load16(qrow + 64 + gq * 16);
   }
 
-  // ---- rotary cos / sin of the query row's pairs: no memory access, so
-  // they are computed while the loads above are in flight
-  float qc[ROPE ? 8 : 1], qs[ROPE ? 8 : 1];
-  if constexpr (ROPE)
-    rope_cos_sin_run<8>(sp.causal_base + r.i, gq * 8, RopeStep{a.rope_step, a.rope_ratio}, qc, qs);
-
-  // ---- fused append (as in the streaming kernel)
-  __shared__ u32x4 s_new[FUSED ? 2 * kMaxFusedRows * VPR : 1];
-  if constexpr (FUSED) {
-    constexpr int HALF_VECS = kHeadDim / 2 / 8;
-    const char *kn = static_cast<const char *>(a.k_new) + head * a.T_new * ROWB;
-    const char *vn = static_cast<const char *>(a.v_new) + head * a.T_new * ROWB;
-    const int n = (kspan - nb0) * HALF_VECS;
-    for (int t = threadIdx.x; t < n; t += blockDim.x) {
-      const int rr = t / HALF_VECS, j = t % HALF_VECS;
-      const int pos = nb0 + rr;
-      const size_t src = (size_t)(pos - sp.new_base) * ROWB;
-      const PairChunks ch = load_pair<DT>(kn + src, vn + src, j, pos, RopeStep{ROPE ? a.rope_step : 0.0, a.rope_ratio});
-      s_new[rr * VPR + j] = ch.klo;
-      s_new[rr * VPR + j + VPR / 2] = ch.khi;
-      s_new[(kMaxFusedRows + rr) * VPR + j] = ch.vlo;
-      s_new[(kMaxFusedRows + rr) * VPR + j + VPR / 2] = ch.vhi;
-      if (blockIdx.y == 0) store_pair<DT>(kc + (size_t)pos * ROWB, vc + (size_t)pos * ROWB, j, ch);
-    }
-    __syncthreads();
-  }
-
-  u32x4 qhi[2], qlo[2];
-  if constexpr (ROPE) {
-    float x0[8], x1[8];
-    unpack16<DT>(qraw[0], x0);
-    unpack16<DT>(qraw[1], x1);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) rope_rotate(x0[e], x1[e], qc[e], qs[e]);
-    split_hi_lo<DT>(x0, qhi[0], qlo[0]);
-    split_hi_lo<DT>(x1, qhi[1], qlo[1]);
-  } else {
-    qhi[0] = qraw[0];
-    qhi[1] = qraw[1];
-    qlo[0] = qlo[1] = u32x4{0, 0, 0, 0};
-  }
-
   float m = -INFINITY, lsum = 0.f;
   f32x4 o[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 qhi[2], qlo[2];  // the query operand, set once the q loads are back
+
+  // ---- new rows (decode_step_self): a wave that needs them loads them,
+  // rotates them (exactly as kv_append does) while its key loads are in
+  // flight, and keeps them in its own slice of LDS, so no barrier is needed.
+  // Lane l takes chunk pair l % 4 of new row l / 4 (N <= 16 rows: one each).
+  constexpr int kNewSlice = 2 * kMaxFusedRows * VPR;  // K rows, then V rows
+  __shared__ u32x4 s_new[FUSED ? kWaves * kNewSlice : 1];
+  u32x4 *my_new = s_new + (FUSED ? wave * kNewSlice : 0);
+  const int new_items = takes_new ? (kspan - nb0) * (VPR / 2) : 0;  // uniform
+  PairChunks nw{};
+  if constexpr (FUSED) {
+    if (lane < new_items) {
+      const char *krow = static_cast<const char *>(a.k_new) +
+                         (head * a.T_new + (nb0 - sp.new_base) + lane / 4) * ROWB;
+      const char *vrow = static_cast<const char *>(a.v_new) +
+                         (head * a.T_new + (nb0 - sp.new_base) + lane / 4) * ROWB;
+      const int j = lane % 4;
+      nw.klo = load16(krow + j * 16);
+      nw.khi = load16(krow + 64 + j * 16);
+      nw.vlo = load16(vrow + j * 16);
+      nw.vhi = load16(vrow + 64 + j * 16);
+    }
+  }
 
   // One 32-key step: its loads, then its scores, softmax update and P.V.
   auto load_step = [&](int s0, u32x4 (&ka)[2][2], u32x2 (&vv)[8]) {
     // K: tile t, dims chunk kk -> key s0 + 16t + c, 16 bytes at dims 8gq + 32kk
     // V: lane's 8 keys s0 + {4gq + j (j < 4), 16 + 4gq + j - 4}, bytes [8c, 8c + 8)
     if (s0 + kStep <= kend && (!FUSED || s0 + kStep <= nb0)) {  // whole step cached
-      // a uniform base plus a per-lane 32-bit offset: scalar address math
-      const char *kb = kc + (size_t)s0 * ROWB;
-      const char *vb = vc + (size_t)s0 * ROWB;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-          ka[t][kk] = load16(kb + (uint32_t)((16 * t + c) * ROWB + gq * 16 + kk * 64));
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int kr = (j < 4) ? 4 * gq + j : 16 + 4 * gq + j - 4;
-        vv[j] = *reinterpret_cast<const u32x2 *>(vb + (uint32_t)(kr * ROWB + c * 8));
-      }
+      load_whole(s0, ka, vv);
       return;
     }
+    // Part of the step lies past kend or holds new rows. Every lane still
+    // loads, its key clamped to the step's last cached key (row 0 if there is
+    // none), so these are plain loads like the ones above: a masked load
+    // behind a zeroed register would make the compiler wait for earlier loads
+    // first. compute_step replaces or masks what lies outside.
+    const int kcap = max(FUSED ? min(kend, nb0) - 1 : kend - 1, 0);
+    const int kbase = min(s0, kcap);  // uniform; offsets from it are in [0, 32 rows)
+    const char *kb = kc + (size_t)kbase * ROWB;
+    const char *vb = vc + (size_t)kbase * ROWB;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int key = s0 + 16 * t + c;
+      const uint32_t row = (uint32_t)(min(s0 + 16 * t + c, kcap) - kbase) * ROWB;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        ka[t][kk] = u32x4{0, 0, 0, 0};
-        if (key < kend) {
-          if (FUSED && key >= nb0) ka[t][kk] = s_new[(key - nb0) * VPR + gq + 4 * kk];
-          else ka[t][kk] = load16(kc + (size_t)key * ROWB + gq * 16 + kk * 64);
-        }
-      }
+      for (int kk = 0; kk < 2; ++kk) ka[t][kk] = load16(kb + row + gq * 16 + kk * 64);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int key = s0 + ((j < 4) ? 4 * gq + j : 16 + 4 * gq + j - 4);
-      vv[j] = u32x2{0, 0};
-      if (key < kend) {
-        if (FUSED && key >= nb0) {
-          const u32x4 row = s_new[(kMaxFusedRows + key - nb0) * VPR + c / 2];
-          vv[j] = (c & 1) ? u32x2{row[2], row[3]} : u32x2{row[0], row[1]};
-        } else {
-          vv[j] = *reinterpret_cast<const u32x2 *>(vc + (size_t)key * ROWB + c * 8);
+      vv[j] = *reinterpret_cast<const u32x2 *>(vb + (uint32_t)(min(key, kcap) - kbase) * ROWB + c * 8);
+    }
+  };
+  auto compute_step = [&](int s0, u32x4 (&ka)[2][2], u32x2 (&vv)[8]) {
+    if (!(s0 + kStep <= kend && (!FUSED || s0 + kStep <= nb0))) {  // uniform
+      // keys past kend: their scores are masked below, and their values are
+      // zeroed so that p = 0 meets no Inf or NaN of an unwritten row
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int key = s0 + ((j < 4) ? 4 * gq + j : 16 + 4 * gq + j - 4);
+        if (key >= kend) vv[j] = u32x2{0, 0};
+      }
+      if constexpr (FUSED) {  // the step's new rows come from the wave's LDS slice
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int key = s0 + 16 * t + c;
+          if (key < kend && key >= nb0) {
+            ka[t][0] = my_new[(key - nb0) * VPR + gq];
+            ka[t][1] = my_new[(key - nb0) * VPR + gq + VPR / 2];
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int key = s0 + ((j < 4) ? 4 * gq + j : 16 + 4 * gq + j - 4);
+          if (key < kend && key >= nb0) {
+            const u32x4 row = my_new[(kMaxFusedRows + key - nb0) * VPR + c / 2];
+            vv[j] = (c & 1) ? u32x2{row[2], row[3]} : u32x2{row[0], row[1]};
+          }
         }
       }
     }
-  };
-  auto compute_step = [&](int s0, const u32x4 (&ka)[2][2], const u32x2 (&vv)[8]) {
     // scores S^T: st[t][i] = q_row . k_(s0 + 16t + 4gq + i)
     f32x4 st[2];
 #pragma unroll
@@ -288,15 +316,59 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
       o[t] = mfma<DT>(va[t], plo, o[t]);
     }
   };
-  const int kstride = NPH * kStep;
-  int s0 = k0 + phase * kStep;
+
+  // ---- otherwise the wave's first step goes out now
+  if (!early && s0 < kend) load_step(s0, kA, vA);
+
+  // ---- cos / sin of the new rows' keys and of the query row: no memory
+  // access, so they are all computed while the loads above are in flight (the
+  // scheduling barrier keeps the compiler from moving the first use of a
+  // loaded value, and so the wait for it, in between)
+  float ncs[ROPE && FUSED ? 8 : 1], nsn[ROPE && FUSED ? 8 : 1];
+  float qc[ROPE ? 8 : 1], qs[ROPE ? 8 : 1];
+  if constexpr (ROPE && FUSED) {
+    if (lane < new_items)
+      rope_cos_sin_run<8>(nb0 + lane / 4, (lane % 4) * 8, RopeStep{a.rope_step, a.rope_ratio}, ncs, nsn);
+  }
+  if constexpr (ROPE)
+    rope_cos_sin_run<8>(sp.causal_base + r.i, gq * 8, RopeStep{a.rope_step, a.rope_ratio}, qc, qs);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- the new rows, rotated (as kv_append rotates them) into the wave's slice
+  if constexpr (FUSED) {
+    if (lane < new_items) {
+      const int rr = lane / 4, j = lane % 4, pos = nb0 + rr;
+      if constexpr (ROPE) rotate_key_pair_cs<DT>(nw.klo, nw.khi, ncs, nsn);
+      my_new[rr * VPR + j] = nw.klo;
+      my_new[rr * VPR + j + VPR / 2] = nw.khi;
+      my_new[(kMaxFusedRows + rr) * VPR + j] = nw.vlo;
+      my_new[(kMaxFusedRows + rr) * VPR + j + VPR / 2] = nw.vhi;
+      if (store_new) store_pair<DT>(kc + (size_t)pos * ROWB, vc + (size_t)pos * ROWB, j, nw);
+    }
+    asm volatile("" ::: "memory");  // the slice is written before the wave reads it
+  }
+
+  // ---- query operand (rotated in fp32, fed as a high and a low part)
+  if constexpr (ROPE) {
+    float x0[8], x1[8];
+    unpack16<DT>(qraw[0], x0);
+    unpack16<DT>(qraw[1], x1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rope_rotate(x0[e], x1[e], qc[e], qs[e]);
+    split_hi_lo<DT>(x0, qhi[0], qlo[0]);
+    split_hi_lo<DT>(x1, qhi[1], qlo[1]);
+  } else {
+    qhi[0] = qraw[0];
+    qhi[1] = qraw[1];
+    qlo[0] = qlo[1] = u32x4{0, 0, 0, 0};
+  }
+
   if constexpr (RW == kWaves) {
     // prefill: a wave walks many steps, so the next step's loads go out
     // before this step's math (two register buffers in turn; three steps
     // ahead measured no faster)
-    u32x4 kA[2][2], kB[2][2];
-    u32x2 vA[8], vB[8];
-    if (s0 < kend) load_step(s0, kA, vA);
+    u32x4 kB[2][2];
+    u32x2 vB[8];
     while (s0 < kend) {
       if (s0 + kstride < kend) load_step(s0 + kstride, kB, vB);
       compute_step(s0, kA, vA);
@@ -308,11 +380,10 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
     }
   } else {
     // verification: one or two steps per wave (prefetching measured slower)
-    for (; s0 < kend; s0 += kstride) {
-      u32x4 ka[2][2];
-      u32x2 vv[8];
-      load_step(s0, ka, vv);
-      compute_step(s0, ka, vv);
+    while (s0 < kend) {
+      compute_step(s0, kA, vA);
+      s0 += kstride;
+      if (s0 < kend) load_step(s0, kA, vA);
     }
   }
   lsum = groups_sum<16>(lsum);  // the row's keys were spread over the 4 lane groups

@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void beam_kernel(BeamArgs a) {
     if (lane < KP) publish(reinterpret_cast<uint64_t *>(rec + 2) + lane, best);
     wait_stores();  // the wavefront's record is in place before it counts
     if (lane == 0)
-      s_last = (arrive(&a.ws_count[b]) == (uint32_t)(K * a.chunks - 1)) ? 1 : 0;
+      s_last = (arrive(&a.ws_count[b * kCounterStride]) == (uint32_t)(K * a.chunks - 1)) ? 1 : 0;
   }
   __syncthreads();
   if (!s_last) return;
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void beam_kernel(BeamArgs a) {
   }
   if (tid == 0) {
     a.fin_count[b] = nf;
-    reset_counter(&a.ws_count[b]);
+    reset_counter(&a.ws_count[b * kCounterStride]);
   }
 }
 

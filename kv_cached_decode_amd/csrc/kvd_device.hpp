@@ -77,7 +77,11 @@ template <> __device__ __forceinline__ uint32_t pack2<F16>(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, h);
 }
 template <> __device__ __forceinline__ uint32_t pack2<BF16>(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  // v_cvt_pk_bf16_f32: round to nearest even, as f32_to_bf16_bits for
+  // every non-NaN value
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 template <int DT> __device__ __forceinline__ u32x4 pack16(const float *in) {
@@ -293,6 +297,41 @@ struct PairChunks {
   u32x4 klo, khi, vlo, vhi;
 };
 // r.step == 0: no rotation.
+// Chunk j of each half of a new key row (dims [j*VE, +VE) and their rotary
+// partners [D/2 + j*VE, +VE)), rotated at position pos when base > 0 and
+// rounded to the storage type: the one definition of a stored rotated key.
+template <int DT>
+__device__ __forceinline__ void rotate_key_pair_cs(u32x4 &klo, u32x4 &khi, const float *cs,
+                                                   const float *sn) {
+  constexpr int VE = vec_elems<DT>();
+  float lo[VE], hi[VE];
+  unpack16<DT>(klo, lo);
+  unpack16<DT>(khi, hi);
+#pragma unroll
+  for (int e = 0; e < VE; ++e) rope_rotate(lo[e], hi[e], cs[e], sn[e]);
+  klo = pack16<DT>(lo);
+  khi = pack16<DT>(hi);
+}
+template <int DT>
+__device__ __forceinline__ void rotate_key_pair(u32x4 &klo, u32x4 &khi, int j, int pos,
+                                                RopeStep r) {
+  constexpr int VE = vec_elems<DT>();
+  if (r.step > 0.0) {
+    float cs[VE], sn[VE];
+    rope_cos_sin_run<VE>(pos, j * VE, r, cs, sn);
+    rotate_key_pair_cs<DT>(klo, khi, cs, sn);
+  }
+}
+template <int DT>
+__device__ __forceinline__ void load_key_pair(const char *k_src, int j, int pos, RopeStep r,
+                                              u32x4 &klo, u32x4 &khi) {
+  constexpr int VE = vec_elems<DT>();
+  constexpr int EB = Storage<DT>::bytes;
+  klo = load16(k_src + j * VE * EB);
+  khi = load16(k_src + (kHeadDim / 2 + j * VE) * EB);
+  rotate_key_pair<DT>(klo, khi, j, pos, r);
+}
+
 template <int DT>
 __device__ __forceinline__ PairChunks load_pair(const char *k_src, const char *v_src, int j,
                                                 int pos, RopeStep r) {
@@ -300,20 +339,9 @@ __device__ __forceinline__ PairChunks load_pair(const char *k_src, const char *v
   constexpr int EB = Storage<DT>::bytes;
   const int lo_off = j * VE * EB, hi_off = (kHeadDim / 2 + j * VE) * EB;
   PairChunks c;
-  c.klo = load16(k_src + lo_off);
-  c.khi = load16(k_src + hi_off);
   c.vlo = load16(v_src + lo_off);
   c.vhi = load16(v_src + hi_off);
-  if (r.step > 0.0) {
-    float lo[VE], hi[VE], cs[VE], sn[VE];
-    unpack16<DT>(c.klo, lo);
-    unpack16<DT>(c.khi, hi);
-    rope_cos_sin_run<VE>(pos, j * VE, r, cs, sn);
-#pragma unroll
-    for (int e = 0; e < VE; ++e) rope_rotate(lo[e], hi[e], cs[e], sn[e]);
-    c.klo = pack16<DT>(lo);
-    c.khi = pack16<DT>(hi);
-  }
+  load_key_pair<DT>(k_src, j, pos, r, c.klo, c.khi);
   return c;
 }
 template <int DT>

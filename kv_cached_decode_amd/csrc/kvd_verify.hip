@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a) {
     k = wave_max_key(k, owner);
     if (lane == 0) publish(a.ws_key + (size_t)(b * a.R + r) * a.chunks + ch, k);
     wait_stores();  // the key is in place before it counts
-    if (lane == 0) s_last = (arrive(&a.ws_count[b]) == (uint32_t)(a.R * a.chunks - 1)) ? 1 : 0;
+    if (lane == 0) s_last = (arrive(&a.ws_count[b * kCounterStride]) == (uint32_t)(a.R * a.chunks - 1)) ? 1 : 0;
   }
   __syncthreads();
   if (!s_last) return;
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a) {
     if (lane == 0) {
       a.accept_len[b] = acc;
       a.next_token[b] = (acc < a.R) ? s_am[acc] : -1;
-      reset_counter(&a.ws_count[b]);
+      reset_counter(&a.ws_count[b * kCounterStride]);
     }
   }
 }
