@@ -83,6 +83,35 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
     vs = static_cast<const char *>(a.v_src) + src;
   }
 
+  // ---- first tiles: when every query row sees all keys of a tile (a causal
+  // row sees at least keys 0 .. causal_base) and none of them is new, the
+  // tile's loads go out before the rows' bookkeeping below. Without new rows,
+  // with few query rows and 4 waves (registers to spare; measured to pay only
+  // there), each wave keeps two tiles in flight: tile i + 2 is loaded into
+  // the buffer tile i just freed.
+  constexpr int PF = (!FUSED && GM <= 2 && NWMAX <= 4) ? 2 : 1;
+  u32x4 kA[kSteps], vA[kSteps], kB[PF == 2 ? kSteps : 1], vB[PF == 2 ? kSteps : 1];
+  const int stride = nw * TILE;
+  int t0 = k0 + wave * TILE;
+  const int kend_lo = min(kspan, (sp.causal_base < 0) ? sp.L : sp.causal_base + 1);
+  auto seen_by_all = [&](int t) { return t + TILE <= kend_lo && (!FUSED || t + TILE <= nb0); };
+  auto load_plain = [&](u32x4 *kd, u32x4 *vd, int t) {  // a whole tile
+    const char *kb = ks + (size_t)t * ROWB;
+    const char *vb = vs + (size_t)t * ROWB;
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      const uint32_t off = (uint32_t)((s * RPL + kr) * ROWB + ds * 16);
+      kd[s] = load16(kb + off);
+      vd[s] = load16(vb + off);
+    }
+  };
+  const bool early_a = seen_by_all(t0);                      // uniform
+  const bool early_b = PF == 2 && seen_by_all(t0 + stride);  // uniform
+  if (early_a) load_plain(kA, vA, t0);
+  if constexpr (PF == 2) {
+    if (early_b) load_plain(kB, vB, t0 + stride);
+  }
+
   // ---- which keys each query row sees (indices only, no memory access)
   int lim[GM];
   int kvis = 0;
@@ -97,12 +126,6 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
   }
   const int kend = __builtin_amdgcn_readfirstlane(min(kspan, kvis));
 
-  // ---- first tiles of cached keys: in flight before anything else waits.
-  // Without new rows, with few query rows and 4 waves (registers to spare;
-  // measured to pay only there), each wave keeps two tiles in flight: tile
-  // i + 2 is loaded into the buffer tile i just freed.
-  constexpr int PF = (!FUSED && GM <= 2 && NWMAX <= 4) ? 2 : 1;
-  u32x4 kA[kSteps], vA[kSteps], kB[PF == 2 ? kSteps : 1], vB[PF == 2 ? kSteps : 1];
   // A whole tile of cached keys: plain loads from a uniform base plus 32-bit
   // lane offsets. A tile reaching past kend or into the new rows loads its
   // keys clamped to the last cached one (row 0 if there is none), again with
@@ -129,13 +152,10 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
     }
   };
   auto load_a = [&](int t) { load_tile(kA, vA, t); };
-  const int stride = nw * TILE;
-  int t0 = k0 + wave * TILE;
+  // ---- the first tiles not loaded above go out now
+  if (!early_a && t0 < kend) load_a(t0);
   if constexpr (PF == 2) {  // (each form measured fastest for its kernels)
-    if (t0 < kend) load_tile(kA, vA, t0);
-    if (t0 + stride < kend) load_tile(kB, vB, t0 + stride);
-  } else {
-    if (t0 < kend) load_a(t0);
+    if (!early_b && t0 + stride < kend) load_tile(kB, vB, t0 + stride);
   }
 
   // ---- query rows: their loads go out before anything waits

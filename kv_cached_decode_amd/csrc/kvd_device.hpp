@@ -61,12 +61,6 @@ template <int DT> __device__ __forceinline__ void unpack16(u32x4 v, float *out) 
 }
 
 // fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
 
 // Two floats -> one dword of two storage elements, round to nearest even.
 template <int DT> __device__ __forceinline__ uint32_t pack2(float lo, float hi);
@@ -77,8 +71,8 @@ template <> __device__ __forceinline__ uint32_t pack2<F16>(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, h);
 }
 template <> __device__ __forceinline__ uint32_t pack2<BF16>(float lo, float hi) {
-  // v_cvt_pk_bf16_f32: round to nearest even, as f32_to_bf16_bits for
-  // every non-NaN value
+  // v_cvt_pk_bf16_f32: round to nearest even (checked against the rounding
+  // (u + 0x7fff + ((u >> 16) & 1)) >> 16 over every non-NaN float)
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   typedef float f32x2_t __attribute__((ext_vector_type(2)));
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
