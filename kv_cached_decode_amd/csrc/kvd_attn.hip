@@ -403,7 +403,9 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
   __syncthreads();
   const size_t tile_id = (size_t)unit * a.row_tiles + rt;
   float *part = a.ws_part + (tile_id * a.splits + split) * GM * kPStride;
-  for (int idx = threadIdx.x; idx < gcount * D; idx += blockDim.x) {
+  // output element idx (row idx / D, dim idx % D) of the tile: the waves'
+  // (m, l, o) merged, then written or published as this split's partial
+  auto finish = [&](int idx) {
     const int g = idx / D, d = idx % D;
     float mw[NWMAX];
     float M = -INFINITY;
@@ -430,7 +432,25 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
         publish(part + g * kPStride + D + 1, Ls);
       }
     }
+  };
+  if (gcount * D <= 64) {
+    // one wavefront holds the tile's output (one query row): it alone
+    // publishes, waits for its stores, counts the arrival and, if last,
+    // merges; the other waves are done, and no second barrier is needed
+    if (wave != 0) return;
+    if (lane < gcount * D) finish(lane);
+    if (a.splits == 1) return;
+    wait_stores();
+    uint32_t *counter = a.ws_count + tile_id * kCounterStride;
+    uint32_t prev = 0;
+    if (lane == 0) prev = arrive(counter);
+    prev = __builtin_amdgcn_readfirstlane(prev);
+    if (prev != (uint32_t)(a.splits - 1)) return;
+    if (lane == 0) reset_counter(counter);  // every split has arrived
+    merge_rows<GM>(a, tile_id, a.splits, g0, gcount, bkv, hk, 0, 1);
+    return;
   }
+  for (int idx = threadIdx.x; idx < gcount * D; idx += blockDim.x) finish(idx);
   if (a.splits == 1) return;
   merge_splits<GM>(a, tile_id, g0, gcount, bkv, hk);
 }
