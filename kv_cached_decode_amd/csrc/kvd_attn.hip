@@ -160,14 +160,15 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
 
   // ---- query rows: their loads go out before anything waits
   u32x4 qraw[GM], qpart[GM];
+  size_t orow[GM];  // element offset of each row in q's layout, which out shares
 #pragma unroll
   for (int g = 0; g < GM; ++g) {
     qraw[g] = u32x4{0, 0, 0, 0};
     qpart[g] = u32x4{0, 0, 0, 0};
+    orow[g] = 0;
     if (g < gcount) {
-      const RowId r = row_id(a, bkv, hk, g0 + g);
-      const char *qrow =
-          static_cast<const char *>(a.q) + ((size_t)(r.b * a.Hq + r.h) * a.N + r.i) * ROWB;
+      orow[g] = out_row(a, row_id(a, bkv, hk, g0 + g));
+      const char *qrow = static_cast<const char *>(a.q) + orow[g] * Storage<DT>::bytes;
       qraw[g] = load16(qrow + ds * 16);
       if (ROPE) qpart[g] = load16(qrow + (ds ^ (LPR / 2)) * 16);
     }
@@ -424,7 +425,7 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
       }
     }
     if (a.splits == 1) {
-      a.out[out_row(a, row_id(a, bkv, hk, g0 + g)) + d] = O / Ls;
+      a.out[orow[g] + d] = O * __builtin_amdgcn_rcpf(Ls);
     } else {
       publish(part + g * kPStride + d, O);
       if (d == 0) {

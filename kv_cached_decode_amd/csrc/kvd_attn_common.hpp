@@ -122,7 +122,7 @@ __device__ void merge_rows(const AttnArgs &a, size_t tile_id, int S, int g0, int
       ob[j] = (j < S) ? __builtin_bit_cast(float, fetch_u32(row + j * SS + lane)) : 0.f;
     const float M = groups_max<1>(mj);
     const float wj = (mj == -INFINITY) ? 0.f : exp2f(mj - M);
-    const float inv = 1.f / groups_sum<1>(lj * wj);
+    const float inv = __builtin_amdgcn_rcpf(groups_sum<1>(lj * wj));
     float O = 0.f;
     for (int s0 = 0; s0 < S; s0 += NB) {
       if (s0 > 0) {
