@@ -106,40 +106,59 @@ __device__ void merge_rows(const AttnArgs &a, size_t tile_id, int S, int g0, int
   constexpr int D = kHeadDim;
   constexpr int NB = 8;               // o loads in flight per lane (default plans: <= 8 splits)
   constexpr int SS = GM * kPStride;   // floats between two partials of one row
+  constexpr int MR = GM < 4 ? GM : 4; // rows of one wave whose loads go out together
   static_assert(D == 64, "one lane per dim");
   const int lane = threadIdx.x & 63;
   const float *src = a.ws_part + tile_id * S * SS;
-  for (int g = g_first; g < gcount; g += g_step) {
+  // one row from its loaded (m, l) of partial `lane` and o[dim] of the first
+  // NB partials; partials past NB (plans of more than NB splits) are loaded
+  // here, a batch at a time
+  auto reduce_row = [&](int g, float mj, float lj, const float (&ob)[NB]) {
     const float *row = src + g * kPStride;
-    float mj = -INFINITY, lj = 0.f;
-    if (lane < S) {
-      mj = __builtin_bit_cast(float, fetch_u32(row + lane * SS + D));
-      lj = __builtin_bit_cast(float, fetch_u32(row + lane * SS + D + 1));
-    }
-    float ob[NB];
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-      ob[j] = (j < S) ? __builtin_bit_cast(float, fetch_u32(row + j * SS + lane)) : 0.f;
     const float M = groups_max<1>(mj);
-    const float wj = (mj == -INFINITY) ? 0.f : exp2f(mj - M);
+    const float wj = (mj == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mj - M);
     const float inv = __builtin_amdgcn_rcpf(groups_sum<1>(lj * wj));
     float O = 0.f;
+    float ob2[NB];
     for (int s0 = 0; s0 < S; s0 += NB) {
-      if (s0 > 0) {
 #pragma unroll
-        for (int j = 0; j < NB; ++j)
-          ob[j] = (s0 + j < S) ? __builtin_bit_cast(float, fetch_u32(row + (s0 + j) * SS + lane)) : 0.f;
+      for (int j = 0; j < NB; ++j) {
+        ob2[j] = ob[j];
+        if (s0 > 0) ob2[j] = (s0 + j < S) ? __builtin_bit_cast(float, fetch_u32(row + (s0 + j) * SS + lane)) : 0.f;
       }
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         if (s0 + j < S) {
           const float w = __builtin_bit_cast(
               float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), s0 + j));
-          O = fmaf(ob[j], w, O);
+          O = fmaf(ob2[j], w, O);
         }
       }
     }
     a.out[out_row(a, row_id(a, bkv, hk, g0 + g)) + lane] = O * inv;
+  };
+  for (int g1 = g_first; g1 < gcount; g1 += MR * g_step) {
+    // the loads of up to MR rows go out before any of them is reduced
+    float mj[MR], lj[MR], ob[MR][NB];
+#pragma unroll
+    for (int r = 0; r < MR; ++r) {
+      const int g = g1 + r * g_step;
+      const float *row = src + g * kPStride;
+      mj[r] = -INFINITY;
+      lj[r] = 0.f;
+      if (g < gcount && lane < S) {
+        mj[r] = __builtin_bit_cast(float, fetch_u32(row + lane * SS + D));
+        lj[r] = __builtin_bit_cast(float, fetch_u32(row + lane * SS + D + 1));
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        ob[r][j] = (g < gcount && j < S) ? __builtin_bit_cast(float, fetch_u32(row + j * SS + lane)) : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < MR; ++r) {
+      const int g = g1 + r * g_step;
+      if (g < gcount) reduce_row(g, mj[r], lj[r], ob[r]);
+    }
   }
 }
 

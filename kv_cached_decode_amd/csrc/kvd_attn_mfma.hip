@@ -363,10 +363,9 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
     qlo[0] = qlo[1] = u32x4{0, 0, 0, 0};
   }
 
-  if constexpr (RW == kWaves) {
-    // prefill: a wave walks many steps, so the next step's loads go out
-    // before this step's math (two register buffers in turn; three steps
-    // ahead measured no faster)
+  {
+    // the next step's loads go out before this step's math (two register
+    // buffers in turn; three steps ahead measured no faster in prefill)
     u32x4 kB[2][2];
     u32x2 vB[8];
     while (s0 < kend) {
@@ -377,13 +376,6 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
       if (s0 + kstride < kend) load_step(s0 + kstride, kA, vA);
       compute_step(s0, kB, vB);
       s0 += kstride;
-    }
-  } else {
-    // verification: one or two steps per wave (prefetching measured slower)
-    while (s0 < kend) {
-      compute_step(s0, kA, vA);
-      s0 += kstride;
-      if (s0 < kend) load_step(s0, kA, vA);
     }
   }
   lsum = groups_sum<16>(lsum);  // the row's keys were spread over the 4 lane groups
@@ -422,9 +414,8 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
     const int g0 = blockIdx.y * kRows;
     const int gcount = min(kRows, a.G - g0);
     float *part = a.ws_part + (tile_id * a.splits + split) * kRows * kPStride;
-    for (int idx = threadIdx.x; idx < kRows * D; idx += blockDim.x) {
+    for (int idx = threadIdx.x; idx < gcount * D; idx += blockDim.x) {
       const int g = idx / D, d = idx % D;
-      if (g >= gcount) continue;
       float mw[NPH];
       float M = -INFINITY;
 #pragma unroll
@@ -436,13 +427,13 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
 #pragma unroll
       for (int w = 0; w < NPH; ++w) {
         if (mw[w] != -INFINITY) {
-          const float f = exp2f(mw[w] - M);
+          const float f = __builtin_amdgcn_exp2f(mw[w] - M);
           Ls = fmaf(sm_l[w * kRows + g], f, Ls);
           O = fmaf(sm_o[(w * kRows + g) * D + d], f, O);
         }
       }
       if (a.splits == 1) {
-        a.out[out_row(a, row_id(a, bkv, hk, g0 + g)) + d] = O / Ls;
+        a.out[out_row(a, row_id(a, bkv, hk, g0 + g)) + d] = O * __builtin_amdgcn_rcpf(Ls);
       } else {
         publish(part + g * kPStride + d, O);
         if (d == 0) {
