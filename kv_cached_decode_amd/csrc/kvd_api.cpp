@@ -55,6 +55,8 @@ size_t attn_bytes(const AttnPlan &p) { return kCounterBytes + p.part_floats * si
 // Fill the plan-dependent fields and the workspace pointers.
 int prepare_attn(AttnArgs &a, int dtype, void *ws, size_t ws_bytes) {
   const int units = a.Bkv * a.Hkv;
+  a.div_N = kvd::make_fast_div((uint32_t)a.N);
+  a.div_group = kvd::make_fast_div((uint32_t)a.group);
   // the beam step runs on the streaming kernel (it alone copies parent rows)
   const AttnPlan p = kvd::plan_attn(dtype, units, a.G, a.N, a.L, a.rope_base > 0.f, !a.parent);
   if (p.row_tiles > 65535 || units > 65535) return KVD_ERR_SHAPE;  // grid limits

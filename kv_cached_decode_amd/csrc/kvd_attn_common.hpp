@@ -16,12 +16,17 @@ struct RowId {
   int b, h, i;
 };
 
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, FastDiv f) {
+  return (__umulhi(n, f.m) + n) >> f.s;
+}
+
 // Query row gg of unit (bkv, hk): numbered (bl * group + j) * N + i.
 __device__ __forceinline__ RowId row_id(const AttnArgs &a, int bkv, int hk, int gg) {
   RowId r;
-  r.i = gg % a.N;
-  const int j = (gg / a.N) % a.group;
-  const int bl = gg / (a.N * a.group);
+  const int q = (int)fast_div((uint32_t)gg, a.div_N);  // gg / N
+  r.i = gg - q * a.N;
+  const int bl = (int)fast_div((uint32_t)q, a.div_group);  // gg / (N * group)
+  const int j = q - bl * a.group;
   r.b = (a.Bkv == 1) ? bl : bkv;
   r.h = hk * a.group + j;
   return r;

@@ -53,6 +53,20 @@ struct ReorderArgs {
 // rows are every (b, h, i) that reads it, numbered g = (bl * group + j) * N + i
 // with bl the batch row within the unit (0 unless the cache is shared),
 // j the head within the group and i the query.
+// Division by a divisor fixed for a launch, as a multiply-high (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994):
+// for 1 <= d < 2^31, s = ceil(log2 d) and m = floor(2^32 (2^s - d) / d) + 1,
+// n / d = (umulhi(n, m) + n) >> s for every 0 <= n < 2^31 (the sum stays below
+// 2^32). A few instructions where a runtime division takes about twenty.
+struct FastDiv {
+  uint32_t m, s;
+};
+inline FastDiv make_fast_div(uint32_t d) {
+  uint32_t s = 0;
+  while (((uint64_t)1 << s) < d) ++s;
+  return FastDiv{(uint32_t)((((uint64_t)1 << 32) * (((uint64_t)1 << s) - d)) / d + 1), s};
+}
+
 struct AttnArgs {
   const void *q;                 // [B][Hq][N][D]
   void *k, *v;                   // [Bkv][Hkv][S_max][D]
@@ -61,6 +75,7 @@ struct AttnArgs {
   float *ws_part;                // partial (o, m, l) per split
   uint32_t *ws_count;            // arrival counters, one per (unit, row tile), kCounterStride apart
   int B, Hq, N, Bkv, Hkv, group, S_max;
+  FastDiv div_N, div_group;      // division by N and by group (query row numbering)
   int G;                         // query rows per unit
   int L;                         // keys: len (self) or frames (cross)
   int causal_base;               // self: len - N; cross: -1 (no mask)
