@@ -83,6 +83,23 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
     vs = static_cast<const char *>(a.v_src) + src;
   }
 
+  // ---- query rows first: the wait for them then leaves the key loads
+  // below in flight (the row numbering costs a few instructions)
+  u32x4 qraw[GM], qpart[GM];
+  size_t orow[GM];  // element offset of each row in q's layout, which out shares
+#pragma unroll
+  for (int g = 0; g < GM; ++g) {
+    qraw[g] = u32x4{0, 0, 0, 0};
+    qpart[g] = u32x4{0, 0, 0, 0};
+    orow[g] = 0;
+    if (g < gcount) {
+      orow[g] = out_row(a, row_id(a, bkv, hk, g0 + g));
+      const char *qrow = static_cast<const char *>(a.q) + orow[g] * Storage<DT>::bytes;
+      qraw[g] = load16(qrow + ds * 16);
+      if (ROPE) qpart[g] = load16(qrow + (ds ^ (LPR / 2)) * 16);
+    }
+  }
+
   // ---- first tiles: when every query row sees all keys of a tile (a causal
   // row sees at least keys 0 .. causal_base) and none of them is new, the
   // tile's loads go out before the rows' bookkeeping below. Without new rows,
@@ -156,22 +173,6 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
   if (!early_a && t0 < kend) load_a(t0);
   if constexpr (PF == 2) {  // (each form measured fastest for its kernels)
     if (!early_b && t0 + stride < kend) load_tile(kB, vB, t0 + stride);
-  }
-
-  // ---- query rows: their loads go out before anything waits
-  u32x4 qraw[GM], qpart[GM];
-  size_t orow[GM];  // element offset of each row in q's layout, which out shares
-#pragma unroll
-  for (int g = 0; g < GM; ++g) {
-    qraw[g] = u32x4{0, 0, 0, 0};
-    qpart[g] = u32x4{0, 0, 0, 0};
-    orow[g] = 0;
-    if (g < gcount) {
-      orow[g] = out_row(a, row_id(a, bkv, hk, g0 + g));
-      const char *qrow = static_cast<const char *>(a.q) + orow[g] * Storage<DT>::bytes;
-      qraw[g] = load16(qrow + ds * 16);
-      if (ROPE) qpart[g] = load16(qrow + (ds ^ (LPR / 2)) * 16);
-    }
   }
 
   // ---- rotary cos / sin at the first row's position: no memory access, so

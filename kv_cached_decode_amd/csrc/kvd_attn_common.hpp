@@ -96,6 +96,7 @@ __device__ __forceinline__ void hoist_args(const AttnArgs &a) {
             f7 = a.causal_base, f8 = a.new_base, f9 = a.chunk, f10 = a.Hq, f11 = a.T_new;
   asm volatile("" ::"s"(f0), "s"(f1), "s"(f2), "s"(f3), "s"(f4), "s"(f5), "s"(f6), "s"(f7),
                "s"(f8), "s"(f9), "s"(f10), "s"(f11), "s"(a.k), "s"(a.v), "s"(a.q));
+  asm volatile("" ::"s"(a.div_N.m), "s"(a.div_N.s), "s"(a.div_group.m), "s"(a.div_group.s));
 }
 
 // Merge of S published partials (o, m, l) of tile `tile_id`, numbered

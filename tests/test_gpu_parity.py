@@ -705,6 +705,24 @@ def test_cross_cache_per_row_and_shared_agree():
     assert max_err(a, ref) <= TOL["f16"] and max_err(b, ref) <= TOL["f16"]
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("B,Hq,Hkv,N,F", [(3, 12, 4, 5, 1500), (7, 15, 5, 3, 300), (2, 14, 2, 11, 129)])
+def test_cross_shared_grouped_rows(dtype, B, Hq, Hkv, N, F, plan):
+    """Shared cross cache with grouped heads and several queries per row: the
+    rows of a KV head are numbered (row, head in group, query), so both
+    divisions of the row numbering (by N, by the group size) are non-trivial."""
+    say(f"case: cross shared {dtype} B={B} Hq={Hq} Hkv={Hkv} N={N} F={F} plan={plan}")
+    g = np.random.default_rng(B * 100 + N)
+    xk = O.narrow(g.standard_normal((1, Hkv, F, 64)), dtype)
+    xv = O.narrow(g.standard_normal((1, Hkv, F, 64)), dtype)
+    q = O.narrow(g.standard_normal((B, Hq, N, 64)) / 4, dtype)
+    shared = kb.Cache.wrap(to_dev(xk, dtype), to_dev(xv, dtype))
+    out = kb.decode_attn_cross(to_dev(q, dtype), shared, F, 0.125, ws=_ws())
+    ox = O.ConcatCache(1, Hkv, 64, dtype)
+    ox.set_once(xk, xv)
+    assert max_err(out, O.attend_cross(q, ox, 0.125)) <= TOL[dtype]
+
+
 # --------------------------------------------------- fused append + attend ----
 
 @pytest.mark.parametrize("dtype,B,Hq,Hkv,N,L,rope", [
