@@ -467,7 +467,7 @@ void launch_gm(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
   }
 }
 
-// The 16-wave variant (one wide workgroup per unit): one query row and no
+// The 8-wave variant (one wide workgroup per unit): one query row and no
 // rotary work, so that it fits 128 registers without spilling.
 template <int DT, bool FUSED, bool RAGGED, bool BEAM>
 void launch_wide(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {

@@ -10,7 +10,7 @@
 namespace kvd {
 
 constexpr int kPStride = kHeadDim + 4;  // partial row: o[D], m, l, 2 pad floats (16-byte rows)
-constexpr int kMaxWaves = 16;           // the widest workgroup (1024 threads)
+constexpr int kMaxWaves = 8;            // the widest workgroup (512 threads; 16 measured slower)
 
 struct RowId {
   int b, h, i;

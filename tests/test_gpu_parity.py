@@ -109,12 +109,12 @@ def test_whisper_greedy_sweep_lengths(layer):
 
 
 # Plans forced through the tuning variables, so that split boundaries and the
-# narrow (1-, 2-wave) and wide (8-, 16-wave) workgroups are covered at lengths
+# narrow (1-, 2-wave) and wide (8-wave) workgroups are covered at lengths
 # the default plan runs otherwise.
 # Blocks of queries (N > 1, 16-bit storage) take the matrix-core kernel by
 # default; "stream" runs them through the streaming kernel instead.
 PLANS = {"default": {}, "chunk128": {"KVD_ATTN_CHUNK": "128"},
-         "wide": {"KVD_ATTN_WAVES": "16"}, "wide_chunk512": {"KVD_ATTN_WAVES": "16", "KVD_ATTN_CHUNK": "512"},
+         "wide": {"KVD_ATTN_WAVES": "8"}, "wide_chunk512": {"KVD_ATTN_WAVES": "8", "KVD_ATTN_CHUNK": "512"},
          "w8_chunk256": {"KVD_ATTN_WAVES": "8", "KVD_ATTN_CHUNK": "256"},
          "w1": {"KVD_ATTN_WAVES": "1"}, "w2_chunk64": {"KVD_ATTN_WAVES": "2", "KVD_ATTN_CHUNK": "64"},
          "stream": {"KVD_ATTN_MFMA": "0"}, "stream_chunk128": {"KVD_ATTN_MFMA": "0", "KVD_ATTN_CHUNK": "128"}}
