@@ -566,7 +566,7 @@ hipError_t launch_attn(int dtype, const AttnArgs &a, hipStream_t s) {
 // KVD_ATTN_WAVES / KVD_ATTN_CHUNK when set), so results are reproducible run
 // to run. The thresholds come from timing back-to-back launches in a graph on
 // MI355X: up to 96 KB of keys a unit stays on one workgroup (8 waves above
-// 64 KB), which avoids the cross-workgroup merge (two memory round trips:
+// 40 KB with one query row), which avoids the cross-workgroup merge (two memory round trips:
 // the arrival count, then the partials); beyond that the keys are split into
 // chunks of at least 32 KB and at most 8 splits.
 AttnPlan plan_attn(int dtype, int units, int G, int N, int L, bool rope, bool allow_mfma) {
@@ -589,7 +589,7 @@ AttnPlan plan_attn(int dtype, int units, int G, int N, int L, bool rope, bool al
   int waves = 4, chunk;
   if (tiles >= 256 || unit_bytes <= 96 * 1024) {
     chunk = L;  // one workgroup per (unit, row tile)
-    if (tiles < 256 && unit_bytes > 64 * 1024 && wide_ok) waves = 8;  // measured: 8 beats 16
+    if (tiles < 256 && unit_bytes > 40 * 1024 && wide_ok) waves = 8;  // measured (self, 1 row)
   } else {
     // at least 32 KB of keys per workgroup (one round of loads for 4 waves),
     // at most 8 splits (the merge costs grow with the split count)
