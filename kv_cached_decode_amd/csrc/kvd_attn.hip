@@ -375,7 +375,7 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
   for (int g = 0; g < GM; ++g) {
     if (g < gcount) {
       const float M = groups_max<LPR>(m[g]);
-      const float f = (M == -INFINITY) ? 0.f : exp2f(m[g] - M);
+      const float f = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[g] - M);
       l[g] = groups_sum<LPR>(l[g] * f);
 #pragma unroll
       for (int e = 0; e < VE; ++e) o[g][e] = groups_sum<LPR>(o[g][e] * f);
@@ -420,7 +420,7 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int w = 0; w < NWMAX; ++w) {
       if (w < nw && mw[w] != -INFINITY) {
-        const float f = exp2f(mw[w] - M);
+        const float f = __builtin_amdgcn_exp2f(mw[w] - M);
         Ls = fmaf(sm_l[w * GM + g], f, Ls);
         O = fmaf(sm_o[(w * GM + g) * D + d], f, O);
       }
@@ -566,9 +566,9 @@ hipError_t launch_attn(int dtype, const AttnArgs &a, hipStream_t s) {
 // KVD_ATTN_WAVES / KVD_ATTN_CHUNK when set), so results are reproducible run
 // to run. The thresholds come from timing back-to-back launches in a graph on
 // MI355X: up to 96 KB of keys a unit stays on one workgroup (8 waves above
-// 40 KB with one query row), which avoids the cross-workgroup merge (two memory round trips:
-// the arrival count, then the partials); beyond that the keys are split into
-// chunks of at least 32 KB and at most 8 splits.
+// 40 KB with one query row), which avoids the cross-workgroup merge (two
+// memory round trips: the arrival count, then the partials); beyond that the
+// keys are split into chunks of at least 32 KB and at most 8 splits.
 AttnPlan plan_attn(int dtype, int units, int G, int N, int L, bool rope, bool allow_mfma) {
   AttnPlan p{};
   // Matrix-core tiles for several query rows per KV head: N > 1 queries, or
