@@ -409,21 +409,24 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
   // (m, l, o) merged, then written or published as this split's partial
   auto finish = [&](int idx) {
     const int g = idx / D, d = idx % D;
-    float mw[NWMAX];
+    float mw[NWMAX], lw[NWMAX];
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NWMAX; ++w) {
       mw[w] = (w < nw) ? sm_m[w * GM + g] : -INFINITY;
+      lw[w] = (w < nw) ? sm_l[w * GM + g] : 0.f;
       M = fmaxf(M, mw[w]);
     }
+    // every slot is read (slots of absent waves hold stale values); a wave
+    // with no keys or no slot contributes zeros
     float Ls = 0.f, O = 0.f;
 #pragma unroll
     for (int w = 0; w < NWMAX; ++w) {
-      if (w < nw && mw[w] != -INFINITY) {
-        const float f = __builtin_amdgcn_exp2f(mw[w] - M);
-        Ls = fmaf(sm_l[w * GM + g], f, Ls);
-        O = fmaf(sm_o[(w * GM + g) * D + d], f, O);
-      }
+      const bool ok = w < nw && mw[w] != -INFINITY;
+      const float ow = sm_o[(w * GM + g) * D + d];
+      const float f = ok ? __builtin_amdgcn_exp2f(mw[w] - M) : 0.f;
+      Ls = fmaf(ok ? lw[w] : 0.f, f, Ls);
+      O = fmaf(ok ? ow : 0.f, f, O);
     }
     if (a.splits == 1) {
       a.out[orow[g] + d] = O * __builtin_amdgcn_rcpf(Ls);
