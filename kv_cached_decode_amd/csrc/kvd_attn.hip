@@ -505,9 +505,9 @@ int env_int(const char *name, int dflt) {
 
 // Matrix-core tile plan (blocks of queries, 16-bit storage): 16-row tiles;
 // four tiles per workgroup and one split when there are enough tiles to fill
-// the chip (prefill), else one tile per workgroup with the 4 waves sharing
-// its keys and the keys split like the streaming kernel's.
-AttnPlan plan_attn_mfma(int units, int G, int L) {
+// the chip (prefill), else one tile per workgroup with its 4 or 8 waves
+// sharing its keys and the keys split like the streaming kernel's.
+AttnPlan plan_attn_mfma(int units, int G, int L, bool rope) {
   constexpr int kRows = 16, kStep = 32;
   AttnPlan p{};
   p.mfma = 1;
@@ -545,6 +545,16 @@ AttnPlan plan_attn_mfma(int units, int G, int L) {
     }
     p.chunk = chunk;
     p.splits = splits;
+    // 8 waves, one or more steps each, when every wave has a step and the
+    // workgroups are fewer than the compute units; not with rotary work, which
+    // every wave repeats for the queries and new rows (measured, 5 rows per
+    // tile: 5-row cross attention at B = 1 7.99 -> 7.24 us and the 5-draft
+    // self step at length 160 / 256 5.45 / 5.88 -> 4.96 / 5.69 us, but the
+    // cross attention of 4 batch rows, 480 workgroups, 11.4 -> 14.2 us, and
+    // GQA decode steps with rotary keys at length 768 7.6 -> 9.0 us)
+    if (!rope && chunk >= 8 * kStep && (size_t)units * p.row_tiles * splits <= 256) p.waves = 8;
+    const int env_waves = env_int("KVD_ATTN_WAVES", 0);
+    if (env_waves == 4 || env_waves == 8) p.waves = env_waves;
   }
   const size_t tiles = (size_t)units * p.row_tiles;
   p.part_floats = (p.splits > 1) ? tiles * p.splits * kRows * kPStride : 0;
@@ -580,7 +590,7 @@ AttnPlan plan_attn(int dtype, int units, int G, int N, int L, bool rope, bool al
   // streaming tiles; 2 rows stay on the streaming kernel).
   const bool use_mfma =
       allow_mfma && dtype != F32 && (N > 1 || G >= 3) && env_int("KVD_ATTN_MFMA", 1) != 0;
-  if (use_mfma) return plan_attn_mfma(units, G, L);
+  if (use_mfma) return plan_attn_mfma(units, G, L, rope);
   p.gm = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
   p.row_tiles = (G + p.gm - 1) / p.gm;
   const int tile = (dtype == F32) ? AttnGeom<F32>::TILE : AttnGeom<F16>::TILE;

@@ -19,10 +19,10 @@
 // rounding stays far below the output tolerance; K, V and stored queries are
 // exact in the storage type already.
 //
-// A workgroup of 4 waves covers RW 16-row tiles: RW = 4 (prefill: each wave
-// its own rows, all keys of the chunk) or RW = 1 (verification: the 4 waves
-// share the rows and take every 4th 32-key step, merged in LDS). Splits over
-// keys are merged as in the streaming kernel.
+// A workgroup of NW waves covers RW 16-row tiles: RW = NW = 4 (prefill: each
+// wave its own rows, all keys of the chunk) or RW = 1 (verification: the 4 or
+// 8 waves share the rows and take every NW-th 32-key step, merged in LDS).
+// Splits over keys are merged as in the streaming kernel.
 #include <stdlib.h>
 
 #include "kvd_attn_common.hpp"
@@ -35,7 +35,7 @@ namespace {
 
 constexpr int kRows = 16;     // query rows per MFMA tile
 constexpr int kStep = 32;     // keys per MFMA step
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;     // prefill (one row tile per wave)
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -89,12 +89,12 @@ __device__ __forceinline__ uint32_t pair16(u32x2 c0, u32x2 c1) {
 }
 
 // One 16-row tile `rt` of the workgroup's waves (see the kernel below).
-template <int DT, int RW, bool FUSED, bool ROPE, bool RAGGED>
+template <int DT, int RW, int NW, bool FUSED, bool ROPE, bool RAGGED>
 __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) {
   constexpr int D = kHeadDim;
   constexpr int ROWB = kHeadDim * 2;
   constexpr int VPR = ROWB / 16;
-  constexpr int NPH = kWaves / RW;  // waves sharing a row tile
+  constexpr int NPH = NW / RW;  // waves sharing a row tile
   static_assert(DT != F32, "matrix-core tiles take 16-bit storage");
 
   hoist_args(a);
@@ -179,7 +179,7 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
   // flight, and keeps them in its own slice of LDS, so no barrier is needed.
   // Lane l takes chunk pair l % 4 of new row l / 4 (N <= 16 rows: one each).
   constexpr int kNewSlice = 2 * kMaxFusedRows * VPR;  // K rows, then V rows
-  __shared__ u32x4 s_new[FUSED ? kWaves * kNewSlice : 1];
+  __shared__ u32x4 s_new[FUSED ? NW * kNewSlice : 1];
   u32x4 *my_new = s_new + (FUSED ? wave * kNewSlice : 0);
   const int new_items = takes_new ? (kspan - nb0) * (VPR / 2) : 0;  // uniform
   PairChunks nw{};
@@ -382,10 +382,10 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
 
   // ---- lane l holds O[row c][16gq + 4i + t] = o[t][i]; merge the phases
   // that shared the row tile, then write the rows or publish the partial
-  constexpr int kSmem = (RW == kWaves) ? 1 : kWaves * kRows * (D + 2);
+  constexpr int kSmem = (RW == NW) ? 1 : NW * kRows * (D + 2);
   __shared__ __attribute__((aligned(16))) float smem[kSmem];
   const size_t tile_id = (size_t)unit * a.row_tiles + blockIdx.y;
-  if constexpr (RW == kWaves) {
+  if constexpr (RW == NW) {
     // one wave per row tile, no split (the plan guarantees it)
     if (active) {
       const float inv = 1.f / lsum;
@@ -399,8 +399,8 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
     return;
   } else {
     float *sm_o = smem;                        // [phase][row][D]
-    float *sm_m = smem + kWaves * kRows * D;   // [phase][row]
-    float *sm_l = sm_m + kWaves * kRows;       // [phase][row]
+    float *sm_m = smem + NW * kRows * D;   // [phase][row]
+    float *sm_l = sm_m + NW * kRows;       // [phase][row]
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -416,21 +416,23 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
     float *part = a.ws_part + (tile_id * a.splits + split) * kRows * kPStride;
     for (int idx = threadIdx.x; idx < gcount * D; idx += blockDim.x) {
       const int g = idx / D, d = idx % D;
-      float mw[NPH];
+      float mw[NPH], lw[NPH];
       float M = -INFINITY;
 #pragma unroll
       for (int w = 0; w < NPH; ++w) {
         mw[w] = sm_m[w * kRows + g];
+        lw[w] = sm_l[w * kRows + g];
         M = fmaxf(M, mw[w]);
       }
+      // no branches: a phase with no keys (m = -inf) contributes zeros
       float Ls = 0.f, O = 0.f;
 #pragma unroll
       for (int w = 0; w < NPH; ++w) {
-        if (mw[w] != -INFINITY) {
-          const float f = __builtin_amdgcn_exp2f(mw[w] - M);
-          Ls = fmaf(sm_l[w * kRows + g], f, Ls);
-          O = fmaf(sm_o[(w * kRows + g) * D + d], f, O);
-        }
+        const bool ok = mw[w] != -INFINITY;
+        const float ow = sm_o[(w * kRows + g) * D + d];
+        const float f = ok ? __builtin_amdgcn_exp2f(mw[w] - M) : 0.f;
+        Ls = fmaf(ok ? lw[w] : 0.f, f, Ls);
+        O = fmaf(ok ? ow : 0.f, f, O);
       }
       if (a.splits == 1) {
         a.out[out_row(a, row_id(a, bkv, hk, g0 + g)) + d] = O * __builtin_amdgcn_rcpf(Ls);
@@ -447,52 +449,55 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
   }
 }
 
-template <int DT, int RW, bool FUSED, bool ROPE, bool RAGGED>
-__global__ __launch_bounds__(64 * kWaves) void attn_mfma_kernel(AttnArgs a) {
+template <int DT, int RW, int NW, bool FUSED, bool ROPE, bool RAGGED>
+__global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if constexpr (RW == kWaves && !FUSED) {
+  if constexpr (RW == NW && !FUSED) {
     if (a.pair) {  // causal prefill: tile t and its complement T - 1 - t
       const int T = (a.G + kRows - 1) / kRows;
       const int t = blockIdx.y * RW + wave;
       if (t >= (T + 1) / 2) return;  // no barrier follows in this mode
-      attn_mfma_tile<DT, RW, FUSED, ROPE, RAGGED>(a, t);
-      if (T - 1 - t > t) attn_mfma_tile<DT, RW, FUSED, ROPE, RAGGED>(a, T - 1 - t);
+      attn_mfma_tile<DT, RW, NW, FUSED, ROPE, RAGGED>(a, t);
+      if (T - 1 - t > t) attn_mfma_tile<DT, RW, NW, FUSED, ROPE, RAGGED>(a, T - 1 - t);
       return;
     }
   }
-  attn_mfma_tile<DT, RW, FUSED, ROPE, RAGGED>(a, blockIdx.y * RW + wave % RW);
+  attn_mfma_tile<DT, RW, NW, FUSED, ROPE, RAGGED>(a, blockIdx.y * RW + wave % RW);
 }
 
-template <int DT, int RW, bool RAGGED>
-void launch_rwr(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
+template <int DT, int RW, int NW, bool RAGGED>
+void launch_rwr(const AttnArgs &a, dim3 grid, hipStream_t s) {
   const bool fused = a.k_new != nullptr, rope = a.rope_base > 0.f;
+  const dim3 block(64 * NW);
   if (fused) {
-    if (rope) launch_kernel(attn_mfma_kernel<DT, RW, true, true, RAGGED>, grid, block, s, a);
-    else launch_kernel(attn_mfma_kernel<DT, RW, true, false, RAGGED>, grid, block, s, a);
+    if (rope) launch_kernel(attn_mfma_kernel<DT, RW, NW, true, true, RAGGED>, grid, block, s, a);
+    else launch_kernel(attn_mfma_kernel<DT, RW, NW, true, false, RAGGED>, grid, block, s, a);
   } else {
-    if (rope) launch_kernel(attn_mfma_kernel<DT, RW, false, true, RAGGED>, grid, block, s, a);
-    else launch_kernel(attn_mfma_kernel<DT, RW, false, false, RAGGED>, grid, block, s, a);
+    if (rope) launch_kernel(attn_mfma_kernel<DT, RW, NW, false, true, RAGGED>, grid, block, s, a);
+    else launch_kernel(attn_mfma_kernel<DT, RW, NW, false, false, RAGGED>, grid, block, s, a);
   }
 }
 
-template <int DT, int RW>
-void launch_rw(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
-  if (a.lens) launch_rwr<DT, RW, true>(a, grid, block, s);
-  else launch_rwr<DT, RW, false>(a, grid, block, s);
+template <int DT, int RW, int NW>
+void launch_rw(const AttnArgs &a, dim3 grid, hipStream_t s) {
+  if (a.lens) launch_rwr<DT, RW, NW, true>(a, grid, s);
+  else launch_rwr<DT, RW, NW, false>(a, grid, s);
+}
+
+// prefill tiles on 4 waves; shared tiles on 4 or 8 (the plan's a.waves)
+template <int DT>
+void launch_dt(const AttnArgs &a, dim3 grid, hipStream_t s) {
+  if (a.rw == kWaves) launch_rw<DT, kWaves, kWaves>(a, grid, s);
+  else if (a.waves == 8) launch_rw<DT, 1, 8>(a, grid, s);
+  else launch_rw<DT, 1, 4>(a, grid, s);
 }
 
 }  // namespace
 
 hipError_t launch_attn_mfma(int dtype, const AttnArgs &a, hipStream_t s) {
   const dim3 grid(a.splits, a.row_tiles, a.Bkv * a.Hkv);
-  const dim3 block(64 * kWaves);
-  if (dtype == F16) {
-    if (a.rw == kWaves) launch_rw<F16, kWaves>(a, grid, block, s);
-    else launch_rw<F16, 1>(a, grid, block, s);
-  } else {
-    if (a.rw == kWaves) launch_rw<BF16, kWaves>(a, grid, block, s);
-    else launch_rw<BF16, 1>(a, grid, block, s);
-  }
+  if (dtype == F16) launch_dt<F16>(a, grid, s);
+  else launch_dt<BF16>(a, grid, s);
   return hipGetLastError();
 }
 
