@@ -326,12 +326,45 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
   // loaded value, and so the wait for it, in between)
   float ncs[ROPE && FUSED ? 8 : 1], nsn[ROPE && FUSED ? 8 : 1];
   float qc[ROPE ? 8 : 1], qs[ROPE ? 8 : 1];
-  if constexpr (ROPE && FUSED) {
-    if (lane < new_items)
-      rope_cos_sin_run<8>(nb0 + lane / 4, (lane % 4) * 8, RopeStep{a.rope_step, a.rope_ratio}, ncs, nsn);
+  // one query per sequence: every row of the tile and the new row sit at
+  // causal_base, so the wave needs the 32 pairs of one position. Each lane
+  // computes one pair (lanes l and l + 32 the same) and the wave reads its
+  // values back from its own LDS slice: cos in slots 0..31, sin in 32..63.
+  __shared__ __attribute__((aligned(16))) float s_rope[(ROPE && RW == 1) ? NW * 64 : 1];
+  if constexpr (ROPE && RW == 1) {
+    if (a.N == 1) {  // uniform
+      float cl, sl;
+      rope_cos_sin_pair<8>(sp.causal_base, lane & 31, RopeStep{a.rope_step, a.rope_ratio}, cl, sl);
+      float *tab = s_rope + wave * 64;
+      tab[lane] = (lane < 32) ? cl : sl;
+      asm volatile("" ::: "memory");  // the slice is written before the wave reads it
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qc[e] = tab[8 * gq + e];
+        qs[e] = tab[32 + 8 * gq + e];
+      }
+      if constexpr (FUSED) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ncs[e] = tab[8 * (lane % 4) + e];
+          nsn[e] = tab[32 + 8 * (lane % 4) + e];
+        }
+      }
+    } else {
+      if constexpr (FUSED) {
+        if (lane < new_items)
+          rope_cos_sin_run<8>(nb0 + lane / 4, (lane % 4) * 8, RopeStep{a.rope_step, a.rope_ratio}, ncs, nsn);
+      }
+      rope_cos_sin_run<8>(sp.causal_base + r.i, gq * 8, RopeStep{a.rope_step, a.rope_ratio}, qc, qs);
+    }
+  } else {
+    if constexpr (ROPE && FUSED) {
+      if (lane < new_items)
+        rope_cos_sin_run<8>(nb0 + lane / 4, (lane % 4) * 8, RopeStep{a.rope_step, a.rope_ratio}, ncs, nsn);
+    }
+    if constexpr (ROPE)
+      rope_cos_sin_run<8>(sp.causal_base + r.i, gq * 8, RopeStep{a.rope_step, a.rope_ratio}, qc, qs);
   }
-  if constexpr (ROPE)
-    rope_cos_sin_run<8>(sp.causal_base + r.i, gq * 8, RopeStep{a.rope_step, a.rope_ratio}, qc, qs);
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- the new rows, rotated (as kv_append rotates them) into the wave's slice

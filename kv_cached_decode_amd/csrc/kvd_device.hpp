@@ -104,31 +104,47 @@ struct RopeStep {
   double step, ratio;
 };
 
+// cos / sin of the angle pos * theta, reduced as described above.
+__device__ __forceinline__ void rope_angle_cs(int pos, double theta, float &c, float &s) {
+  const double ang = (double)pos * theta;       // >= 0
+  const double k = rint(ang * 0.6366197723675814);   // 2 / pi
+  double yd = fma(-k, 1.5707963267948966, ang);      // pi/2, high part
+  yd = fma(-k, 6.123233995736766e-17, yd);           // pi/2, low part
+  const float y = (float)yd, y2 = y * y;
+  float ps = fmaf(y2, 2.7557319e-06f, -1.9841270e-04f);  // 1/9!, -1/7!
+  ps = fmaf(ps, y2, 8.3333333e-03f);                     // 1/5!
+  ps = fmaf(ps, y2, -1.6666667e-01f);                    // -1/3!
+  const float sy = fmaf(ps * y2, y, y);
+  float pc = fmaf(y2, -2.7557319e-07f, 2.4801587e-05f);  // -1/10!, 1/8!
+  pc = fmaf(pc, y2, -1.3888889e-03f);                    // -1/6!
+  pc = fmaf(pc, y2, 4.1666668e-02f);                     // 1/4!
+  pc = fmaf(pc, y2, -0.5f);
+  const float cy = fmaf(pc, y2, 1.0f);
+  const int q = (int)k & 3;  // 0 <= k < 2^31: the angle is at most pos
+  const float sv = (q & 1) ? cy : sy, cv = (q & 1) ? sy : cy;
+  s = (q & 2) ? -sv : sv;                           // sin: s, c, -s, -c
+  c = (q == 1 || q == 2) ? -cv : cv;                // cos: c, -s, -c, s
+}
+
 template <int n>
 __device__ __forceinline__ void rope_cos_sin_run(int pos, int i0, RopeStep r, float *c, float *s) {
   double theta = exp2(-(double)i0 * r.step);
 #pragma unroll
   for (int e = 0; e < n; ++e) {
-    const double ang = (double)pos * theta;       // >= 0
-    const double k = rint(ang * 0.6366197723675814);   // 2 / pi
-    double yd = fma(-k, 1.5707963267948966, ang);      // pi/2, high part
-    yd = fma(-k, 6.123233995736766e-17, yd);           // pi/2, low part
-    const float y = (float)yd, y2 = y * y;
-    float ps = fmaf(y2, 2.7557319e-06f, -1.9841270e-04f);  // 1/9!, -1/7!
-    ps = fmaf(ps, y2, 8.3333333e-03f);                     // 1/5!
-    ps = fmaf(ps, y2, -1.6666667e-01f);                    // -1/3!
-    const float sy = fmaf(ps * y2, y, y);
-    float pc = fmaf(y2, -2.7557319e-07f, 2.4801587e-05f);  // -1/10!, 1/8!
-    pc = fmaf(pc, y2, -1.3888889e-03f);                    // -1/6!
-    pc = fmaf(pc, y2, 4.1666668e-02f);                     // 1/4!
-    pc = fmaf(pc, y2, -0.5f);
-    const float cy = fmaf(pc, y2, 1.0f);
-    const int q = (int)((long long)k & 3);
-    const float sv = (q & 1) ? cy : sy, cv = (q & 1) ? sy : cy;
-    s[e] = (q & 2) ? -sv : sv;                        // sin: s, c, -s, -c
-    c[e] = (q == 1 || q == 2) ? -cv : cv;             // cos: c, -s, -c, s
+    rope_angle_cs(pos, theta, c[e], s[e]);
     theta *= r.ratio;
   }
+}
+// Pair i alone, bit for bit what rope_cos_sin_run<n> gives for it in the run
+// that starts at the multiple of n below i (the same multiplications of theta
+// in the same order).
+template <int n>
+__device__ __forceinline__ void rope_cos_sin_pair(int pos, int i, RopeStep r, float &c, float &s) {
+  const int e = i & (n - 1);
+  double theta = exp2(-(double)(i - e) * r.step);
+#pragma unroll
+  for (int t = 0; t < n - 1; ++t) theta = (t < e) ? theta * r.ratio : theta;
+  rope_angle_cs(pos, theta, c, s);
 }
 __device__ __forceinline__ void rope_rotate(float &lo, float &hi, float c, float s) {
   const float l = lo, h = hi;
