@@ -518,7 +518,7 @@ AttnPlan plan_attn_mfma(int units, int G, int L, bool rope) {
   const int forced = env_int("KVD_ATTN_CHUNK", 0);
   // one 16-row tile per wave (prefill) needs 4 tiles per unit to keep the
   // workgroup's waves busy, and enough units to fill the chip; fewer rows
-  // (verification) share one tile across the 4 waves and split the keys
+  // (verification) share one tile across the workgroup's waves
   if ((long)units * tiles16 >= 64 && tiles16 >= 4 && forced <= 0) {
     p.rw = 4;
     p.row_tiles = (tiles16 + 3) / 4;
@@ -528,8 +528,13 @@ AttnPlan plan_attn_mfma(int units, int G, int L, bool rope) {
     p.rw = 1;
     p.row_tiles = tiles16;
     const int min_chunk = kStep * 4;
-    // as the streaming plan, with the one-workgroup limit at 64 KB (measured)
-    int chunk = (unit_bytes <= 64 * 1024) ? L : max(min_chunk, (L + 7) / 8);
+    const size_t tiles = (size_t)units * p.row_tiles;
+    // Without rotary work (which every wave repeats for the queries and new
+    // rows) and with at most 256 tiles, a workgroup of 8 waves keeps a unit of
+    // up to 128 KB of keys and values unsplit; otherwise the limit is 64 KB
+    // on 4 waves, and the keys are split as in the streaming plan.
+    const bool wide = !rope && tiles <= 256;
+    int chunk = (unit_bytes <= (wide ? 128 : 64) * 1024) ? L : max(min_chunk, (L + 7) / 8);
     if (forced > 0) chunk = forced;
     chunk = ((chunk + min_chunk - 1) / min_chunk) * min_chunk;
     const int max_splits = kMaxSplits;
@@ -538,21 +543,25 @@ AttnPlan plan_attn_mfma(int units, int G, int L, bool rope) {
       chunk = (((L + max_splits - 1) / max_splits + min_chunk - 1) / min_chunk) * min_chunk;
       splits = (L + chunk - 1) / chunk;
     }
-    const size_t tiles = (size_t)units * p.row_tiles;
     if (splits > 1 && tiles > (size_t)kMaxCounters) {
       chunk = ((L + min_chunk - 1) / min_chunk) * min_chunk;
       splits = 1;
     }
     p.chunk = chunk;
     p.splits = splits;
-    // 8 waves, one or more steps each, when every wave has a step and the
-    // workgroups are fewer than the compute units; not with rotary work, which
-    // every wave repeats for the queries and new rows (measured, 5 rows per
-    // tile: 5-row cross attention at B = 1 7.99 -> 7.24 us and the 5-draft
-    // self step at length 160 / 256 5.45 / 5.88 -> 4.96 / 5.69 us, but the
-    // cross attention of 4 batch rows, 480 workgroups, 11.4 -> 14.2 us, and
-    // GQA decode steps with rotary keys at length 768 7.6 -> 9.0 us)
-    if (!rope && chunk >= 8 * kStep && (size_t)units * p.row_tiles * splits <= 256) p.waves = 8;
+    // 8 waves there when every wave has a step, or the keys are split
+    // anyway, and the workgroups number at most 256. Measured, back-to-back
+    // periods, 5 rows per tile (5 drafts, or 5 beams sharing the cross cache):
+    // - self step, one sequence: unsplit on 8 waves at length 300 / 448 / 512
+    //   6.08 / 6.67 / 6.78 us, against 7.09 / 7.2 / 7.55 split on 4 waves; at
+    //   640 and 1024, split chunks on 8 waves 7.26 / 7.2 against 7.55 / 7.53;
+    //   up to 128 keys 4 waves stay ahead (4.28 against 4.46 us at 64);
+    // - self step, 4 sequences (80 tiles) at length 448: unsplit on 8 waves
+    //   7.4 us, against 8.4 split on 4 and 13.1 split on 8;
+    // - cross attention over 1500 frames: 7.99 -> 7.24 us on 8 waves at
+    //   B = 1 (120 workgroups), but 11.4 -> 14.2 us at B = 4 (480);
+    // - GQA decode steps with rotary keys at length 768: 7.6 -> 9.0 us.
+    if (wide && (splits > 1 || chunk >= 8 * kStep) && tiles * splits <= 256) p.waves = 8;
     const int env_waves = env_int("KVD_ATTN_WAVES", 0);
     if (env_waves == 4 || env_waves == 8) p.waves = env_waves;
   }
