@@ -529,10 +529,13 @@ AttnPlan plan_attn_mfma(int units, int G, int L, bool rope) {
     p.row_tiles = tiles16;
     const int min_chunk = kStep * 4;
     const size_t tiles = (size_t)units * p.row_tiles;
-    // Without rotary work (which every wave repeats for the queries and new
-    // rows) and with at most 256 tiles, a workgroup of 8 waves keeps a unit of
-    // up to 128 KB of keys and values unsplit; otherwise the limit is 64 KB
-    // on 4 waves, and the keys are split as in the streaming plan.
+    // Without rotary work and with at most 256 tiles, a workgroup of 8 waves
+    // keeps a unit of up to 128 KB of keys and values unsplit; otherwise the
+    // limit is 64 KB on 4 waves, and the keys are split as in the streaming
+    // plan. (GQA decode steps with rotary keys, 3 rows per tile and 24 units,
+    // measured slower on 8 waves with every chunk tried, also after the
+    // rotary values became shared: 6.95 us on 4 waves at length 768 against
+    // 8.1-8.6 on 8.)
     const bool wide = !rope && tiles <= 256;
     int chunk = (unit_bytes <= (wide ? 128 : 64) * 1024) ? L : max(min_chunk, (L + 7) / 8);
     if (forced > 0) chunk = forced;
@@ -568,7 +571,7 @@ AttnPlan plan_attn_mfma(int units, int G, int L, bool rope) {
     //   7.4 us, against 8.4 split on 4 and 13.1 split on 8;
     // - cross attention over 1500 frames: 7.99 -> 7.24 us on 8 waves at
     //   B = 1 (120 workgroups), but 11.4 -> 14.2 us at B = 4 (480);
-    // - GQA decode steps with rotary keys at length 768: 7.6 -> 9.0 us.
+    // - GQA decode steps with rotary keys at length 768: 6.95 -> 8.5 us.
     if (wide && (splits > 1 || chunk >= 8 * kStep) && tiles * splits <= 256) p.waves = 8;
     const int env_waves = env_int("KVD_ATTN_WAVES", 0);
     if (env_waves == 4 || env_waves == 8) p.waves = env_waves;
