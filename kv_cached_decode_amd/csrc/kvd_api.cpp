@@ -395,7 +395,9 @@ int decode_attn_cross(const void *q, int32_t B, int32_t Hq, int32_t N, const kvd
 size_t kvd_attn_workspace_bytes(int32_t B, int32_t Hq, int32_t N, int32_t len_max) {
   if (B < 1 || Hq < 1 || N < 1 || len_max < 1) return 0;
   // The largest plan over every grouping the calls can use (Hkv divides Hq,
-  // cache per row or shared), every dtype and every length up to len_max.
+  // cache per row or shared), every dtype, with and without rotary keys
+  // (the plans differ: rotary ones keep 4 waves and split more) and every
+  // length up to len_max.
   size_t best = 0;
   for (int hkv = 1; hkv <= Hq; ++hkv) {
     if (Hq % hkv) continue;
@@ -406,12 +408,14 @@ size_t kvd_attn_workspace_bytes(int32_t B, int32_t Hq, int32_t N, int32_t len_ma
       const int G = (shared ? B : 1) * group * N;
       // fp32, 16-bit on matrix-core tiles, 16-bit streaming (the beam step)
       for (int dt = 0; dt < 3; ++dt) {
-        for (int L = 1; L <= len_max; ++L) {
-          const AttnPlan p =
-              kvd::plan_attn(dt == 0 ? kvd::F32 : kvd::F16, units, G, N, L, false, dt != 2);
-          if (p.splits > 1) {
-            const size_t b = attn_bytes(p);
-            if (b > best) best = b;
+        for (int rope = 0; rope < 2; ++rope) {
+          for (int L = 1; L <= len_max; ++L) {
+            const AttnPlan p = kvd::plan_attn(dt == 0 ? kvd::F32 : kvd::F16, units, G, N, L,
+                                              rope != 0, dt != 2);
+            if (p.splits > 1) {
+              const size_t b = attn_bytes(p);
+              if (b > best) best = b;
+            }
           }
         }
       }

@@ -765,6 +765,42 @@ def test_step_self_equals_append_then_attend(dtype, B, Hq, Hkv, N, L, rope, plan
     assert max_err(o2, O.attend_self(q, oc, 0.125, rope_base=rope)) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype,B,Hq,Hkv,N,L,rope", [
+    ("bf16", 1, 9, 3, 1, 448, 10000.0),     # the rotary tile splits where the plain one does not
+    ("bf16", 1, 9, 3, 1, 448, 0.0),
+    ("f16", 1, 20, 20, 5, 448, 10000.0),
+    ("f16", 4, 20, 20, 5, 300, 0.0),
+    ("bf16", 2, 9, 3, 1, 1024, 10000.0),
+    ("f32", 1, 4, 4, 1, 700, 10000.0),
+])
+def test_queried_workspace_suffices(dtype, B, Hq, Hkv, N, L, rope):
+    """A workspace of exactly kvd_attn_workspace_bytes(B, Hq, N, len) serves
+    decode_attn_self and decode_step_self at that length, rotary plans
+    included, on the default plan."""
+    say(f"case: exact workspace {dtype} B={B} Hq={Hq} Hkv={Hkv} N={N} L={L} rope={rope}")
+    g = np.random.default_rng(L * 3 + N + B)
+    k_all = O.narrow(g.standard_normal((B, Hkv, L, 64)), dtype)
+    v_all = O.narrow(g.standard_normal((B, Hkv, L, 64)), dtype)
+    q = O.narrow(g.standard_normal((B, Hq, N, 64)), dtype)
+    old, new = slice(0, L - N), slice(L - N, L)
+    nbytes = kb.attn_workspace_bytes(B, Hq, N, L)
+    ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    c1 = kb.Cache(B, Hkv, L, TORCH_DTYPE[dtype])
+    c2 = kb.Cache(B, Hkv, L, TORCH_DTYPE[dtype])
+    for c in (c1, c2):
+        kb.kv_append(c, to_dev(k_all[:, :, old], dtype), to_dev(v_all[:, :, old], dtype), 0, rope)
+    kb.kv_append(c1, to_dev(k_all[:, :, new], dtype), to_dev(v_all[:, :, new], dtype), L - N, rope)
+    o1 = kb.decode_attn_self(to_dev(q, dtype), c1, L, 0.125, rope_base=rope, ws=ws)
+    o2 = kb.decode_step_self(to_dev(q, dtype), to_dev(k_all[:, :, new], dtype),
+                             to_dev(v_all[:, :, new], dtype), c2, L, 0.125, rope_base=rope, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    oc = O.ConcatCache(B, Hkv, 64, dtype)
+    oc.append(k_all[:, :, old], v_all[:, :, old], rope)
+    oc.append(k_all[:, :, new], v_all[:, :, new], rope)
+    assert max_err(o1, O.attend_self(q, oc, 0.125, rope_base=rope)) <= TOL[dtype]
+
+
 # ------------------------------------------ fused beam step (two caches) ----
 
 @pytest.mark.parametrize("dtype,B,Hq,Hkv,N,L,rope", [
