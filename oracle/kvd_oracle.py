@@ -39,6 +39,8 @@ before the K-th next beam recorded as finished.
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 # ---------------------------------------------------------------------------
@@ -93,15 +95,25 @@ def narrow(x: np.ndarray, dtype: str) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 
+def rope_theta(base: float, D: int) -> np.ndarray:
+    """theta_i = base^(-2i/D) for i < D/2, each the C library's float64 pow
+    of the exact exponent -2i/D (math.pow; a vectorised numpy power may
+    round differently from one CPU to the next)."""
+    return np.array([math.pow(float(base), -(2.0 * i) / D) for i in range(D // 2)],
+                    dtype=np.float64)
+
+
 def rope(x: np.ndarray, positions, base: float) -> np.ndarray:
     """Rotate float64 rows x[..., t, :] by position positions[t].
 
-    Pairs (i, i + D/2) turn by angle p * base^(-2i/D).
+    Pairs (i, i + D/2) turn by angle p * theta_i, one float64 product, with
+    theta_i = base^(-2i/D); then (lo, hi) -> (lo c - hi s, hi c + lo s) with
+    every product and sum rounded in float64.
     """
     x = np.asarray(x, dtype=np.float64)
     D = x.shape[-1]
     half = D // 2
-    theta = base ** (-(2.0 * np.arange(half)) / D)
+    theta = rope_theta(base, D)
     ang = np.asarray(positions, dtype=np.float64)[:, None] * theta[None, :]
     c, s = np.cos(ang), np.sin(ang)
     lo, hi = x[..., :half], x[..., half:]

@@ -111,6 +111,120 @@ def test_rope_scores_depend_on_relative_position_only():
     assert norms[0] == pytest.approx(norms[1], rel=1e-14)
 
 
+# Exact arithmetic for the stored rotated keys: 50 significant digits, pi
+# from Machin's formula, cos / sin from their Taylor series, and rounding to
+# the storage type by hand (none of numpy's trigonometry or rounding).
+_DEC = 50
+
+
+def _dec_pi():
+    from decimal import Decimal, localcontext
+    with localcontext() as ctx:
+        ctx.prec = _DEC + 10
+
+        def arctan_inv(n):
+            x = Decimal(1) / n
+            total, term, k, sign = x, x, 1, -1
+            while True:
+                term = term / (n * n)
+                step = term / (2 * k + 1)
+                if step < Decimal(10) ** -(_DEC + 8):
+                    return total
+                total += sign * step
+                sign, k = -sign, k + 1
+        return 16 * arctan_inv(5) - 4 * arctan_inv(239)
+
+
+def _dec_cos_sin(angle: float):
+    from decimal import Decimal, localcontext
+    with localcontext() as ctx:
+        ctx.prec = _DEC + 10
+        x = Decimal(angle)                        # the float64 angle, exactly
+        half_pi = _dec_pi() / 2
+        k = int((x / half_pi).to_integral_value())
+        y = x - k * half_pi
+        c, s, term, n = Decimal(0), Decimal(0), Decimal(1), 0
+        while True:                               # term = y^n / n!
+            if n % 4 == 0:
+                c += term
+            elif n % 4 == 1:
+                s += term
+            elif n % 4 == 2:
+                c -= term
+            else:
+                s -= term
+            n += 1
+            term = term * y / n
+            if abs(term) < Decimal(10) ** -(_DEC + 8):
+                break
+        for _ in range(k % 4):                    # turn by pi/2 per quadrant
+            c, s = -s, c
+        return c, s
+
+
+def _round_to(v, dtype):
+    """Nearest storage value of the Decimal v (ties to even), and its
+    distance to the nearest rounding boundary in units of the spacing."""
+    from fractions import Fraction
+    f = Fraction(v)
+    if f == 0:
+        return 0.0, 1.0
+    bits = 8 if dtype == "bf16" else 11
+    e = math.floor(math.log2(abs(f)))
+    if Fraction(2) ** e > abs(f):
+        e -= 1
+    elif Fraction(2) ** (e + 1) <= abs(f):
+        e += 1
+    e = max(e, (-126 if dtype == "bf16" else -14))   # subnormal spacing below
+    q = Fraction(2) ** (e - bits + 1)
+    t = f / q
+    lo = math.floor(t)
+    frac = t - lo
+    n = lo + 1 if frac > Fraction(1, 2) or (frac == Fraction(1, 2) and lo % 2) else lo
+    return float(n * q), float(abs(frac - Fraction(1, 2)))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_rope_stored_keys_are_the_exact_rotation_rounded_once(dtype):
+    """A rotated key stored by the oracle is the exact rotation of the stored
+    input by the angle p * theta_i, rounded once to the storage type: checked
+    in 50-digit arithmetic on random rows at positions up to 4096, pairs
+    across the whole frequency range."""
+    from decimal import Decimal
+    g = np.random.default_rng(11 if dtype == "bf16" else 12)
+    D, T = 64, 24
+    x = O.narrow(g.standard_normal((T, D)), dtype)
+    pos = np.concatenate([[0, 1, 2, 1023, 1024, 4095], g.integers(0, 4096, T - 6)])
+    got = O.widen(O.narrow(O.rope(O.widen(x, dtype), pos, 1e4), dtype), dtype)
+    xw = O.widen(x, dtype)
+    theta = O.rope_theta(1e4, D)
+    checked = 0
+    for t in range(T):
+        for i in range(D // 2):
+            c, s = _dec_cos_sin(float(pos[t]) * theta[i])     # the angle one float64 product
+            lo, hi = Decimal(float(xw[t, i])), Decimal(float(xw[t, i + D // 2]))
+            for col, v in ((i, lo * c - hi * s), (i + D // 2, hi * c + lo * s)):
+                want, margin = _round_to(v, dtype)
+                if margin < 1e-9:      # too near a boundary to decide in 50 digits: none expected
+                    continue
+                assert got[t, col] == want, (t, i, col, got[t, col], want)
+                checked += 1
+    assert checked >= 2 * D // 2 * T - 2
+
+
+def test_rope_theta_is_the_correctly_rounded_power():
+    """theta_i = 10000^(-2i/64) to within half an ulp of the 50-digit value
+    (one rounding of the exact power)."""
+    from decimal import Decimal, localcontext
+    th = O.rope_theta(1e4, 64)
+    for i in range(32):
+        with localcontext() as ctx:
+            ctx.prec = _DEC
+            exact = Decimal(10000) ** (Decimal(-2 * i) / Decimal(64))
+        err = abs(Decimal(float(th[i])) - exact)
+        assert err <= Decimal(math.ulp(float(th[i]))) / 2 * Decimal("1.0000001"), (i, th[i], exact)
+
+
 # ------------------------------------------------------------- attention ----
 
 def _sdpa(q, k, v, scale, causal_offset):
