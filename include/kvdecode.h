@@ -27,8 +27,9 @@
  *     accumulates in fp32 and writes fp32 output.
  *   - Head dimension D must be 64.
  *   - All device buffers are contiguous, row-major in the order written, and
- *     16-byte aligned, except where a call states otherwise. The caller owns every buffer; the library allocates
- *     nothing and keeps no state between calls.
+ *     16-byte aligned, except where a call states otherwise. The caller owns
+ *     every buffer; the library allocates nothing and keeps no state between
+ *     calls (besides the testing hook's forced plan).
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
  *     default stream). Calls are thread-safe; two calls that share a
  *     workspace must be ordered (same stream).
@@ -36,7 +37,9 @@
  *     KVD_ERR_LAUNCH is decided on the host before any HIP call, so nothing is
  *     enqueued when a call fails.
  *   - Results are deterministic: split counts depend only on the shape and
- *     every reduction runs in a fixed order.
+ *     every reduction runs in a fixed order. The one exception is a plan a
+ *     test forces with kvd_set_plan_override (declared below, off unless
+ *     called); the library reads no environment variable.
  */
 #ifndef KVDECODE_H
 #define KVDECODE_H
@@ -318,6 +321,30 @@ size_t kvd_beam_workspace_bytes(int32_t B, int32_t K, int32_t V);
  *   sink: device uint32, 4-byte aligned.
  * Errors: KVD_ERR_NULL, KVD_ERR_SHAPE, KVD_ERR_ALIGN, KVD_ERR_LAUNCH. */
 int kvd_read_probe(const void *a, const void *b, size_t bytes, uint32_t *sink, void *stream);
+
+/* The same read with its shape chosen by the caller, so that the yardstick
+ * can be the fastest of several: every thread keeps `unroll` 16-byte loads in
+ * flight per round (1, 2, 4, 8 or 16), over `blocks` workgroups of 256
+ * threads (1 .. 65535; 0: enough for one round of loads per thread), reading
+ * a's vectors and then b's as one grid-stride sequence. kvd_read_probe is
+ * unroll 4, blocks 0.
+ * Errors: as kvd_read_probe; KVD_ERR_SHAPE also for another unroll or
+ * blocks > 65535. */
+int kvd_read_probe_ex(const void *a, const void *b, size_t bytes, uint32_t *sink, int32_t unroll,
+                      size_t blocks, void *stream);
+
+/* Testing hook: force the split plan of every later attention call and
+ * workspace query in this process, so tests can reach plans the shapes they
+ * use would not get. mfma: -1 plan as usual, 0 keep 16-bit caches on the
+ * streaming kernel (1 is the same as -1); waves: waves per workgroup (0: as
+ * planned; the planner keeps only values its kernel supports); chunk: keys
+ * per split (0: as planned). kvd_set_plan_override(-1, 0, 0) restores the
+ * default, under which the plan is a pure function of the call's shape. A
+ * workspace sized under one setting may be too small under another (the
+ * call then returns KVD_ERR_WORKSPACE). Not for use while other threads
+ * make calls.
+ * Errors: KVD_ERR_SHAPE for values outside those ranges. */
+int kvd_set_plan_override(int32_t mfma, int32_t waves, int32_t chunk);
 
 /* Profiling aid: the next kernel launch made by the calling thread records
  * `start_event` when the kernel begins and `stop_event` when it ends (created

@@ -77,6 +77,9 @@ _SIGNATURES = {
     "kvd_status_string": (ctypes.c_char_p, [c_int]),
     "kvd_time_next_launch": (c_int, [c_void_p, c_void_p]),
     "kvd_read_probe": (c_int, [c_void_p, c_void_p, c_size_t, c_void_p, c_void_p]),
+    "kvd_read_probe_ex": (c_int, [c_void_p, c_void_p, c_size_t, c_void_p, c_int32, c_size_t,
+                                  c_void_p]),
+    "kvd_set_plan_override": (c_int, [c_int32, c_int32, c_int32]),
 }
 
 
@@ -178,12 +181,34 @@ def time_next_launch(start: "torch.cuda.Event", stop: "torch.cuda.Event"):
     _check("kvd_time_next_launch", lib().kvd_time_next_launch(start.cuda_event, stop.cuda_event))
 
 
-def read_probe(a: torch.Tensor, b: torch.Tensor | None, nbytes: int, sink: torch.Tensor):
+def read_probe(a: torch.Tensor, b: torch.Tensor | None, nbytes: int, sink: torch.Tensor,
+               unroll: int = 4, blocks: int = 0):
     """Plain streaming read of nbytes from a (and from b): the attainable
-    rate for one launch that reads that much."""
-    _check("kvd_read_probe", lib().kvd_read_probe(
+    rate for one launch that reads that much. unroll: loads in flight per
+    thread; blocks: workgroups of 256 threads (0: one round of loads)."""
+    _check("kvd_read_probe_ex", lib().kvd_read_probe_ex(
         _dev(a, "a"), _dev(b, "b") if b is not None else None, int(nbytes), _dev(sink, "sink"),
-        _stream()))
+        int(unroll), int(blocks), _stream()))
+
+
+class plan_override:
+    """Context manager that forces the attention split plan of the calls made
+    inside it (a testing hook: kvd_set_plan_override). mfma=0 keeps 16-bit
+    caches on the streaming kernel; waves / chunk force the waves per
+    workgroup and the keys per split; None leaves each as planned. Workspace
+    sizes queried inside the block follow the forced plan."""
+
+    def __init__(self, mfma: int | None = None, waves: int | None = None, chunk: int | None = None):
+        self.args = (-1 if mfma is None else int(mfma), 0 if waves is None else int(waves),
+                     0 if chunk is None else int(chunk))
+
+    def __enter__(self):
+        _check("kvd_set_plan_override", lib().kvd_set_plan_override(*self.args))
+        return self
+
+    def __exit__(self, *exc):
+        _check("kvd_set_plan_override", lib().kvd_set_plan_override(-1, 0, 0))
+        return False
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:

@@ -8,12 +8,14 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvdecode.so")
+OBJ_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["kvd_copy.hip", "kvd_attn.hip", "kvd_attn_mfma.hip", "kvd_verify.hip", "kvd_beam.hip",
            "kvd_probe.hip",
            "kvd_api.cpp"]
@@ -41,22 +43,36 @@ def compile_flags() -> list[str]:
     ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libkvdecode.so; returns its path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *compile_flags(), "-shared", "-o", tmp,
-           *[os.path.join(CSRC, s) for s in SOURCES]]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with status {res.returncode}")
+        raise RuntimeError(f"hipcc failed with status {res.returncode}: {cmd[-1]}")
     if verbose and res.stderr.strip():
         # the host pass does not know the packed-fp32 feature and says so
         msgs = [ln for ln in res.stderr.splitlines() if "packed-fp32-ops" not in ln]
         if msgs:
             sys.stderr.write("\n".join(msgs) + "\n")
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    """Compile every source (one hipcc per file, in parallel) and link
+    libkvdecode.so; returns its path."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    cc, flags = hipcc(), compile_flags()
+    objs, cmds = [], []
+    for s in SOURCES:
+        o = os.path.join(OBJ_DIR, os.path.splitext(s)[0] + ".o")
+        objs.append(o)
+        cmds.append([cc, *flags, "-c", "-o", o, os.path.join(CSRC, s)])
+    jobs = jobs or min(len(cmds), max(1, min(8, os.cpu_count() or 1)))
+    with ThreadPoolExecutor(jobs) as ex:
+        for f in [ex.submit(_run, c, verbose) for c in cmds]:
+            f.result()
+    tmp = LIB + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
     return LIB
 

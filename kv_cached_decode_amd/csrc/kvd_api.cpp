@@ -39,9 +39,30 @@ int check_cache(const kvd_cache *c) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? KVD_OK : KVD_ERR_LAUNCH; }
 
-// Rotary angle step: theta_i = base^(-2i/D) = 2^(-i * step).
-double rope_step_of(float rope_base) {
-  return rope_base > 0.f ? 2.0 * log2((double)rope_base) / kvd::kHeadDim : 0.0;
+// Rotary angles theta_i = base^(-2i/D), i < D/2, each the C library's fp64
+// pow of the exact exponent -2i/D ([N] "nanoVLM における技術的実装", item 2:
+// rotary positions at start_pos; the RoFormer frequencies); zeros without
+// rotation.
+// Returns false if a correction does not fit its byte (never seen: at most
+// 24 ulps for bases 1e-3 .. 3.4e38).
+bool rope_theta_of(float rope_base, kvd::RopeTheta &r) {
+  r = kvd::RopeTheta{};
+  if (!(rope_base > 0.f)) return true;
+  const double base = rope_base;
+  r.pw[0] = pow(base, -2.0 / kvd::kHeadDim);
+  for (int k = 1; k < 5; ++k) r.pw[k] = r.pw[k - 1] * r.pw[k - 1];
+  for (int i = 0; i < kvd::kHeadDim / 2; ++i) {
+    double t = 1.0;
+    for (int k = 0; k < 5; ++k) t = t * (((i >> k) & 1) ? r.pw[k] : 1.0);
+    const double theta = pow(base, -2.0 * i / kvd::kHeadDim);
+    int64_t bt, bp;
+    memcpy(&bt, &theta, 8);
+    memcpy(&bp, &t, 8);
+    const int64_t d = bt - bp;
+    if (d < -128 || d > 127) return false;
+    r.delta[i / 4] |= (uint32_t)(uint8_t)(int8_t)d << (8 * (i % 4));
+  }
+  return true;
 }
 
 // Every workspace starts with a fixed block of arrival counters, zero at rest
@@ -104,12 +125,24 @@ kvd::LaunchTiming kvd::take_launch_timing() {
 
 extern "C" {
 
-int kvd_read_probe(const void *a, const void *b, size_t bytes, uint32_t *sink, void *stream) {
+int kvd_read_probe_ex(const void *a, const void *b, size_t bytes, uint32_t *sink, int32_t unroll,
+                      size_t blocks, void *stream) {
   if (!a || !sink) return KVD_ERR_NULL;
-  if (bytes == 0 || bytes % 16) return KVD_ERR_SHAPE;
+  if (bytes == 0 || bytes % 16 || !kvd::probe_unroll_ok(unroll) || blocks > 65535)
+    return KVD_ERR_SHAPE;
   if (!aligned16(a) || (b && !aligned16(b)) || !aligned4(sink)) return KVD_ERR_ALIGN;
-  kvd::ProbeArgs p{a, b, bytes / 16, sink};
+  kvd::ProbeArgs p{a, b, bytes / 16, sink, unroll, blocks};
   return status_of(kvd::launch_probe(p, static_cast<hipStream_t>(stream)));
+}
+
+int kvd_read_probe(const void *a, const void *b, size_t bytes, uint32_t *sink, void *stream) {
+  return kvd_read_probe_ex(a, b, bytes, sink, 4, 0, stream);
+}
+
+int kvd_set_plan_override(int32_t mfma, int32_t waves, int32_t chunk) {
+  if (mfma < -1 || mfma > 1 || waves < 0 || waves > 16 || chunk < 0) return KVD_ERR_SHAPE;
+  kvd::set_plan_override(kvd::PlanOverride{mfma, waves, chunk});
+  return KVD_OK;
 }
 
 int kvd_time_next_launch(void *start_event, void *stop_event) {
@@ -163,8 +196,7 @@ int append_impl(const kvd_cache *cache, const void *k_new, const void *v_new, in
   a.T = T;
   a.pos = pos;
   a.rope_base = rope_base;
-  a.rope_step = rope_step_of(rope_base);
-  a.rope_ratio = exp2(-a.rope_step);
+  if (!rope_theta_of(rope_base, a.rope_theta)) return KVD_ERR_SHAPE;
   return status_of(kvd::launch_append(cache->dtype, a, static_cast<hipStream_t>(stream)));
 }
 
@@ -253,8 +285,9 @@ int prepare_self(AttnArgs &a, const void *q, const void *k_new, const void *v_ne
   a.T_new = k_new ? N : 0;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.rope_base = rope_base;
-  a.rope_step = rope_step_of(rope_base);
+  a.rope_step = rope_base > 0.f ? 2.0 * log2((double)rope_base) / kvd::kHeadDim : 0.0;
   a.rope_ratio = exp2(-a.rope_step);
+  if (!rope_theta_of(rope_base, a.rope_theta)) return KVD_ERR_SHAPE;
   return prepare_attn(a, cache->dtype, ws, ws_bytes);
 }
 
@@ -294,8 +327,7 @@ int decode_step_self(const void *q, const void *k_new, const void *v_new, int32_
     ap.T = N;
     ap.pos = len - N;
     ap.rope_base = rope_base;
-    ap.rope_step = rope_step_of(rope_base);
-    ap.rope_ratio = exp2(-ap.rope_step);
+    ap.rope_theta = a.rope_theta;  // built (and checked) by prepare_self
     const int sa = status_of(kvd::launch_append(cache->dtype, ap, s));
     if (sa) return sa;
   }

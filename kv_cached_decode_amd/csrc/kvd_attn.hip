@@ -20,6 +20,8 @@
 // need no ordering within the launch.
 #include <stdlib.h>
 
+#include <atomic>
+
 #include "kvd_attn_common.hpp"
 #include "kvd_device.hpp"
 #include "kvd_internal.hpp"
@@ -178,8 +180,14 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
   // ---- rotary cos / sin at the first row's position: no memory access, so
   // they are computed while the loads above are in flight
   float rc[ROPE ? VE : 1], rs[ROPE ? VE : 1];  // cos / sin at position rpos
+  double thn[ROPE && FUSED ? VE : 1];           // exact angles of the lane's new-key pairs
   int rpos = -1;
   if constexpr (ROPE) {
+    if constexpr (FUSED) {
+      constexpr int HALF_VECS = kHeadDim / 2 / VE;  // the new-row loop's pair chunk is fixed per lane
+#pragma unroll
+      for (int e = 0; e < VE; ++e) thn[e] = rope_theta_at(a.rope_theta, (threadIdx.x % HALF_VECS) * VE + e);
+    }
     rpos = sp.causal_base + row_id(a, bkv, hk, g0).i;
     rope_slice_cs<DT>(ds, rpos, RopeStep{a.rope_step, a.rope_ratio}, rc, rs);
   }
@@ -197,7 +205,7 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
       const int r = t / HALF_VECS, j = t % HALF_VECS;
       const int pos = nb0 + r;
       const size_t src = (size_t)(pos - sp.new_base) * ROWB;
-      const PairChunks c = load_pair<DT>(kn + src, vn + src, j, pos, RopeStep{ROPE ? a.rope_step : 0.0, a.rope_ratio});
+      const PairChunks c = load_pair<DT, true>(kn + src, vn + src, j, pos, ROPE ? thn : nullptr);
       s_new[r * VPR + j] = c.klo;
       s_new[r * VPR + j + VPR / 2] = c.khi;
       s_new[(kMaxFusedRows + r) * VPR + j] = c.vlo;
@@ -496,12 +504,23 @@ void launch_dt(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
   else launch_rg<DT, FUSED, false>(a, grid, block, s);
 }
 
-int env_int(const char *name, int dflt) {
-  const char *v = getenv(name);
-  return (v && *v) ? atoi(v) : dflt;
-}
+// The testing hook's forced plan: one process-wide setting, read at every
+// planning call; at rest (the default) nothing is forced.
+std::atomic<int> g_force_mfma{-1}, g_force_waves{0}, g_force_chunk{0};
 
 }  // namespace
+
+PlanOverride plan_override() {
+  return PlanOverride{g_force_mfma.load(std::memory_order_relaxed),
+                      g_force_waves.load(std::memory_order_relaxed),
+                      g_force_chunk.load(std::memory_order_relaxed)};
+}
+
+void set_plan_override(PlanOverride o) {
+  g_force_mfma.store(o.mfma, std::memory_order_relaxed);
+  g_force_waves.store(o.waves, std::memory_order_relaxed);
+  g_force_chunk.store(o.chunk, std::memory_order_relaxed);
+}
 
 // Matrix-core tile plan (blocks of queries, 16-bit storage): 16-row tiles;
 // four tiles per workgroup and one split when there are enough tiles to fill
@@ -515,7 +534,8 @@ AttnPlan plan_attn_mfma(int units, int G, int L, bool rope) {
   p.waves = 4;
   const int tiles16 = (G + kRows - 1) / kRows;
   const long unit_bytes = (long)L * 2 * kHeadDim * 2;
-  const int forced = env_int("KVD_ATTN_CHUNK", 0);
+  const PlanOverride ov = plan_override();
+  const int forced = ov.chunk;
   // one 16-row tile per wave (prefill) needs 4 tiles per unit to keep the
   // workgroup's waves busy, and enough units to fill the chip; fewer rows
   // (verification) share one tile across the workgroup's waves
@@ -573,8 +593,7 @@ AttnPlan plan_attn_mfma(int units, int G, int L, bool rope) {
     //   B = 1 (120 workgroups), but 11.4 -> 14.2 us at B = 4 (480);
     // - GQA decode steps with rotary keys at length 768: 6.95 -> 8.5 us.
     if (wide && (splits > 1 || chunk >= 8 * kStep) && tiles * splits <= 256) p.waves = 8;
-    const int env_waves = env_int("KVD_ATTN_WAVES", 0);
-    if (env_waves == 4 || env_waves == 8) p.waves = env_waves;
+    if (ov.waves == 4 || (ov.waves == 8 && !rope)) p.waves = ov.waves;  // rotary: 4 waves
   }
   const size_t tiles = (size_t)units * p.row_tiles;
   p.part_floats = (p.splits > 1) ? tiles * p.splits * kRows * kPStride : 0;
@@ -595,9 +614,8 @@ hipError_t launch_attn(int dtype, const AttnArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Split plan: a pure function of the shape (and of the tuning variables
-// KVD_ATTN_WAVES / KVD_ATTN_CHUNK when set), so results are reproducible run
-// to run. The thresholds come from timing back-to-back launches in a graph on
+// Split plan: a pure function of the shape (unless a test forces a plan
+// through kvd_set_plan_override), so results are reproducible run to run. The thresholds come from timing back-to-back launches in a graph on
 // MI355X: up to 96 KB of keys a unit stays on one workgroup (8 waves above
 // 40 KB with one query row), which avoids the cross-workgroup merge (two
 // memory round trips: the arrival count, then the partials); beyond that the
@@ -608,8 +626,8 @@ AttnPlan plan_attn(int dtype, int units, int G, int N, int L, bool rope, bool al
   // G >= 3 rows from grouped heads or beams sharing one cache (measured: 3
   // GQA rows 12% and 5 beam rows 31% faster per decode step than 4- and 8-row
   // streaming tiles; 2 rows stay on the streaming kernel).
-  const bool use_mfma =
-      allow_mfma && dtype != F32 && (N > 1 || G >= 3) && env_int("KVD_ATTN_MFMA", 1) != 0;
+  const PlanOverride ov = plan_override();
+  const bool use_mfma = allow_mfma && dtype != F32 && (N > 1 || G >= 3) && ov.mfma != 0;
   if (use_mfma) return plan_attn_mfma(units, G, L, rope);
   p.gm = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
   p.row_tiles = (G + p.gm - 1) / p.gm;
@@ -633,12 +651,10 @@ AttnPlan plan_attn(int dtype, int units, int G, int N, int L, bool rope, bool al
     const int c4 = ((chunk + 4 * tile - 1) / (4 * tile)) * (4 * tile);
     if (wide_ok && c4 % (8 * tile) == 0) waves = 8;
   }
-  const int env_waves = env_int("KVD_ATTN_WAVES", 0);
-  if (env_waves == 1 || env_waves == 2 || env_waves == 4 ||
-      ((env_waves == 8 || env_waves == kMaxWaves) && wide_ok))
-    waves = env_waves;
-  const int forced = env_int("KVD_ATTN_CHUNK", 0);
-  if (forced > 0) chunk = forced;
+  if (ov.waves == 1 || ov.waves == 2 || ov.waves == 4 ||
+      ((ov.waves == 8 || ov.waves == kMaxWaves) && wide_ok))
+    waves = ov.waves;
+  if (ov.chunk > 0) chunk = ov.chunk;
   p.waves = waves;
 
   const int min_chunk = tile * waves;

@@ -146,19 +146,48 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
   }
   // ---- this lane's query row. Without new rows its loads go out before the
   // first key loads (measured: 5-row cross attention 7.25 -> 7.08 us); the
-  // fused kernels keep them after (measured slower the other way round)
+  // fused kernels keep them after (measured slower the other way round),
+  // except with rotary work: that waits for the query and the new rows, and
+  // vector loads complete in issue order, so behind the key loads it would
+  // start only once they had all landed, instead of under their latency.
+  constexpr bool kSmallFirst = !FUSED || ROPE;
   const int grow = rt * kRows + c;
   const bool active = grow < a.G;
   RowId r{0, 0, 0};
   if (active) r = row_id(a, bkv, hk, grow);
   u32x4 qraw[2] = {u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}};
-  if constexpr (!FUSED) {
+  auto load_q = [&]() {
     if (active) {
       const char *qrow = static_cast<const char *>(a.q) + out_row(a, r) * 2;
       qraw[0] = load16(qrow + gq * 16);
       qraw[1] = load16(qrow + 64 + gq * 16);
     }
-  }
+  };
+  if constexpr (kSmallFirst) load_q();
+
+  // ---- new rows (decode_step_self): a wave that needs them loads them,
+  // rotates them (exactly as kv_append does) while its key loads are in
+  // flight, and keeps them in its own slice of LDS, so no barrier is needed.
+  // Lane l takes chunk pair l % 4 of new row l / 4 (N <= 16 rows: one each).
+  constexpr int kNewSlice = 2 * kMaxFusedRows * VPR;  // K rows, then V rows
+  __shared__ u32x4 s_new[FUSED ? NW * kNewSlice : 1];
+  u32x4 *my_new = s_new + (FUSED ? wave * kNewSlice : 0);
+  const int new_items = takes_new ? (kspan - nb0) * (VPR / 2) : 0;  // uniform
+  PairChunks nw{};
+  auto load_new = [&]() {
+    if (lane < new_items) {
+      const char *krow = static_cast<const char *>(a.k_new) +
+                         (head * a.T_new + (nb0 - sp.new_base) + lane / 4) * ROWB;
+      const char *vrow = static_cast<const char *>(a.v_new) +
+                         (head * a.T_new + (nb0 - sp.new_base) + lane / 4) * ROWB;
+      const int j = lane % 4;
+      nw.klo = load16(krow + j * 16);
+      nw.khi = load16(krow + 64 + j * 16);
+      nw.vlo = load16(vrow + j * 16);
+      nw.vhi = load16(vrow + 64 + j * 16);
+    }
+  };
+  if constexpr (FUSED && kSmallFirst) load_new();
 
   const int kend_lo = min(kspan, (sp.causal_base < 0) ? sp.L : sp.causal_base + 1);
   const bool early = s0 + kStep <= kend_lo && (!FUSED || s0 + kStep <= nb0);  // uniform
@@ -173,13 +202,7 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
 
   // ---- query operand: dims [8gq, +8) and [32 + 8gq, +8) of the row; a rotary
   // pair (i, i + 32) sits in one lane
-  if constexpr (FUSED) {
-    if (active) {
-      const char *qrow = static_cast<const char *>(a.q) + out_row(a, r) * 2;
-      qraw[0] = load16(qrow + gq * 16);
-      qraw[1] = load16(qrow + 64 + gq * 16);
-    }
-  }
+  if constexpr (!kSmallFirst) load_q();
 
   float m = -INFINITY, lsum = 0.f;
   f32x4 o[4];
@@ -187,28 +210,7 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
   for (int t = 0; t < 4; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   u32x4 qhi[2], qlo[2];  // the query operand, set once the q loads are back
 
-  // ---- new rows (decode_step_self): a wave that needs them loads them,
-  // rotates them (exactly as kv_append does) while its key loads are in
-  // flight, and keeps them in its own slice of LDS, so no barrier is needed.
-  // Lane l takes chunk pair l % 4 of new row l / 4 (N <= 16 rows: one each).
-  constexpr int kNewSlice = 2 * kMaxFusedRows * VPR;  // K rows, then V rows
-  __shared__ u32x4 s_new[FUSED ? NW * kNewSlice : 1];
-  u32x4 *my_new = s_new + (FUSED ? wave * kNewSlice : 0);
-  const int new_items = takes_new ? (kspan - nb0) * (VPR / 2) : 0;  // uniform
-  PairChunks nw{};
-  if constexpr (FUSED) {
-    if (lane < new_items) {
-      const char *krow = static_cast<const char *>(a.k_new) +
-                         (head * a.T_new + (nb0 - sp.new_base) + lane / 4) * ROWB;
-      const char *vrow = static_cast<const char *>(a.v_new) +
-                         (head * a.T_new + (nb0 - sp.new_base) + lane / 4) * ROWB;
-      const int j = lane % 4;
-      nw.klo = load16(krow + j * 16);
-      nw.khi = load16(krow + 64 + j * 16);
-      nw.vlo = load16(vrow + j * 16);
-      nw.vhi = load16(vrow + 64 + j * 16);
-    }
-  }
+  if constexpr (FUSED && !kSmallFirst) load_new();
 
   // One 32-key step: its loads, then its scores, softmax update and P.V.
   auto load_step = [&](int s0, u32x4 (&ka)[2][2], u32x2 (&vv)[8]) {
@@ -337,16 +339,18 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
   // access, so they are all computed while the loads above are in flight (the
   // scheduling barrier keeps the compiler from moving the first use of a
   // loaded value, and so the wait for it, in between)
-  float ncs[ROPE && FUSED ? 8 : 1], nsn[ROPE && FUSED ? 8 : 1];
+  double ncs[ROPE && FUSED ? 8 : 1], nsn[ROPE && FUSED ? 8 : 1];  // new keys: fp64
   float qc[ROPE ? 8 : 1], qs[ROPE ? 8 : 1];
   // Fused steps of up to 16 rows (new rows where the queries are), and one
   // query without new rows: every position the tile needs lies in
-  // causal_base + [0, N), so the wave computes the cos / sin of those N x 32
-  // pairs once, one pair per lane at a time, into its own LDS slice
+  // causal_base + [0, N), so the wave computes the fp32 cos / sin of those
+  // N x 32 pairs once, one pair per lane at a time, into its own LDS slice
   // (position p: cos in slots 64p .. 64p + 31, sin in the next 32), and each
-  // lane reads its values back. (Without new rows and N > 1 a lane's own 8
-  // query pairs cost about as much as its share of the table: measured
-  // 4.72 against 4.91 us for 5 queries at length 64.)
+  // lane reads its query's values back. The new keys are then rotated one
+  // pair per lane in the wave's LDS slice (pair_rot below), each with its
+  // own fp64 cos / sin. (Without new rows and N > 1 a lane's own 8 query
+  // pairs cost about as much as its share of the table: measured 4.72
+  // against 4.91 us for 5 queries at length 64.)
   constexpr int kRopeSlice = kMaxFusedRows * 64;
   __shared__ __attribute__((aligned(16))) float s_rope[(ROPE && RW == 1) ? NW * kRopeSlice : 1];
   bool shared_cs = false;
@@ -356,11 +360,11 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
     if constexpr (ROPE && RW == 1) {
       float *tab = s_rope + wave * kRopeSlice;
       for (int idx = lane; idx < a.N * 32; idx += 64) {
+        const int pos = sp.causal_base + idx / 32, slot = (idx / 32) * 64 + idx % 32;
         float cl, sl;
-        rope_cos_sin_pair<8>(sp.causal_base + idx / 32, idx % 32, RopeStep{a.rope_step, a.rope_ratio}, cl,
-                             sl);
-        tab[(idx / 32) * 64 + idx % 32] = cl;
-        tab[(idx / 32) * 64 + 32 + idx % 32] = sl;
+        rope_cos_sin_pair<8>(pos, idx % 32, RopeStep{a.rope_step, a.rope_ratio}, cl, sl);
+        tab[slot] = cl;
+        tab[slot + 32] = sl;
       }
       asm volatile("" ::: "memory");  // the slice is written before the wave reads it
       const float *qt = tab + r.i * 64 + 8 * gq;
@@ -369,39 +373,61 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
         qc[e] = qt[e];
         qs[e] = qt[32 + e];
       }
-      if constexpr (FUSED) {
-        if (lane < new_items) {
-          const float *nt = tab + (nb0 + lane / 4 - sp.causal_base) * 64 + 8 * (lane % 4);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            ncs[e] = nt[e];
-            nsn[e] = nt[32 + e];
-          }
-        }
-      }
     }
   } else {
     if constexpr (ROPE && FUSED) {
-      if (lane < new_items)
-        rope_cos_sin_run<8>(nb0 + lane / 4, (lane % 4) * 8, RopeStep{a.rope_step, a.rope_ratio}, ncs, nsn);
+      double thn[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) thn[e] = rope_theta_at(a.rope_theta, (lane % 4) * 8 + e);
+      if (lane < new_items) rope_cos_sin_run64<8>(nb0 + lane / 4, thn, ncs, nsn);
     }
     if constexpr (ROPE)
       rope_cos_sin_run<8>(sp.causal_base + r.i, gq * 8, RopeStep{a.rope_step, a.rope_ratio}, qc, qs);
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- the new rows, rotated (as kv_append rotates them) into the wave's slice
+  // ---- the new rows into the wave's slice, keys rotated as kv_append
+  // rotates them: per lane (8 pairs each) off the shared table, else one pair
+  // per lane in the slice, then stored from there
   if constexpr (FUSED) {
+    const bool pair_rot = ROPE && shared_cs;  // uniform
     if (lane < new_items) {
       const int rr = lane / 4, j = lane % 4, pos = nb0 + rr;
-      if constexpr (ROPE) rotate_key_pair_cs<DT>(nw.klo, nw.khi, ncs, nsn);
+      if constexpr (ROPE) {
+        if (!pair_rot) rotate_key_pair_cs<DT>(nw.klo, nw.khi, ncs, nsn);
+      }
       my_new[rr * VPR + j] = nw.klo;
       my_new[rr * VPR + j + VPR / 2] = nw.khi;
       my_new[(kMaxFusedRows + rr) * VPR + j] = nw.vlo;
       my_new[(kMaxFusedRows + rr) * VPR + j + VPR / 2] = nw.vhi;
-      if (store_new) store_pair<DT>(kc + (size_t)pos * ROWB, vc + (size_t)pos * ROWB, j, nw);
+      if (store_new && !pair_rot) store_pair<DT>(kc + (size_t)pos * ROWB, vc + (size_t)pos * ROWB, j, nw);
     }
     asm volatile("" ::: "memory");  // the slice is written before the wave reads it
+    if constexpr (ROPE) {
+      if (pair_rot && new_items > 0) {  // uniform
+        const int rows = new_items / (VPR / 2);
+        const double th = rope_theta_at(a.rope_theta, lane & 31);  // exact, as kv_append's
+        for (int item = lane; item < rows * 32; item += 64) {  // pair item % 32 == lane % 32
+          const int rr = item / 32, pr = item % 32;
+          double c64, s64;
+          rope_angle_cs64(nb0 + rr, th, c64, s64);
+          uint16_t *kr = reinterpret_cast<uint16_t *>(my_new + rr * VPR);
+          float lo = widen16<DT>(kr[pr]), hi = widen16<DT>(kr[pr + kHeadDim / 2]);
+          rotate_elem64<DT>(lo, hi, c64, s64);
+          const uint32_t w = pack2<DT>(lo, hi);
+          kr[pr] = (uint16_t)w;
+          kr[pr + kHeadDim / 2] = (uint16_t)(w >> 16);
+        }
+        asm volatile("" ::: "memory");  // rotated before the wave reads or stores them
+        if (store_new && lane < new_items) {
+          const int rr = lane / 4, j = lane % 4, pos = nb0 + rr;
+          PairChunks c = nw;
+          c.klo = my_new[rr * VPR + j];
+          c.khi = my_new[rr * VPR + j + VPR / 2];
+          store_pair<DT>(kc + (size_t)pos * ROWB, vc + (size_t)pos * ROWB, j, c);
+        }
+      }
+    }
   }
 
   // ---- query operand (rotated in fp32, fed as a high and a low part)
@@ -525,7 +551,13 @@ template <int DT, int RW, int NW, bool RAGGED>
 void launch_rwr(const AttnArgs &a, dim3 grid, hipStream_t s) {
   const bool fused = a.k_new != nullptr, rope = a.rope_base > 0.f;
   const dim3 block(64 * NW);
-  if (fused) {
+  if constexpr (RW == 1 && NW == 8) {
+    // rotary tiles always run on 4 waves (launch_dt): their per-wave LDS
+    // tables would not fit 8
+    (void)rope;
+    if (fused) launch_kernel(attn_mfma_kernel<DT, RW, NW, true, false, RAGGED>, grid, block, s, a);
+    else launch_kernel(attn_mfma_kernel<DT, RW, NW, false, false, RAGGED>, grid, block, s, a);
+  } else if (fused) {
     if (rope) launch_kernel(attn_mfma_kernel<DT, RW, NW, true, true, RAGGED>, grid, block, s, a);
     else launch_kernel(attn_mfma_kernel<DT, RW, NW, true, false, RAGGED>, grid, block, s, a);
   } else {
@@ -540,11 +572,12 @@ void launch_rw(const AttnArgs &a, dim3 grid, hipStream_t s) {
   else launch_rwr<DT, RW, NW, false>(a, grid, s);
 }
 
-// prefill tiles on 4 waves; shared tiles on 4 or 8 (the plan's a.waves)
+// prefill tiles on 4 waves; shared tiles on 4 or 8 (the plan's a.waves;
+// rotary tiles on 4)
 template <int DT>
 void launch_dt(const AttnArgs &a, dim3 grid, hipStream_t s) {
   if (a.rw == kWaves) launch_rw<DT, kWaves, kWaves>(a, grid, s);
-  else if (a.waves == 8) launch_rw<DT, 1, 8>(a, grid, s);
+  else if (a.waves == 8 && !(a.rope_base > 0.f)) launch_rw<DT, 1, 8>(a, grid, s);
   else launch_rw<DT, 1, 4>(a, grid, s);
 }
 

@@ -33,9 +33,13 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
   }
   const size_t src = (size_t)row * ROWB;
   const size_t dst = ((size_t)bh * a.S_max + pos + t) * ROWB;
+  constexpr int VE = vec_elems<DT>();
+  double th[VE];  // angles of the thread's VE rotary pairs (zeros without rotation)
+#pragma unroll
+  for (int e = 0; e < VE; ++e) th[e] = rope_theta_at(a.rope_theta, j * VE + e);
   const PairChunks c = load_pair<DT>(static_cast<const char *>(a.k_new) + src,
                                      static_cast<const char *>(a.v_new) + src, j, pos + t,
-                                     RopeStep{a.rope_step, a.rope_ratio});
+                                     a.rope_base > 0.f ? th : nullptr);
   store_pair<DT>(static_cast<char *>(a.k_cache) + dst, static_cast<char *>(a.v_cache) + dst, j, c);
 }
 

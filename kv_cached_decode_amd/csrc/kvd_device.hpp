@@ -41,6 +41,15 @@ template <> __device__ __forceinline__ void unpack2<BF16>(uint32_t w, float &lo,
   hi = __builtin_bit_cast(float, w & 0xffff0000u);
 }
 
+// One 16-bit storage element -> float.
+template <int DT> __device__ __forceinline__ float widen16(uint16_t b);
+template <> __device__ __forceinline__ float widen16<F16>(uint16_t b) {
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+template <> __device__ __forceinline__ float widen16<BF16>(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
 // A 16-byte vector -> vec_elems<DT>() floats.
 template <int DT> __device__ __forceinline__ void unpack16(u32x4 v, float *out) {
   if constexpr (DT == F32) {
@@ -91,26 +100,42 @@ template <int DT> __device__ __forceinline__ u32x4 pack16(const float *in) {
 }
 
 // Rotary angles. Pair (i, i + D/2) at absolute position pos turns by
-// pos * theta_i, theta_i = base^(-2i/D) = 2^(-i * step); the host passes
-// step = 2 log2(base) / D and ratio = 2^(-step) in fp64 (step == 0: no
-// rotation). For a run of n consecutive pairs i0 .. i0 + n - 1, theta_i0 comes
-// from one fp64 exp2 and each next theta from one fp64 multiply by ratio. The
-// angle is formed and reduced modulo pi/2 in fp64 (Cody-Waite reduction with
-// pi/2 split in two constants), so the reduced angle y (|y| <= pi/4) is
-// accurate to far below fp32 rounding; cos y and sin y come from their Taylor
-// polynomials in fp32 (degree 10 and 9: truncation below 2^-28 on |y| <= pi/4)
-// and the quadrant k mod 4 maps them onto cos / sin of the full angle.
-struct RopeStep {
-  double step, ratio;
-};
+// pos * theta_i, theta_i = base^(-2i/D). The angle is one fp64 product,
+// reduced modulo pi/2 in fp64 (Cody-Waite: k = nearest integer to
+// angle * 2/pi, then angle - k * pi/2 with pi/2 split into three doubles, the
+// first step exact), which leaves |y| <= pi/4 + a rounding.
+//  - Stored keys (rope_theta_at, rope_angle_cs64, rotate_elem64): theta_i
+//    exactly as the host's C library pow gives it (RopeTheta), cos y and
+//    sin y as fp64 Taylor polynomials (sin through y^17, cos through y^18:
+//    truncation below 2^-60 on |y| <= pi/4; cos as w + ((1 - w) - z/2 +
+//    z^2 r(z)) with w = 1 - z/2, z = y^2, so the rounding of w is carried),
+//    the rotation in fp64 and one rounding to the storage type. The result
+//    is the correctly rounded rotation unless the exact value lies within
+//    about 2^-50 (relative) of a rounding boundary of the storage type.
+//  - Queries (RopeStep, rope_angle_cs): theta_i = 2^(-i step) in fp64 from
+//    the host's step = 2 log2(base) / D (one exp2 per run of pairs, then
+//    multiplies by 2^(-step); a few ulps from the exact theta_i), fp32 Taylor
+//    polynomials of y (degree 10 and 9, truncation below 2^-28) and the
+//    rotation in fp32: queries are not stored, so they only need to be
+//    accurate, and one definition serves every kernel and plan, so a query
+//    is rotated with the same bits everywhere. No memory access.
+// The quadrant k mod 4 maps cos y / sin y onto cos / sin of the full angle.
+// A double in the constant address space (read with scalar loads).
+typedef const __attribute__((address_space(4))) double const_double;
 
-// cos / sin of the angle pos * theta, reduced as described above.
+__device__ __forceinline__ double rope_reduce(int pos, double theta, int &quadrant) {
+  const double ang = (double)pos * theta;                   // >= 0, < 2^31
+  const double k = rint(ang * 0x1.45f306dc9c883p-1);      // 2 / pi
+  double y = fma(-k, 0x1.921fb54442d18p+0, ang);          // pi/2, first 53 bits (exact step)
+  y = fma(-k, 0x1.1a62633145c07p-54, y);                  // next 53 bits
+  y = fma(-k, -0x1.f1976b7ed8fbcp-110, y);                // next 53 bits
+  quadrant = (int)k & 3;
+  return y;
+}
+
 __device__ __forceinline__ void rope_angle_cs(int pos, double theta, float &c, float &s) {
-  const double ang = (double)pos * theta;       // >= 0
-  const double k = rint(ang * 0.6366197723675814);   // 2 / pi
-  double yd = fma(-k, 1.5707963267948966, ang);      // pi/2, high part
-  yd = fma(-k, 6.123233995736766e-17, yd);           // pi/2, low part
-  const float y = (float)yd, y2 = y * y;
+  int q;
+  const float y = (float)rope_reduce(pos, theta, q), y2 = y * y;
   float ps = fmaf(y2, 2.7557319e-06f, -1.9841270e-04f);  // 1/9!, -1/7!
   ps = fmaf(ps, y2, 8.3333333e-03f);                     // 1/5!
   ps = fmaf(ps, y2, -1.6666667e-01f);                    // -1/3!
@@ -120,12 +145,75 @@ __device__ __forceinline__ void rope_angle_cs(int pos, double theta, float &c, f
   pc = fmaf(pc, y2, 4.1666668e-02f);                     // 1/4!
   pc = fmaf(pc, y2, -0.5f);
   const float cy = fmaf(pc, y2, 1.0f);
-  const int q = (int)k & 3;  // 0 <= k < 2^31: the angle is at most pos
   const float sv = (q & 1) ? cy : sy, cv = (q & 1) ? sy : cy;
   s = (q & 2) ? -sv : sv;                           // sin: s, c, -s, -c
   c = (q == 1 || q == 2) ? -cv : cv;                // cos: c, -s, -c, s
 }
 
+// Taylor coefficients 1/n! (rounded to nearest) of the fp64 cos / sin:
+// sin y = y + y z p(z) with p from 1/17! down to -1/3!, cos y = 1 - z/2 +
+// z^2 r(z) with r from -1/18! down to 1/4!.
+#define KVD_SIN64_COEFS                                                                      \
+  0x1.952c77030ad4ap-49, -0x1.ae7f3e733b81fp-41, 0x1.6124613a86d09p-33, -0x1.ae64567f544e4p-26, \
+      0x1.71de3a556c734p-19, -0x1.a01a01a01a01ap-13, 0x1.1111111111111p-7, -0x1.5555555555555p-3
+#define KVD_COS64_COEFS                                                                        \
+  -0x1.6827863b97d97p-53, 0x1.ae7f3e733b81fp-45, -0x1.93974a8c07c9dp-37, 0x1.1eed8eff8d898p-29, \
+      -0x1.27e4fb7789f5cp-22, 0x1.a01a01a01a01ap-16, -0x1.6c16c16c16c17p-10, 0x1.5555555555555p-5
+__constant__ const double kSinCos64[16] = {KVD_SIN64_COEFS, KVD_COS64_COEFS};
+
+// fp64 cos / sin at pos * theta. OPAQUE: read the coefficients from constant
+// memory at the call (scalar loads the optimiser cannot hoist), for callers in
+// a loop where 32 hoisted scalar registers of constants make a kernel spill;
+// otherwise they are immediates.
+template <bool OPAQUE = false>
+__device__ __forceinline__ void rope_angle_cs64(int pos, double theta, double &c, double &s) {
+  int q;
+  const double y = rope_reduce(pos, theta, q), z = y * y;
+  constexpr double kImm[16] = {KVD_SIN64_COEFS, KVD_COS64_COEFS};
+  const_double *tab = (const_double *)kSinCos64;
+  if constexpr (OPAQUE) asm volatile("" : "+s"(tab));  // constant address space kept: scalar loads
+  auto k = [&](int i) -> double {
+    if constexpr (OPAQUE) return tab[i];
+    else return kImm[i];
+  };
+  double p = fma(z, k(0), k(1));
+#pragma unroll
+  for (int i = 2; i < 8; ++i) p = fma(p, z, k(i));
+  const double sy = fma(y * z, p, y);
+  double r = fma(z, k(8), k(9));
+#pragma unroll
+  for (int i = 10; i < 16; ++i) r = fma(r, z, k(i));
+  const double hz = 0.5 * z, w = 1.0 - hz;
+  const double cy = w + (((1.0 - w) - hz) + (z * z) * r);
+  const double sv = (q & 1) ? cy : sy, cv = (q & 1) ? sy : cy;
+  s = (q & 2) ? -sv : sv;
+  c = (q == 1 || q == 2) ? -cv : cv;
+}
+
+// theta_i (i in [0, 32), may differ per lane) rebuilt from the kernel
+// arguments' RopeTheta: the product of pw[k] over the set bits of i in
+// ascending k (a factor 1.0 for a clear bit leaves the product exact), then
+// the byte correction added to the bit pattern. The words are read at
+// constant indices (scalar loads) and picked per lane by selects: no vector
+// memory access, so nothing waits behind the key loads.
+__device__ __forceinline__ double rope_theta_at(const RopeTheta &r, int i) {
+  double t = 1.0;
+#pragma unroll
+  for (int k = 0; k < 5; ++k) t = t * (((i >> k) & 1) ? r.pw[k] : 1.0);
+  uint32_t w = r.delta[0];
+#pragma unroll
+  for (int q = 1; q < kHeadDim / 8; ++q) w = ((i >> 2) == q) ? r.delta[q] : w;
+  const int d = (int)(int8_t)(w >> (8 * (i & 3)));
+  return __builtin_bit_cast(double, __builtin_bit_cast(int64_t, t) + (int64_t)d);
+}
+
+// Query angles: pair i's theta from RopeStep. For a run of n consecutive
+// pairs i0 .. i0 + n - 1 (i0 a multiple of n), theta_i0 = exp2(-i0 step) and
+// each next theta one fp64 multiply by ratio; rope_cos_sin_pair gives pair i
+// alone bit for bit what the run that holds it gives.
+struct RopeStep {
+  double step, ratio;
+};
 template <int n>
 __device__ __forceinline__ void rope_cos_sin_run(int pos, int i0, RopeStep r, float *c, float *s) {
   double theta = exp2(-(double)i0 * r.step);
@@ -135,9 +223,6 @@ __device__ __forceinline__ void rope_cos_sin_run(int pos, int i0, RopeStep r, fl
     theta *= r.ratio;
   }
 }
-// Pair i alone, bit for bit what rope_cos_sin_run<n> gives for it in the run
-// that starts at the multiple of n below i (the same multiplications of theta
-// in the same order).
 template <int n>
 __device__ __forceinline__ void rope_cos_sin_pair(int pos, int i, RopeStep r, float &c, float &s) {
   const int e = i & (n - 1);
@@ -146,11 +231,32 @@ __device__ __forceinline__ void rope_cos_sin_pair(int pos, int i, RopeStep r, fl
   for (int t = 0; t < n - 1; ++t) theta = (t < e) ? theta * r.ratio : theta;
   rope_angle_cs(pos, theta, c, s);
 }
+// Key angles: n pairs whose exact angles th[0 .. n) are given.
+template <int n>
+__device__ __forceinline__ void rope_cos_sin_run64(int pos, const double *th, double *c, double *s) {
+#pragma unroll
+  for (int e = 0; e < n; ++e) rope_angle_cs64(pos, th[e], c[e], s[e]);
+}
+// Query rotation (fp32).
 __device__ __forceinline__ void rope_rotate(float &lo, float &hi, float c, float s) {
   const float l = lo, h = hi;
   lo = fmaf(l, c, -(h * s));
   hi = fmaf(h, c, l * s);
 }
+
+// fp64 -> fp32 rounded to odd: truncated, with the last bit set when the
+// conversion is inexact. Rounding that to nearest in a format with at least
+// two fewer significant bits (fp16, bf16) gives the nearest value of the
+// original fp64, which a direct fp32 rounding first would not always give.
+__device__ __forceinline__ float f64_to_f32_odd(double x) {
+  const float f = (float)x;  // nearest
+  const double back = (double)f;
+  if (back == x || x != x) return f;
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if (fabs(back) > fabs(x)) u -= 1;  // rounded away from zero: one step back
+  return __builtin_bit_cast(float, u | 1u);
+}
+
 
 // ---------------------------------------------------------------------------
 // Cross-lane sums with DPP (no LDS round trip). Every lane of an aligned group
@@ -232,7 +338,7 @@ template <> __device__ __forceinline__ float group_sum<16>(float x) {
   return x;
 }
 
-// cos / sin of the VE rotary pairs held by lane slice `ds` of a row at
+// Query cos / sin of the VE rotary pairs held by lane slice `ds` of a row at
 // position pos (slice ds and ds ^ (LPR/2) hold the two halves of the pairs
 // (ds % (LPR/2)) * VE + e).
 template <int DT>
@@ -302,56 +408,83 @@ __device__ __forceinline__ void reset_counter(uint32_t *counter) {
 
 // One rotary pair of 16-byte chunks of a new K/V row (chunk j in the first
 // half of the row, j + D/2 in the second), the key rotated at position pos
-// when base > 0, rounded to the storage type.
+// when there is a rotation, rounded to the storage type.
 struct PairChunks {
   u32x4 klo, khi, vlo, vhi;
 };
-// r.step == 0: no rotation.
-// Chunk j of each half of a new key row (dims [j*VE, +VE) and their rotary
-// partners [D/2 + j*VE, +VE)), rotated at position pos when base > 0 and
-// rounded to the storage type: the one definition of a stored rotated key.
+// One rotary pair of a new key, (lo, hi) -> (lo c - hi s, hi c + lo s) with
+// the fp64 cos / sin c, s: each product and the sum rounded in fp64 (no fused
+// multiply-add), then one rounding to the storage type (fp32 storage: to
+// nearest; 16-bit storage: to odd here, to nearest when packed). The one
+// definition of a stored rotated key.
 template <int DT>
-__device__ __forceinline__ void rotate_key_pair_cs(u32x4 &klo, u32x4 &khi, const float *cs,
-                                                   const float *sn) {
+__device__ __forceinline__ void rotate_elem64(float &lo, float &hi, double c, double s) {
+  const double l = lo, h = hi;
+  const double lc = l * c, hs = h * s, hc = h * c, ls = l * s;
+  if constexpr (DT == F32) {
+    lo = (float)(lc - hs);
+    hi = (float)(hc + ls);
+  } else {
+    lo = f64_to_f32_odd(lc - hs);
+    hi = f64_to_f32_odd(hc + ls);
+  }
+}
+// Chunk j of each half of a new key row (dims [j*VE, +VE) and their rotary
+// partners [D/2 + j*VE, +VE)) rotated with the fp64 cos / sin cs, sn of those
+// VE pairs.
+template <int DT>
+__device__ __forceinline__ void rotate_key_pair_cs(u32x4 &klo, u32x4 &khi, const double *cs,
+                                                   const double *sn) {
   constexpr int VE = vec_elems<DT>();
   float lo[VE], hi[VE];
   unpack16<DT>(klo, lo);
   unpack16<DT>(khi, hi);
 #pragma unroll
-  for (int e = 0; e < VE; ++e) rope_rotate(lo[e], hi[e], cs[e], sn[e]);
+  for (int e = 0; e < VE; ++e) rotate_elem64<DT>(lo[e], hi[e], cs[e], sn[e]);
   klo = pack16<DT>(lo);
   khi = pack16<DT>(hi);
 }
-template <int DT>
-__device__ __forceinline__ void rotate_key_pair(u32x4 &klo, u32x4 &khi, int j, int pos,
-                                                RopeStep r) {
+// The same at position pos, each pair's cos / sin computed just before its
+// rotation (two doubles live at a time); th: the VE pairs' angles, or null
+// for no rotation.
+template <int DT, bool OPAQUE = false>
+__device__ __forceinline__ void rotate_key_pair(u32x4 &klo, u32x4 &khi, int pos, const double *th) {
   constexpr int VE = vec_elems<DT>();
-  if (r.step > 0.0) {
-    float cs[VE], sn[VE];
-    rope_cos_sin_run<VE>(pos, j * VE, r, cs, sn);
-    rotate_key_pair_cs<DT>(klo, khi, cs, sn);
+  if (th) {
+    float lo[VE], hi[VE];
+    unpack16<DT>(klo, lo);
+    unpack16<DT>(khi, hi);
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+      double c, s;
+      rope_angle_cs64<OPAQUE>(pos, th[e], c, s);
+      rotate_elem64<DT>(lo[e], hi[e], c, s);
+    }
+    klo = pack16<DT>(lo);
+    khi = pack16<DT>(hi);
   }
 }
-template <int DT>
-__device__ __forceinline__ void load_key_pair(const char *k_src, int j, int pos, RopeStep r,
+// th: the angles of pairs j*VE .. j*VE + VE - 1, or null.
+template <int DT, bool OPAQUE = false>
+__device__ __forceinline__ void load_key_pair(const char *k_src, int j, int pos, const double *th,
                                               u32x4 &klo, u32x4 &khi) {
   constexpr int VE = vec_elems<DT>();
   constexpr int EB = Storage<DT>::bytes;
   klo = load16(k_src + j * VE * EB);
   khi = load16(k_src + (kHeadDim / 2 + j * VE) * EB);
-  rotate_key_pair<DT>(klo, khi, j, pos, r);
+  rotate_key_pair<DT, OPAQUE>(klo, khi, pos, th);
 }
 
-template <int DT>
+template <int DT, bool OPAQUE = false>
 __device__ __forceinline__ PairChunks load_pair(const char *k_src, const char *v_src, int j,
-                                                int pos, RopeStep r) {
+                                                int pos, const double *th) {
   constexpr int VE = vec_elems<DT>();
   constexpr int EB = Storage<DT>::bytes;
   const int lo_off = j * VE * EB, hi_off = (kHeadDim / 2 + j * VE) * EB;
   PairChunks c;
   c.vlo = load16(v_src + lo_off);
   c.vhi = load16(v_src + hi_off);
-  load_key_pair<DT>(k_src, j, pos, r, c.klo, c.khi);
+  load_key_pair<DT, OPAQUE>(k_src, j, pos, th, c.klo, c.khi);
   return c;
 }
 template <int DT>

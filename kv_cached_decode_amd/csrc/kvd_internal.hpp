@@ -31,6 +31,19 @@ constexpr int kMaxSplits = 64;  // key splits per tile: the merge gives each spl
 // verify_accept: (value, index) pairs one batch row may stage for its merge.
 constexpr int kMaxVerifyChunks = 512;  // 2048-logit chunks per row (8 keys per lane in the merge)
 
+// Rotary angle per pair, theta_i = base^(-2i/D) for i < D/2, as the host's C
+// library pow gives it in fp64, carried in a form a kernel rebuilds in
+// registers (no table in memory): with r = pow(base, -2/D) and pw[k] = r^(2^k)
+// by repeated squaring, theta'_i is the product of pw[k] over the set bits k
+// of i, multiplied in ascending k (IEEE fp64 products, the same on host and
+// device), and delta_i = bits(theta_i) - bits(theta'_i) is a small signed
+// count of ulps (|delta_i| <= 24 for bases 1e-3 .. 3.4e38), packed four to a
+// word; theta_i's bits are theta'_i's plus delta_i.
+struct RopeTheta {
+  double pw[5];
+  uint32_t delta[kHeadDim / 8];
+};
+
 struct AppendArgs {
   void *k_cache, *v_cache;       // [B][H][S_max][D]
   const void *k_new, *v_new;     // [B][H][T][D]
@@ -38,8 +51,7 @@ struct AppendArgs {
   const int32_t *pos_rows;       // [B] per-row positions (ragged batch), or null: pos for all
   int32_t *dev_status;           // a row outside the cache is skipped and flagged here, or null
   float rope_base;               // > 0: rotate keys at pos + t
-  double rope_step;              // 2 log2(rope_base) / D (0: no rotation)
-  double rope_ratio;             // 2^(-rope_step)
+  RopeTheta rope_theta;          // exact theta_i for stored keys, when rope_base > 0
 };
 
 struct ReorderArgs {
@@ -87,8 +99,9 @@ struct AttnArgs {
   const int32_t *parent;         // [Bkv] beam step parents (k, v are then the destination), or null
   float scale_log2;              // scale * log2(e)
   float rope_base;               // > 0: rotate q at causal_base + i (and new keys)
-  double rope_step;              // 2 log2(rope_base) / D (0: no rotation)
+  double rope_step;              // queries: theta_i = 2^(-i * rope_step), rope_step = 2 log2(base) / D
   double rope_ratio;             // 2^(-rope_step)
+  RopeTheta rope_theta;          // new keys: the exact theta_i (as kv_append stores them)
   // plan
   int chunk;                     // keys per workgroup
   int splits;                    // workgroups per (unit, row tile)
@@ -113,6 +126,14 @@ struct VerifyArgs {
   int B, R, V, N;
   int chunk, chunks;
 };
+
+// Plan forced by kvd_set_plan_override (a testing hook): mfma -1 none, 0 keep
+// 16-bit caches on the streaming kernel; waves, chunk 0: as planned.
+struct PlanOverride {
+  int mfma, waves, chunk;
+};
+PlanOverride plan_override();
+void set_plan_override(PlanOverride o);
 
 // Attention planning shared by the entry points and the workspace-size query.
 struct AttnPlan {
@@ -173,7 +194,10 @@ struct ProbeArgs {
   const void *a, *b;  // buffers to read (b may be NULL)
   size_t vecs;        // 16-byte vectors read from each
   uint32_t *sink;
+  int unroll;         // loads in flight per thread: 1, 2, 4, 8 or 16
+  size_t blocks;      // workgroups of 256 threads; 0: one round of loads per thread
 };
+int probe_unroll_ok(int u);
 hipError_t launch_probe(const ProbeArgs &a, hipStream_t s);
 
 }  // namespace kvd

@@ -232,3 +232,28 @@ def test_beam_select_validation(lib):
     assert call(ws=None) == -6 and call(wsb=ws_need - 4) == -6
     assert call(logits=FAKE + 2) == -7 and call(logits=FAKE + 1, dt=kb.F16) == -7
     assert call(parent=FAKE + 2) == -7
+
+
+def test_read_probe_ex_validation(lib):
+    f = lib.kvd_read_probe_ex
+    assert f(None, None, 16, FAKE, 4, 0, None) == -1
+    assert f(FAKE, None, 16, None, 4, 0, None) == -1
+    for u in (0, 3, 5, 32, -1):                       # loads in flight: 1, 2, 4, 8 or 16
+        assert f(FAKE, None, 16, FAKE, u, 0, None) == -2
+    assert f(FAKE, None, 16, FAKE, 4, 65536, None) == -2      # grid limit
+    assert f(FAKE, None, 24, FAKE, 4, 0, None) == -2          # not a multiple of 16
+    assert f(MIS, None, 16, FAKE, 4, 0, None) == -7
+
+
+def test_plan_override_validation_and_reset(lib):
+    f = lib.kvd_set_plan_override
+    assert f(2, 0, 0) == -2
+    assert f(-2, 0, 0) == -2
+    assert f(-1, 17, 0) == -2
+    assert f(-1, 0, -5) == -2
+    base = kb.attn_workspace_bytes(1, 20, 1, 1500)
+    with kb.plan_override(chunk=128):                 # more splits: more partials
+        forced = kb.attn_workspace_bytes(1, 20, 1, 1500)
+    assert forced > base
+    assert kb.attn_workspace_bytes(1, 20, 1, 1500) == base    # restored on exit
+    assert f(-1, 0, 0) == 0

@@ -3,8 +3,9 @@
 Bit-exact: cache append (plain copy), beam reorder, argmax, accepted length and
 corrected token. Attention outputs: max |err| <= 1e-5 with fp32 storage and
 <= 2e-3 with fp16/bf16 storage (fp32 accumulation on the GPU, fp64 in the
-oracle, both reading the same stored bits). Rotary keys: within one bf16 ulp
-of the oracle's once-rounded fp64 value (the kernel rounds an fp32 rotation).
+oracle, both reading the same stored bits). Rotated keys are bit-exact too:
+kernel and oracle both rotate in fp64 (the same pow-derived angles, each side
+with its own cos / sin) and round once to the storage type.
 """
 import numpy as np
 import pytest
@@ -108,23 +109,22 @@ def test_whisper_greedy_sweep_lengths(layer):
     say(f"whisper layer {layer}: worst max|err| {worst:.2e}")
 
 
-# Plans forced through the tuning variables, so that split boundaries and the
-# narrow (1-, 2-wave) and wide (8-wave) workgroups are covered at lengths
-# the default plan runs otherwise.
+# Plans forced through the library's testing hook (kvd_set_plan_override),
+# so that split boundaries and the narrow (1-, 2-wave) and wide (8-wave)
+# workgroups are covered at lengths the default plan runs otherwise.
 # Blocks of queries (N > 1, 16-bit storage) take the matrix-core kernel by
 # default; "stream" runs them through the streaming kernel instead.
-PLANS = {"default": {}, "chunk128": {"KVD_ATTN_CHUNK": "128"},
-         "wide": {"KVD_ATTN_WAVES": "8"}, "wide_chunk512": {"KVD_ATTN_WAVES": "8", "KVD_ATTN_CHUNK": "512"},
-         "w8_chunk256": {"KVD_ATTN_WAVES": "8", "KVD_ATTN_CHUNK": "256"},
-         "w1": {"KVD_ATTN_WAVES": "1"}, "w2_chunk64": {"KVD_ATTN_WAVES": "2", "KVD_ATTN_CHUNK": "64"},
-         "stream": {"KVD_ATTN_MFMA": "0"}, "stream_chunk128": {"KVD_ATTN_MFMA": "0", "KVD_ATTN_CHUNK": "128"}}
+PLANS = {"default": {}, "chunk128": {"chunk": 128},
+         "wide": {"waves": 8}, "wide_chunk512": {"waves": 8, "chunk": 512},
+         "w8_chunk256": {"waves": 8, "chunk": 256},
+         "w1": {"waves": 1}, "w2_chunk64": {"waves": 2, "chunk": 64},
+         "stream": {"mfma": 0}, "stream_chunk128": {"mfma": 0, "chunk": 128}}
 
 
 @pytest.fixture(params=list(PLANS))
-def plan(request, monkeypatch):
-    for k, v in PLANS[request.param].items():
-        monkeypatch.setenv(k, v)
-    return request.param
+def plan(request):
+    with kb.plan_override(**PLANS[request.param]):
+        yield request.param
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
@@ -248,11 +248,14 @@ def test_ragged_step_self_equals_append_then_attend(dtype, N, plan):
     assert np.array_equal(bits(from_dev(fused.v, dtype)), bits(from_dev(split.v, dtype)))
     assert torch.equal(out_f, out_s)
     rows = []
+    fk, fv = from_dev(fused.k, dtype), from_dev(fused.v, dtype)
     for b, L in enumerate(lens):
         c = O.ConcatCache(1, 2, 64, dtype)
         c.append(ks[b:b + 1, :, :L - N], vs[b:b + 1, :, :L - N])
         c.append(kn[b:b + 1], vn[b:b + 1], rope_base=rope)
         rows.append(c)
+        assert _same_bits(fk[b:b + 1, :, :L], c.k, f"row {b} keys")
+        assert _same_bits(fv[b:b + 1, :, :L], c.v, f"row {b} values")
     e = max_err(out_f, O.attend_self_ragged(qs, rows, 0.125, rope_base=rope))
     assert e <= TOL[dtype], e
 
@@ -630,19 +633,12 @@ def test_reorder_duplicate_parents_and_bad_parent():
 
 # ---------------------------------------------------------- GQA + RoPE ----
 
-def _rope_key_check(gpu_bits, ref_bits, raw_bits):
-    """Rotated keys: the kernel rounds an fp32 rotation to bf16, the oracle an
-    fp64 one. They may differ by one bf16 step, plus the fp32 rounding error
-    of lo*c - hi*s (about 2^-22 of |lo| + |hi|) where the two terms cancel.
-    Returns (worst ratio to that bound, share of elements that differ)."""
-    g = O.widen(gpu_bits, "bf16")
-    r = O.widen(ref_bits, "bf16")
-    x = np.abs(O.widen(raw_bits, "bf16"))
-    half = x.shape[-1] // 2
-    pair = np.concatenate([x[..., :half] + x[..., half:]] * 2, axis=-1)
-    ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(r), 1e-38))[1] - 8)
-    bound = ulp + pair * 2.0 ** -20
-    return float(np.max(np.abs(g - r) / bound)), float(np.mean(g != r))
+def _same_bits(gpu, ref, what):
+    """Bit equality of two storage arrays, reporting how many elements differ."""
+    gb, rb = bits(gpu), bits(ref)
+    diff = int(np.count_nonzero(gb != rb))
+    say(f"{what}: {diff} of {gb.size} elements differ")
+    return diff == 0
 
 
 @pytest.mark.parametrize("layer", [0, 29])
@@ -663,9 +659,7 @@ def test_gqa_prefill_then_decode_with_rope(layer):
     qp = I.queries(w, layer, 0, N=P)
     out = kb.decode_attn_self(to_dev(qp, "bf16"), cache, P, w.attn_scale, rope_base=w.rope_base, ws=ws)
     gk = from_dev(cache.k, "bf16")[:, :, :P]
-    worst, share = _rope_key_check(gk, oc.k, k_all[:, :, :P])
-    say(f"rope keys: worst/bound {worst:.3f}, share differing {share:.2e}")
-    assert worst <= 1.0 and share < 0.01
+    assert _same_bits(gk, oc.k, "prefill rotated keys")
     assert np.array_equal(from_dev(cache.v, "bf16")[:, :, :P], oc.v)
     # the oracle attends over its own rotated keys; the kernel over its own
     e = max_err(out, O.attend_self(qp, oc, w.attn_scale, rope_base=w.rope_base))
@@ -683,8 +677,8 @@ def test_gqa_prefill_then_decode_with_rope(layer):
             e = max_err(o, O.attend_self(q, oc, w.attn_scale, rope_base=w.rope_base))
             say(f"decode L={L} max|err| {e:.2e}")
             assert e <= TOL["bf16"]
-    worst, share = _rope_key_check(from_dev(cache.k, "bf16"), oc.k, k_all)
-    assert worst <= 1.0 and share < 0.01
+    assert _same_bits(from_dev(cache.k, "bf16"), oc.k, "rotated keys after decode to 1024")
+    assert _same_bits(from_dev(cache.v, "bf16"), oc.v, "values after decode to 1024")
 
 
 def test_cross_cache_per_row_and_shared_agree():
@@ -762,6 +756,8 @@ def test_step_self_equals_append_then_attend(dtype, B, Hq, Hkv, N, L, rope, plan
     if L > N:
         oc.append(k_all[:, :, old], v_all[:, :, old], rope)
     oc.append(k_all[:, :, new], v_all[:, :, new], rope)
+    assert _same_bits(from_dev(c2.k, dtype)[:, :, :L], oc.k, "appended keys")
+    assert _same_bits(from_dev(c2.v, dtype)[:, :, :L], oc.v, "appended values")
     assert max_err(o2, O.attend_self(q, oc, 0.125, rope_base=rope)) <= TOL[dtype]
 
 
@@ -815,13 +811,19 @@ def test_queried_workspace_suffices(dtype, B, Hq, Hkv, N, L, rope):
     ("f32", 3, 4, 4, 3, 70, 10000.0),
     ("f32", 2, 4, 2, 1, 1100, 0.0),
 ])
-def test_beam_step_equals_reorder_then_step(dtype, B, Hq, Hkv, N, L, rope, plan, monkeypatch):
+def test_beam_step_equals_reorder_then_step(dtype, B, Hq, Hkv, N, L, rope, plan):
     """decode_step_self_beams(src -> dst) leaves dst exactly as a copy of
     src, kv_reorder and decode_step_self would (rows from L on untouched),
     leaves src as it was, returns the same output bit for bit on the same
     (streaming) plan, and matches the oracle."""
     say(f"case: beam step {dtype} B={B} Hq={Hq} Hkv={Hkv} N={N} L={L} rope={rope} plan={plan}")
-    monkeypatch.setenv("KVD_ATTN_MFMA", "0")   # the composition on the beam step's kernel
+    # the composition on the beam step's kernel (the streaming one)
+    forced = dict(PLANS[plan], mfma=0)
+    with kb.plan_override(**forced):
+        _beam_step_case(dtype, B, Hq, Hkv, N, L, rope)
+
+
+def _beam_step_case(dtype, B, Hq, Hkv, N, L, rope):
     g = np.random.default_rng(L * 11 + N + B)
     S = L + 5
     old, new = slice(0, L - N), slice(L - N, L)
@@ -864,23 +866,8 @@ def test_beam_step_equals_reorder_then_step(dtype, B, Hq, Hkv, N, L, rope, plan,
     oc.append(k_new, v_new, rope)
     assert np.array_equal(bits(gk[:, :, old]), bits(oc.k[:, :, old]))   # copied rows
     assert np.array_equal(bits(gv[:, :, :L]), bits(oc.v))
-    if rope > 0:   # rotated in fp32 by the kernel, in fp64 by the oracle
-        assert _rotated_rows_close(gk[:, :, new], oc.k[:, :, new], k_new, dtype)
-    else:
-        assert np.array_equal(bits(gk[:, :, new]), bits(oc.k[:, :, new]))
+    assert _same_bits(gk[:, :, new], oc.k[:, :, new], "new keys")
     assert max_err(o_beam, O.attend_self(q, oc, 0.125, rope_base=rope)) <= TOL[dtype]
-
-
-def _rotated_rows_close(gpu, ref, raw, dtype):
-    """Keys rotated by the kernel (fp32 rotation, rounded to nearest) against
-    the oracle's (fp64, rounded): one step of the storage type apart at most,
-    plus the fp32 error of lo*c - hi*s where the two terms cancel."""
-    mant = {"f32": 23, "f16": 10, "bf16": 7}[dtype]
-    g, r, x = O.widen(gpu, dtype), O.widen(ref, dtype), np.abs(O.widen(raw, dtype))
-    half = x.shape[-1] // 2
-    pair = np.concatenate([x[..., :half] + x[..., half:]] * 2, axis=-1)
-    ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(r), 1e-38))[1] - 1 - mant)
-    return bool(np.all(np.abs(g - r) <= ulp + pair * 2.0 ** -20))
 
 
 def test_beam_step_bad_parent_reads_own_rows():
