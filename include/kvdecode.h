@@ -62,7 +62,9 @@ enum kvd_status {
   KVD_ERR_ROWS = -5,       /* verify: logits rows R is neither N nor N + 1 */
   KVD_ERR_WORKSPACE = -6,  /* workspace NULL or smaller than required */
   KVD_ERR_ALIGN = -7,      /* a device pointer is not 16-byte aligned */
-  KVD_ERR_LAUNCH = -8      /* the HIP launch reported an error */
+  KVD_ERR_LAUNCH = -8,     /* the HIP launch reported an error */
+  KVD_ERR_SCRATCH = -9     /* decode_step_self_static: the shape needs more
+                              scratch than the library's static array holds */
 };
 
 /* One layer's K/V cache ([N] per-layer key/value tensors).
@@ -172,6 +174,25 @@ int decode_attn_self_ragged(const void *q, int32_t Hq, int32_t N, const kvd_cach
                             const int32_t *lens, int32_t len_max, float scale, float rope_base,
                             float *out, void *ws, size_t ws_bytes, int32_t *dev_status,
                             void *stream);
+
+/* decode_step_self_static - decode_step_self for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation): no workspace argument; the split merge
+ * uses a static device array of kvd_static_scratch_bytes() (4 MiB) that
+ * each GPU holds until the process ends. The call itself allocates nothing.
+ *   Arguments, results and bits of `out` as decode_step_self.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (several streams or threads at once) race and must be ordered by the
+ *   caller. The first call on a GPU clears the array's counter block with a
+ *   kernel on `stream` (inside a stream capture, once per captured graph).
+ * Errors: as decode_step_self, KVD_ERR_SCRATCH when the shape's merge needs
+ *   more than the array holds (it holds every Whisper-large-v2 and 8-row GQA
+ *   decode step; kvd_attn_workspace_bytes(B, Hq, N, len) <= 4 MiB), and
+ *   KVD_ERR_LAUNCH if the device array cannot be found. */
+int decode_step_self_static(const void *q, const void *k_new, const void *v_new, int32_t Hq,
+                            int32_t N, const kvd_cache *cache, int32_t len, float scale,
+                            float rope_base, float *out, void *stream);
+size_t kvd_static_scratch_bytes(void);
 
 /* decode_step_self_ragged - decode_step_self with per-row lengths, in one
  * launch (N <= 16): row b's N new K/V rows are written at

@@ -80,6 +80,10 @@ _SIGNATURES = {
     "kvd_read_probe_ex": (c_int, [c_void_p, c_void_p, c_size_t, c_void_p, c_int32, c_size_t,
                                   c_void_p]),
     "kvd_set_plan_override": (c_int, [c_int32, c_int32, c_int32]),
+    "decode_step_self_static": (c_int, [c_void_p, c_void_p, c_void_p, c_int32, c_int32,
+                                        ctypes.POINTER(KvdCache), c_int32, c_float, c_float,
+                                        c_void_p, c_void_p]),
+    "kvd_static_scratch_bytes": (c_size_t, []),
 }
 
 
@@ -294,6 +298,30 @@ def decode_step_self(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, 
         _dev(out, "out", torch.float32), _dev(ws, "ws"), ws.numel() * ws.element_size(),
         _stream()))
     return out
+
+
+def decode_step_self_static(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                            cache: Cache, length: int, scale: float, rope_base: float = 0.0,
+                            out: torch.Tensor | None = None) -> torch.Tensor:
+    """decode_step_self with no workspace: the library's static device array
+    serves the split merge (nothing is allocated by the call; `out` is
+    allocated here when not given)."""
+    d = cache.desc()
+    if q.dim() != 4 or q.shape[0] != d.B or q.shape[3] != d.D:
+        raise ValueError(f"q must be [B={d.B}, Hq, N, {d.D}], got {tuple(q.shape)}")
+    Hq, N = q.shape[1], q.shape[2]
+    if tuple(k_new.shape) != (d.B, d.H, N, d.D) or k_new.shape != v_new.shape:
+        raise ValueError(f"k_new/v_new must be [{d.B}, {d.H}, {N}, {d.D}]")
+    out = _attn_out(q, out)
+    _check("decode_step_self_static", lib().decode_step_self_static(
+        _dev(q, "q", cache.dtype), _dev(k_new, "k_new", cache.dtype),
+        _dev(v_new, "v_new", cache.dtype), Hq, N, ctypes.byref(d), length, scale, rope_base,
+        _dev(out, "out", torch.float32), _stream()))
+    return out
+
+
+def static_scratch_bytes() -> int:
+    return int(lib().kvd_static_scratch_bytes())
 
 
 def _rows(t: torch.Tensor, B: int, name: str):

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvdecode.so")
 OBJ_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["kvd_copy.hip", "kvd_attn.hip", "kvd_attn_mfma.hip", "kvd_verify.hip", "kvd_beam.hip",
-           "kvd_probe.hip",
+           "kvd_probe.hip", "kvd_static.hip",
            "kvd_api.cpp"]
 ARCH = "gfx950"
 

@@ -162,6 +162,7 @@ const char *kvd_status_string(int status) {
     case KVD_ERR_WORKSPACE: return "workspace missing or too small";
     case KVD_ERR_ALIGN: return "device pointer not 16-byte aligned";
     case KVD_ERR_LAUNCH: return "HIP launch failed";
+    case KVD_ERR_SCRATCH: return "shape needs more than the static scratch array holds";
     default: return "unknown status";
   }
 }
@@ -236,6 +237,8 @@ int kv_reorder(const kvd_cache *cache, const int32_t *parent, int32_t len, int32
   return status_of(kvd::launch_reorder(cache->dtype, a, static_cast<hipStream_t>(stream)));
 }
 
+}  // extern "C"
+
 namespace {
 
 // Shared by decode_attn_self and decode_step_self: validate and plan (no HIP
@@ -293,29 +296,20 @@ int prepare_self(AttnArgs &a, const void *q, const void *k_new, const void *v_ne
 
 }  // namespace
 
-int decode_attn_self(const void *q, int32_t Hq, int32_t N, const kvd_cache *cache, int32_t len,
-                     float scale, float rope_base, float *out, void *ws, size_t ws_bytes,
-                     void *stream) {
-  AttnArgs a{};
-  const int st = prepare_self(a, q, nullptr, nullptr, Hq, N, cache, len, scale, rope_base, out,
-                              ws, ws_bytes);
-  if (st) return st;
-  return status_of(kvd::launch_attn(cache->dtype, a, static_cast<hipStream_t>(stream)));
-}
-
-int decode_step_self(const void *q, const void *k_new, const void *v_new, int32_t Hq, int32_t N,
-                     const kvd_cache *cache, int32_t len, float scale, float rope_base,
-                     float *out, void *ws, size_t ws_bytes, void *stream) {
+int kvd::step_self(const void *q, const void *k_new, const void *v_new, int32_t Hq, int32_t N,
+                   const kvd_cache *cache, int32_t len, float scale, float rope_base, float *out,
+                   void *ws, size_t ws_bytes, void *stream, bool check_only) {
   if (!k_new || !v_new) return KVD_ERR_NULL;
   const bool fused = N <= kvd::kMaxFusedRows;
   AttnArgs a{};
   const int st = prepare_self(a, q, fused ? k_new : nullptr, fused ? v_new : nullptr, Hq, N, cache,
                               len, scale, rope_base, out, ws, ws_bytes);
   if (st) return st;
+  if (!fused && (!aligned16(k_new) || !aligned16(v_new))) return KVD_ERR_ALIGN;
+  if (check_only) return KVD_OK;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (!fused) {
     // a long block of new rows (prefill): append first, then attend
-    if (!aligned16(k_new) || !aligned16(v_new)) return KVD_ERR_ALIGN;
     kvd::AppendArgs ap{};
     ap.k_cache = cache->k;
     ap.v_cache = cache->v;
@@ -332,6 +326,25 @@ int decode_step_self(const void *q, const void *k_new, const void *v_new, int32_
     if (sa) return sa;
   }
   return status_of(kvd::launch_attn(cache->dtype, a, s));
+}
+
+extern "C" {
+
+int decode_attn_self(const void *q, int32_t Hq, int32_t N, const kvd_cache *cache, int32_t len,
+                     float scale, float rope_base, float *out, void *ws, size_t ws_bytes,
+                     void *stream) {
+  AttnArgs a{};
+  const int st = prepare_self(a, q, nullptr, nullptr, Hq, N, cache, len, scale, rope_base, out,
+                              ws, ws_bytes);
+  if (st) return st;
+  return status_of(kvd::launch_attn(cache->dtype, a, static_cast<hipStream_t>(stream)));
+}
+
+int decode_step_self(const void *q, const void *k_new, const void *v_new, int32_t Hq, int32_t N,
+                     const kvd_cache *cache, int32_t len, float scale, float rope_base,
+                     float *out, void *ws, size_t ws_bytes, void *stream) {
+  return kvd::step_self(q, k_new, v_new, Hq, N, cache, len, scale, rope_base, out, ws, ws_bytes,
+                        stream, false);
 }
 
 int decode_attn_self_ragged(const void *q, int32_t Hq, int32_t N, const kvd_cache *cache,

@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+struct kvd_cache;  // the C ABI's cache descriptor (kvdecode.h)
+
 namespace kvd {
 
 enum DType { F32 = 0, F16 = 1, BF16 = 2 };  // same values as enum kvd_dtype
@@ -163,6 +165,12 @@ inline void launch_kernel(void (*kernel)(Args...), dim3 grid, dim3 block, hipStr
   else
     (void)hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, argv, 0, s);
 }
+
+// decode_step_self's work: validation and planning (all on the host before
+// any HIP call) and, unless check_only, the launches on `stream`.
+int step_self(const void *q, const void *k_new, const void *v_new, int32_t Hq, int32_t N,
+              const ::kvd_cache *cache, int32_t len, float scale, float rope_base, float *out,
+              void *ws, size_t ws_bytes, void *stream, bool check_only);
 
 hipError_t launch_append(int dtype, const AppendArgs &a, hipStream_t s);
 hipError_t launch_reorder(int dtype, const ReorderArgs &a, hipStream_t s);

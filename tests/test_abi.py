@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         s = kb.status_string(code)
         assert s and s != "unknown status"
     assert kb.status_string(-99) == "unknown status"
