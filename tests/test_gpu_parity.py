@@ -380,7 +380,7 @@ def test_prefill_tiles_paired(dtype, rope, N, ragged):
 
 # ------------------------------------------------------ speculative verify ----
 
-@pytest.mark.parametrize("L_before", [64, 128, 443])
+@pytest.mark.parametrize("L_before", list(I.WHISPER_VERIFY.extra["L_before"]))
 def test_verify_attention_n5(L_before, plan):
     """Five draft rows appended at once, causal among themselves, over the
     self cache and the cross cache (large-v2 layer shape)."""
@@ -422,17 +422,30 @@ def _verify_gpu(logits, draft, dtype="f32"):
 
 
 def test_verify_accept_random_trials_bit_exact():
+    """1000 trials at V = 51865 (7 in 8 with a planted argmax per row that the
+    drafts copy with p = 0.75): argmax, accepted length and next token equal
+    the oracle's; over the planted trials the accepted lengths follow
+    P(n = k) = 0.75^k 0.25 for k < 5 and P(5) = 0.75^5 (chi-square, 5 degrees
+    of freedom, below the 0.001 critical value 20.52)."""
     w = I.WHISPER_VERIFY
-    say("case: verify_accept 400 trials V=51865")
+    trials = 1000
+    say(f"case: verify_accept {trials} trials V=51865")
     hist = np.zeros(6, dtype=int)
-    for t in range(400):
-        logits, draft = I.verify_logits(w, t, plant=(t % 8 != 0))
+    for t in range(trials):
+        planted = t % 8 != 0
+        logits, draft = I.verify_logits(w, t, plant=planted)
         acc, nxt, am = _verify_gpu(logits, draft)
         ram, racc, rnxt = O.verify_accept(logits, draft)
         assert np.array_equal(am, ram), t
         assert np.array_equal(acc, racc) and np.array_equal(nxt, rnxt), t
-        hist[racc[0]] += 1
-    say(f"accept histogram {hist.tolist()}")
+        if planted:
+            hist[int(acc[0])] += 1
+    p = w.extra["p_match"]
+    probs = np.array([p ** k * (1 - p) for k in range(5)] + [p ** 5])
+    expected = probs * hist.sum()
+    chi2 = float(((hist - expected) ** 2 / expected).sum())
+    say(f"accept histogram {hist.tolist()} expected {np.round(expected, 1).tolist()} chi2 {chi2:.2f}")
+    assert chi2 < 20.52
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])

@@ -65,3 +65,30 @@ def test_greedy_loop_emits_the_same_stream(loop):
     n = loop.run_greedy(60)
     torch.cuda.synchronize()
     assert loop.greedy_stream() == _greedy_tokens(loop, CFG.prompt, n)
+
+
+def test_full_large_v2_shape_stream_equals_greedy():
+    """The same loop at the large-v2 shape (32-layer main model, 2-layer
+    assistant, 20 heads, 448 positions, 1500 frames, vocab 51865), from
+    captured graphs: the stream equals the greedy stream and the last
+    verification pass of the first and last main layers matches the oracle."""
+    cfg = SpecConfig()
+    say("case: speculative loop at the large-v2 shape")
+    big = SpecLoop(cfg)
+    big.capture()
+    n_it = big.run()
+    torch.cuda.synchronize()
+    log, stream = big.emitted()
+    am = O.argmax_rows(big.LM.cpu().numpy().astype(np.float64))
+    assert stream == [int(am[p]) for p in range(cfg.prompt, cfg.prompt + len(stream))]
+    P = log[:, 0].tolist()
+    acc = log[:, 1].tolist()
+    say(f"{n_it} iterations, {len(stream)} tokens, mean accepted {np.mean(acc):.2f}")
+    assert 0 < sum(acc) < cfg.drafts * n_it
+    L = P[-1] + big.R
+    for l in (0, cfg.main_layers - 1):
+        assert torch.equal(big.m_self[l].k[0, :, :L], big.mk[l, :, :L])
+        c = O.ConcatCache(1, cfg.heads, 64, "f16")
+        c.append(big.mk[l, :, :L][None].cpu().numpy(), big.mv[l, :, :L][None].cpu().numpy())
+        q = big.mq[l, :, P[-1]:L][None].cpu().numpy()
+        assert max_err(big.m_out[l], O.attend_self(q, c, 0.125)) <= TOL["f16"]
