@@ -525,7 +525,7 @@ def headline(torch, kb, I, args) -> dict:
 
     steps_per_s = args.steps / elapsed
     gbps = kv_bytes / elapsed / 1e9
-    r = roof(CROSS_BYTES, k_period, "decode_attn_cross (attn_kernel<f16, 1 row, 8 waves>, 6 splits x 20 heads)")
+    r = roof(CROSS_BYTES, k_period, "decode_attn_cross (attn_kernel<f16, 1 row, 4 waves>, 12 splits x 20 heads)")
     r["traffic"] = measured_traffic()
     r["timing"] = ("per-launch time of 32 back-to-back launches (one per layer) in a hipGraph, "
                    "HIP events on the replay stream, 20 replays; the same kernel launched alone, "

@@ -615,11 +615,13 @@ hipError_t launch_attn(int dtype, const AttnArgs &a, hipStream_t s) {
 }
 
 // Split plan: a pure function of the shape (unless a test forces a plan
-// through kvd_set_plan_override), so results are reproducible run to run. The thresholds come from timing back-to-back launches in a graph on
+// through kvd_set_plan_override), so results are reproducible run to run.
+// The thresholds come from timing back-to-back launches in a graph on
 // MI355X: up to 96 KB of keys a unit stays on one workgroup (8 waves above
-// 40 KB with one query row), which avoids the cross-workgroup merge (two
-// memory round trips: the arrival count, then the partials); beyond that the
-// keys are split into chunks of at least 32 KB and at most 8 splits.
+// 40 KB with one query row), which avoids the cross-workgroup merge (three
+// memory round trips: the partial's stores, the arrival count, then the
+// partials); beyond that the keys are split into chunks of at least 32 KB
+// and at most 16 splits.
 AttnPlan plan_attn(int dtype, int units, int G, int N, int L, bool rope, bool allow_mfma) {
   AttnPlan p{};
   // Matrix-core tiles for several query rows per KV head: N > 1 queries, or
@@ -643,8 +645,15 @@ AttnPlan plan_attn(int dtype, int units, int G, int N, int L, bool rope, bool al
     if (tiles < 256 && unit_bytes > 32 * 1024 && wide_ok) waves = 8;  // measured (self, 1 row)
   } else {
     // at least 32 KB of keys per workgroup (one round of loads for 4 waves),
-    // at most 8 splits (the merge costs grow with the split count)
-    chunk = max((32 * 1024) / key_bytes, (L + 7) / 8);
+    // at most 16 splits. More workgroups pull more bandwidth (a few CUs
+    // cannot stream a unit alone: the read probe over the 7.68 MB of one
+    // cross-attention layer takes 4.3 us on 120 workgroups, 3.5 on 240 and
+    // 2.9 on 960), and the merge reads every partial in one round trip, so
+    // 1500 frames x 20 heads run as 12 splits of 128 on 4 waves: 5.67 us
+    // back to back, against 6.10 for 6 splits of 256 on 8 waves and 6.06
+    // to 6.74 for 24 to 47 splits of 1 or 2 waves (more arrivals per
+    // counter, more partials)
+    chunk = max((32 * 1024) / key_bytes, (L + 15) / 16);
     // a chunk that gives each of 4 waves an even number of tiles goes to 8
     // waves instead, same chunk (measured: 6 splits of 1500 frames, 6.02
     // against 6.21 us; with one tile per wave, 4 waves stay ahead)

@@ -103,69 +103,73 @@ __device__ __forceinline__ void hoist_args(const AttnArgs &a) {
 // 0..S-1 in a fixed order, by one wavefront: it takes rows g_first,
 // g_first + g_step, ... (< gcount), one dim per lane (D equals the wavefront
 // width). Lane j reads m and l of partial j, so the max, the weights and
-// their sum are wavefront reductions; every lane reads o[dim] of a batch of
-// partials with all loads in flight, and the outputs are summed in partial
-// order so that the result does not depend on the arrival order.
-template <int GM>
-__device__ void merge_rows(const AttnArgs &a, size_t tile_id, int S, int g0, int gcount, int bkv,
-                           int hk, int g_first, int g_step) {
+// their sum are wavefront reductions; every lane reads o[dim] of all S
+// partials with every load in flight (one memory round trip whatever S is:
+// NB >= S is the load count a lane keeps ready), and the outputs are summed
+// in partial order so that the result does not depend on the arrival order.
+template <int GM, int NB, int MR>
+__device__ void merge_rows_nb(const AttnArgs &a, size_t tile_id, int S, int g0, int gcount,
+                              int bkv, int hk, int g_first, int g_step) {
   constexpr int D = kHeadDim;
-  constexpr int NB = 8;               // o loads in flight per lane (default plans: <= 8 splits)
-  constexpr int SS = GM * kPStride;   // floats between two partials of one row
-  constexpr int MR = GM < 4 ? GM : 4; // rows of one wave whose loads go out together
+  constexpr int SS = GM * kPStride;  // floats between two partials of one row
   static_assert(D == 64, "one lane per dim");
   const int lane = threadIdx.x & 63;
   const float *src = a.ws_part + tile_id * S * SS;
-  // one row from its loaded (m, l) of partial `lane` and o[dim] of the first
-  // NB partials; partials past NB (plans of more than NB splits) are loaded
-  // here, a batch at a time
-  auto reduce_row = [&](int g, float mj, float lj, const float (&ob)[NB]) {
-    const float *row = src + g * kPStride;
-    const float M = groups_max<1>(mj);
-    const float wj = (mj == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mj - M);
-    const float inv = __builtin_amdgcn_rcpf(groups_sum<1>(lj * wj));
-    float O = 0.f;
-    float ob2[NB];
-    for (int s0 = 0; s0 < S; s0 += NB) {
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        ob2[j] = ob[j];
-        if (s0 > 0) ob2[j] = (s0 + j < S) ? __builtin_bit_cast(float, fetch_u32(row + (s0 + j) * SS + lane)) : 0.f;
-      }
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        if (s0 + j < S) {
-          const float w = __builtin_bit_cast(
-              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), s0 + j));
-          O = fmaf(ob2[j], w, O);
-        }
-      }
-    }
-    a.out[out_row(a, row_id(a, bkv, hk, g0 + g)) + lane] = O * inv;
-  };
   for (int g1 = g_first; g1 < gcount; g1 += MR * g_step) {
-    // the loads of up to MR rows go out before any of them is reduced
+    // the loads of up to MR rows go out before any of them is reduced, with
+    // no branch around a load: rows past gcount read row g1 again and
+    // partials past S partial 0, and those values go unused
     float mj[MR], lj[MR], ob[MR][NB];
 #pragma unroll
     for (int r = 0; r < MR; ++r) {
-      const int g = g1 + r * g_step;
+      const int g = (g1 + r * g_step < gcount) ? g1 + r * g_step : g1;
       const float *row = src + g * kPStride;
-      mj[r] = -INFINITY;
-      lj[r] = 0.f;
-      if (g < gcount && lane < S) {
-        mj[r] = __builtin_bit_cast(float, fetch_u32(row + lane * SS + D));
-        lj[r] = __builtin_bit_cast(float, fetch_u32(row + lane * SS + D + 1));
-      }
+      const int jl = (lane < S) ? lane : 0;
+      mj[r] = __builtin_bit_cast(float, fetch_u32(row + jl * SS + D));
+      lj[r] = __builtin_bit_cast(float, fetch_u32(row + jl * SS + D + 1));
 #pragma unroll
       for (int j = 0; j < NB; ++j)
-        ob[r][j] = (g < gcount && j < S) ? __builtin_bit_cast(float, fetch_u32(row + j * SS + lane)) : 0.f;
+        ob[r][j] = __builtin_bit_cast(float, fetch_u32(row + ((j < S) ? j : 0) * SS + lane));
     }
 #pragma unroll
     for (int r = 0; r < MR; ++r) {
       const int g = g1 + r * g_step;
-      if (g < gcount) reduce_row(g, mj[r], lj[r], ob[r]);
+      if (g < gcount) {
+        const float m = (lane < S) ? mj[r] : -INFINITY;
+        const float l = (lane < S) ? lj[r] : 0.f;
+        const float M = groups_max<1>(m);
+        const float wj = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M);
+        const float inv = __builtin_amdgcn_rcpf(groups_sum<1>(l * wj));
+        float O = 0.f;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          if (j < S) {
+            const float w = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), j));
+            O = fmaf(ob[r][j], w, O);
+          }
+        }
+        a.out[out_row(a, row_id(a, bkv, hk, g0 + g)) + lane] = O * inv;
+      }
     }
   }
+}
+
+// The merge with a load count sized to S (at most kMaxSplits): up to 8
+// partials, up to 4 rows of a wave load together; more partials, fewer rows.
+template <int GM>
+__device__ void merge_rows(const AttnArgs &a, size_t tile_id, int S, int g0, int gcount, int bkv,
+                           int hk, int g_first, int g_step) {
+  constexpr int MR = GM < 4 ? GM : 4;
+  static_assert(kMaxSplits == 64, "the largest load count below covers kMaxSplits");
+  if (S <= 8)
+    merge_rows_nb<GM, 8, MR>(a, tile_id, S, g0, gcount, bkv, hk, g_first, g_step);
+  else if (S <= 16)
+    merge_rows_nb<GM, 16, (MR < 2 ? MR : 2)>(a, tile_id, S, g0, gcount, bkv, hk, g_first, g_step);
+  else if (S <= 32)
+    merge_rows_nb<GM, 32, 1>(a, tile_id, S, g0, gcount, bkv, hk, g_first, g_step);
+  else
+    merge_rows_nb<GM, 64, 1>(a, tile_id, S, g0, gcount, bkv, hk, g_first, g_step);
 }
 
 // After every thread has published its part of this workgroup's partial

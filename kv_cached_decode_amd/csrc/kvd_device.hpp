@@ -397,7 +397,15 @@ __device__ __forceinline__ uint32_t fetch_u32(const void *p) {
   return __hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// (the asm orders the compiler's memory accesses around the wait; the
+// builtin, the same wait again and free, tells the compiler's wait counting
+// that nothing is outstanding, so it guards no later load with waits for
+// loads issued before this point; gfx9 encoding: vmcnt 0, expcnt and lgkmcnt
+// at their maxima)
+__device__ __forceinline__ void wait_stores() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
 // Returns the arrival count before this one (call from one thread).
 __device__ __forceinline__ uint32_t arrive(uint32_t *counter) {
   return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
