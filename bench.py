@@ -847,9 +847,10 @@ def prefill_flops(B=8, Hq=9, P=512):
 
 
 def workload_prefill(torch, kb, reps):
-    """The GQA prefill attention alone (the matrix-core tile with one 16-row
-    tile per wave): B8, 9 query / 3 KV heads x 64, bf16, rotary base 1e4,
-    512 causal queries over 512 cached keys, one layer's cache per launch."""
+    """The GQA prefill attention alone (the prefill tile: 64 query rows per
+    workgroup, keys staged through LDS): B8, 9 query / 3 KV heads x 64, bf16,
+    rotary base 1e4, 512 causal queries over 512 cached keys, one layer's
+    cache per launch."""
     layers, P = 4, 512
     caches, q = _prefill_state(torch, kb, layers)
     out = torch.empty((8, 9, P, D), dtype=torch.float32, device="cuda")

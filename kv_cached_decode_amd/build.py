@@ -17,9 +17,14 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvdecode.so")
 OBJ_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["kvd_copy.hip", "kvd_attn.hip", "kvd_attn_mfma.hip", "kvd_verify.hip", "kvd_beam.hip",
-           "kvd_probe.hip", "kvd_static.hip",
+           "kvd_probe.hip", "kvd_static.hip", "kvd_prefill.hip",
            "kvd_api.cpp"]
 ARCH = "gfx950"
+# Per-file code generation options. The prefill tile keeps its matrix-core
+# accumulators in ordinary VGPRs (the VGPR form of v_mfma) instead of AGPRs:
+# its softmax reads and rescales them every step, and in AGPRs each of those
+# accesses costs a v_accvgpr copy (measured: 64 copies per 32-key step).
+FILE_FLAGS = {"kvd_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:
@@ -66,7 +71,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     for s in SOURCES:
         o = os.path.join(OBJ_DIR, os.path.splitext(s)[0] + ".o")
         objs.append(o)
-        cmds.append([cc, *flags, "-c", "-o", o, os.path.join(CSRC, s)])
+        cmds.append([cc, *flags, *FILE_FLAGS.get(s, []), "-c", "-o", o, os.path.join(CSRC, s)])
     jobs = jobs or min(len(cmds), max(1, min(8, os.cpu_count() or 1)))
     with ThreadPoolExecutor(jobs) as ex:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:

@@ -176,6 +176,9 @@ hipError_t launch_append(int dtype, const AppendArgs &a, hipStream_t s);
 hipError_t launch_reorder(int dtype, const ReorderArgs &a, hipStream_t s);
 hipError_t launch_attn(int dtype, const AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_mfma(int dtype, const AttnArgs &a, hipStream_t s);
+// Prefill-sized blocks of queries (a matrix-core plan of four 16-row tiles
+// per workgroup, no new rows): K/V staged through LDS once per workgroup.
+hipError_t launch_prefill(int dtype, const AttnArgs &a, hipStream_t s);
 hipError_t launch_verify(const VerifyArgs &a, hipStream_t s);
 
 // Beam-search candidate scoring.

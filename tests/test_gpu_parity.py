@@ -378,6 +378,47 @@ def test_prefill_tiles_paired(dtype, rope, N, ragged):
     assert e <= TOL[dtype], e
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("N", [96, 37])
+def test_query_block_over_cross_cache(dtype, N):
+    """A block of N queries per head over a 1500-frame cross cache (no mask):
+    with 96 rows the matrix-core prefill plan (every row sees every frame, the
+    last 64-key block ragged at 1500); with 37 the shared-tile plan."""
+    say(f"case: query block over cross cache {dtype} N={N}")
+    g = np.random.default_rng([46, N, len(dtype)])
+    B, H, F = 1, 20, 1500
+    xk = O.narrow(g.standard_normal((B, H, F, 64)) / 8, dtype)
+    xv = O.narrow(g.standard_normal((B, H, F, 64)) / 8, dtype)
+    q = O.narrow(g.standard_normal((B, H, N, 64)) / 8, dtype)
+    xc = kb.Cache(B, H, F, TORCH_DTYPE[dtype])
+    kb.kv_append(xc, to_dev(xk, dtype), to_dev(xv, dtype), 0)
+    out = kb.decode_attn_cross(to_dev(q, dtype), xc, F, 0.125, ws=_ws())
+    ox = O.ConcatCache(B, H, 64, dtype)
+    ox.set_once(xk, xv)
+    e = max_err(out, O.attend_cross(q, ox, 0.125))
+    assert e <= TOL[dtype], e
+
+
+@pytest.mark.parametrize("dtype,rope", [("f16", 0.0), ("bf16", 1e4), ("f16", 1e4)])
+@pytest.mark.parametrize("N,L", [(200, 200), (130, 333), (64, 64)])
+def test_prefill_blocks_mha(dtype, rope, N, L):
+    """One query head per KV head (no grouping), N causal queries at the end
+    of a cache of L rows: row blocks of 64 that end inside a sequence, cache
+    lengths that are not a multiple of the 64-key staging block."""
+    say(f"case: mha prefill {dtype} rope={rope} N={N} L={L}")
+    g = np.random.default_rng([47, N, L, len(dtype), int(rope)])
+    B, H, S = 2, 4, 352
+    k = O.narrow(g.standard_normal((B, H, S, 64)), dtype)
+    v = O.narrow(g.standard_normal((B, H, S, 64)), dtype)
+    q = O.narrow(g.standard_normal((B, H, N, 64)), dtype)
+    cache = kb.Cache.wrap(to_dev(k, dtype), to_dev(v, dtype))
+    out = kb.decode_attn_self(to_dev(q, dtype), cache, L, 0.125, rope_base=rope, ws=_ws())
+    oc = O.ConcatCache(B, H, 64, dtype)
+    oc.append(k[:, :, :L], v[:, :, :L])
+    e = max_err(out, O.attend_self(q, oc, 0.125, rope_base=rope))
+    assert e <= TOL[dtype], e
+
+
 # ------------------------------------------------------ speculative verify ----
 
 @pytest.mark.parametrize("L_before", list(I.WHISPER_VERIFY.extra["L_before"]))
