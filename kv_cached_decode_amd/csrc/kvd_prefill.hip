@@ -18,7 +18,7 @@
 //   S^T = K Q^T on v_mfma_f32_16x16x32 (lane l: scores of row l%16 against
 //   keys 4*(l/16)+i of each 16-key half), online softmax per row in the log2
 //   domain, O^T += V^T P^T with P fed as a high and a low part in the
-//   storage type and V^T built from 8-byte row chunks (dims interleaved).
+//   storage type and V^T read from LDS with the transpose read.
 // The K and V operands of a step are read from LDS once per wave and serve
 // all TPW tiles. Rotated queries are rotated in fp32 at their positions,
 // scaled by scale * log2(e), and fed as a high and a low part; stored
@@ -40,11 +40,25 @@ namespace {
 
 constexpr int kBlockKeys = 64;                // keys staged in LDS per block
 constexpr int kChunks = kHeadDim * 2 / 16;    // 16-byte chunks per K or V row
+// Workgroup shape, measured on the GQA prefill (B8, 9/3 heads, 512 causal
+// queries): 4 waves of one 16-row tile, 15.6 us; 2 or 8 waves of one tile
+// 16.6 / 16.8 us; two tiles per wave (4 or 2 waves) far slower.
 constexpr int kPrefillWaves = 4;              // waves per workgroup
 constexpr int kPrefillTiles = 1;              // 16-row tiles per wave
 
 // LDS slot of chunk ch of staged row r.
 __device__ __forceinline__ int swz(int r, int ch) { return r * kChunks + (ch ^ (r & 7)); }
+
+// LDS transpose read of 16-bit elements (ds_read_b64_tr_b16, gfx950): in
+// each group of 16 lanes, the 8 bytes that lanes 4j .. 4j + 3 address form
+// row j (16 elements, lane 4j + k's element e at column 4k + e) of a 4 x 16
+// block, and lane c receives column c: element c of rows 0, 1, 2, 3.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x4 lds_read_tr16(const void *p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4 *)(__attribute__((address_space(3))) const char *)p);
+}
 
 template <int DT, int NW, int TPW, bool ROPE, bool RAGGED>
 __global__ __launch_bounds__(64 * NW) void prefill_kernel(AttnArgs a) {
@@ -216,22 +230,27 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(AttnArgs a) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
           ka[h][t][kk] = s_k[buf][swz(32 * h + 16 * t + c, gq + 4 * kk)];
-    // V^T operand, half h, rows 4c + t: element t of each of the lane's 8 key
-    // chunks (keys 32h + {4gq + j (j < 4), 16 + 4gq + j - 4}, bytes [8c, 8c + 8))
+    // V^T operand, half h, dims 16t .. 16t + 15 (row c: dim 16t + c) against
+    // the lane's 8 keys 32h + {4gq + j, 16 + 4gq + j} (j < 4), from two LDS
+    // transpose reads: in each group of 16 lanes (one gq), lanes 4j .. 4j + 3
+    // read the 32 bytes of dims 16t .. 16t + 15 of key j of the four, and
+    // lane c receives dim 16t + c of all four keys
     u32x4 va[2][4];
+    const int tr_k = c & 3, tr_j = c >> 2;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      u32x2 vv[8];
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int rr = 32 * h + ((j < 4) ? 4 * gq + j : 16 + 4 * gq + j - 4);
-        vv[j] = reinterpret_cast<const u32x2 *>(&s_v[buf][swz(rr, c >> 1)])[c & 1];
+      for (int t = 0; t < 4; ++t) {
+        u32x2 w[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int rr = 32 * h + 16 * u + 4 * gq + tr_j;
+          const char *at = reinterpret_cast<const char *>(&s_v[buf][swz(rr, 2 * t + (tr_k >> 1))]) +
+                           8 * (tr_k & 1);
+          w[u] = __builtin_bit_cast(u32x2, lds_read_tr16(at));
+        }
+        va[h][t] = u32x4{w[0][0], w[0][1], w[1][0], w[1][1]};
       }
-      va[h][0] = u32x4{pair16<0>(vv[0], vv[1]), pair16<0>(vv[2], vv[3]), pair16<0>(vv[4], vv[5]), pair16<0>(vv[6], vv[7])};
-      va[h][1] = u32x4{pair16<1>(vv[0], vv[1]), pair16<1>(vv[2], vv[3]), pair16<1>(vv[4], vv[5]), pair16<1>(vv[6], vv[7])};
-      va[h][2] = u32x4{pair16<2>(vv[0], vv[1]), pair16<2>(vv[2], vv[3]), pair16<2>(vv[4], vv[5]), pair16<2>(vv[6], vv[7])};
-      va[h][3] = u32x4{pair16<3>(vv[0], vv[1]), pair16<3>(vv[2], vv[3]), pair16<3>(vv[4], vv[5]), pair16<3>(vv[6], vv[7])};
-    }
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
       if (s0 >= tmax[tt]) continue;  // uniform: no row of the tile sees these keys
@@ -326,18 +345,15 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(AttnArgs a) {
     block(Set1{}, b + 1);
   }
 
-  // ---- lane l holds O[row c][16gq + 4i + t] = o[t][i]
+  // ---- lane l holds O[row c][16t + 4gq + i] = o[t][i]
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
     const float l = groups_sum<16>(lsum[tt]);  // the row's keys were spread over the 4 lane groups
     if (active[tt]) {
       const float inv = 1.f / l;
-      float *orow = a.out + out_row(a, rid[tt]) + 16 * gq;
+      float *orow = a.out + out_row(a, rid[tt]) + 4 * gq;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4 v = f32x4{o[tt][0][i], o[tt][1][i], o[tt][2][i], o[tt][3][i]} * inv;
-        *reinterpret_cast<f32x4 *>(orow + 4 * i) = v;
-      }
+      for (int t = 0; t < 4; ++t) *reinterpret_cast<f32x4 *>(orow + 16 * t) = o[tt][t] * inv;
     }
   }
 }
