@@ -557,7 +557,7 @@ AttnPlan plan_attn_mfma(int units, int G, int L, bool rope) {
     // rotary values became shared: 6.95 us on 4 waves at length 768 against
     // 8.1-8.6 on 8.)
     const bool wide = !rope && tiles <= 256;
-    int chunk = (unit_bytes <= (wide ? 128 : 64) * 1024) ? L : max(min_chunk, (L + 7) / 8);
+    int chunk = (unit_bytes <= (wide ? 128 : 64) * 1024) ? L : max(min_chunk, (L + 15) / 16);
     if (forced > 0) chunk = forced;
     chunk = ((chunk + min_chunk - 1) / min_chunk) * min_chunk;
     const int max_splits = kMaxSplits;
@@ -580,19 +580,23 @@ AttnPlan plan_attn_mfma(int units, int G, int L, bool rope) {
     }
     p.chunk = chunk;
     p.splits = splits;
-    // 8 waves there when every wave has a step, or the keys are split
-    // anyway, and the workgroups number at most 256. Measured, back-to-back
-    // periods, 5 rows per tile (5 drafts, or 5 beams sharing the cross cache):
+    // 8 waves there when every wave has a step and the workgroups number at
+    // most 256. Measured, back-to-back periods, 5 rows per tile (5 drafts, or
+    // 5 beams sharing the cross cache):
     // - self step, one sequence: unsplit on 8 waves at length 300 / 448 / 512
-    //   6.08 / 6.67 / 6.78 us, against 7.09 / 7.2 / 7.55 split on 4 waves; at
-    //   640 and 1024, split chunks on 8 waves 7.26 / 7.2 against 7.55 / 7.53;
+    //   6.08 / 6.67 / 6.78 us, against 7.09 / 7.2 / 7.55 split on 4 waves;
     //   up to 128 keys 4 waves stay ahead (4.28 against 4.46 us at 64);
+    // - split chunks of 128 keys (every partial read in one round trip by the
+    //   merge): self at 640 / 1024 on 4 waves 6.25 / 6.50 us, against 6.44 /
+    //   6.67 on 8 waves of 128 and 6.73 / 6.83 on 8 waves of 256; cross
+    //   attention over 1500 frames (12 splits) on 4 waves 6.72 us, against
+    //   6.93 on 8 waves of 128 and 7.04 on 8 waves of 256 (6 splits);
     // - self step, 4 sequences (80 tiles) at length 448: unsplit on 8 waves
     //   7.4 us, against 8.4 split on 4 and 13.1 split on 8;
-    // - cross attention over 1500 frames: 7.99 -> 7.24 us on 8 waves at
-    //   B = 1 (120 workgroups), but 11.4 -> 14.2 us at B = 4 (480);
+    // - cross attention over 1500 frames at B = 4 (480 workgroups): 11.4 us
+    //   on 4 waves against 14.2 on 8;
     // - GQA decode steps with rotary keys at length 768: 6.95 -> 8.5 us.
-    if (wide && (splits > 1 || chunk >= 8 * kStep) && tiles * splits <= 256) p.waves = 8;
+    if (wide && chunk >= 8 * kStep && tiles * splits <= 256) p.waves = 8;
     if (ov.waves == 4 || (ov.waves == 8 && !rope)) p.waves = ov.waves;  // rotary: 4 waves
   }
   const size_t tiles = (size_t)units * p.row_tiles;

@@ -252,7 +252,7 @@ def test_plan_override_validation_and_reset(lib):
     assert f(-1, 17, 0) == -2
     assert f(-1, 0, -5) == -2
     base = kb.attn_workspace_bytes(1, 20, 1, 1500)
-    with kb.plan_override(chunk=128):                 # more splits: more partials
+    with kb.plan_override(waves=2, chunk=64):         # more splits: more partials
         forced = kb.attn_workspace_bytes(1, 20, 1, 1500)
     assert forced > base
     assert kb.attn_workspace_bytes(1, 20, 1, 1500) == base    # restored on exit
