@@ -24,7 +24,11 @@ ARCH = "gfx950"
 # accumulators in ordinary VGPRs (the VGPR form of v_mfma) instead of AGPRs:
 # its softmax reads and rescales them every step, and in AGPRs each of those
 # accesses costs a v_accvgpr copy (measured: 64 copies per 32-key step).
-FILE_FLAGS = {"kvd_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# The streaming attention kernel takes its first 11 arguments as plain
+# scalars (the values its first key loads need); the hardware preloads them
+# into SGPRs at wave start, about 0.25 us before a load of them would return.
+FILE_FLAGS = {"kvd_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+              "kvd_attn.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=11"]}
 
 
 def hipcc() -> str:

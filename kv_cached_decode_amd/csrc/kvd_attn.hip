@@ -41,33 +41,45 @@ struct AttnGeom {
 };
 
 template <int DT, int GM, bool FUSED, int NWMAX, bool ROPE, bool RAGGED, bool BEAM>
-__global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * NWMAX) void attn_kernel(KVD_LEAD_PARAMS, AttnArgs args) {
   using Geo = AttnGeom<DT>;
   constexpr int D = kHeadDim;
   constexpr int VE = Geo::VE, LPR = Geo::LPR, RPL = Geo::RPL, TILE = Geo::TILE;
   constexpr int ROWB = Geo::ROWB;
   constexpr int VPR = ROWB / 16;  // 16-byte vectors per row
+  // The struct: read through lead_struct() once the first key loads are out
+  // (16-bit caches with no per-row lengths or beam parents, which the first
+  // loads would need); otherwise the parameter itself, whose fields the
+  // compiler fetches where they are used, and the lead values taken from it
+  // too (fp32 kernels, which use more registers, would spill with both sets
+  // held in scalar registers).
+  constexpr bool kLateArgs = DT != F32 && !RAGGED && !BEAM;
+  const Lead ld = kLateArgs ? KVD_LEAD
+                            : Lead{static_cast<char *>(args.k), static_cast<char *>(args.v),
+                                   FastDiv{lead_hkv_m, lead_hkv_s}, args.Hkv, args.S_max, args.chunk,
+                                   args.L, args.causal_base, args.new_base, lead_nw};
+  AttnArgs a;
+  if constexpr (!kLateArgs) a = args;
 
   const int lane = threadIdx.x & 63;
   // wave-uniform values kept in scalar registers, so that the key loop and
   // its tests are scalar branches and not per-lane masks
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nw = blockDim.x >> 6;
+  const int nw = ld.nw;
   const int kr = lane / LPR;  // key row within a wave load
   const int ds = lane % LPR;  // dims [ds*VE, ds*VE + VE)
 
-  hoist_args(a);
+  // ---- the unit, its key range and its rows' bases: preloaded arguments
+  // only, so the first tiles' loads below wait for no memory access
   const int split = blockIdx.x, rt = blockIdx.y, unit = blockIdx.z;
-  const int bkv = unit / a.Hkv, hk = unit % a.Hkv;
-  const int g0 = rt * GM;
-  const int gcount = min(GM, a.G - g0);
-  const int k0 = split * a.chunk;
-  const RowSpan sp = row_span<RAGGED>(a, bkv);
-  const int kspan = min(k0 + a.chunk, sp.L);
+  const int bkv = (int)fast_div((uint32_t)unit, ld.div_Hkv), hk = unit - bkv * ld.Hkv;
+  const int k0 = split * ld.chunk;
+  const RowSpan sp = row_span<RAGGED>(a, bkv, ld.L, ld.causal_base, ld.new_base);
+  const int kspan = min(k0 + ld.chunk, sp.L);
 
-  const size_t head = (size_t)bkv * a.Hkv + hk;
-  char *kc = static_cast<char *>(a.k) + head * a.S_max * ROWB;
-  char *vc = static_cast<char *>(a.v) + head * a.S_max * ROWB;
+  const size_t head = (size_t)bkv * ld.Hkv + hk;
+  char *kc = ld.k + head * ld.S_max * ROWB;
+  char *vc = ld.v + head * ld.S_max * ROWB;
   const int nb0 = max(k0, sp.new_base);  // first new row of this key range
   // Where the cached rows are read: this unit's own rows, or (beam step:
   // reorder + append + attend) the rows of beam parent[b] in the source
@@ -80,34 +92,17 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
       if (a.dev_status && threadIdx.x == 0) *a.dev_status = kStatusBadShape;
       p = bkv;
     }
-    const size_t src = ((size_t)p * a.Hkv + hk) * a.S_max * ROWB;
+    const size_t src = ((size_t)p * ld.Hkv + hk) * ld.S_max * ROWB;
     ks = static_cast<const char *>(a.k_src) + src;
     vs = static_cast<const char *>(a.v_src) + src;
   }
 
-  // ---- query rows first: the wait for them then leaves the key loads
-  // below in flight (the row numbering costs a few instructions)
-  u32x4 qraw[GM], qpart[GM];
-  size_t orow[GM];  // element offset of each row in q's layout, which out shares
-#pragma unroll
-  for (int g = 0; g < GM; ++g) {
-    qraw[g] = u32x4{0, 0, 0, 0};
-    qpart[g] = u32x4{0, 0, 0, 0};
-    orow[g] = 0;
-    if (g < gcount) {
-      orow[g] = out_row(a, row_id(a, bkv, hk, g0 + g));
-      const char *qrow = static_cast<const char *>(a.q) + orow[g] * Storage<DT>::bytes;
-      qraw[g] = load16(qrow + ds * 16);
-      if (ROPE) qpart[g] = load16(qrow + (ds ^ (LPR / 2)) * 16);
-    }
-  }
-
   // ---- first tiles: when every query row sees all keys of a tile (a causal
   // row sees at least keys 0 .. causal_base) and none of them is new, the
-  // tile's loads go out before the rows' bookkeeping below. Without new rows,
-  // with few query rows and 4 waves (registers to spare; measured to pay only
-  // there), each wave keeps two tiles in flight: tile i + 2 is loaded into
-  // the buffer tile i just freed.
+  // tile's loads go out first, before the query rows and the rows'
+  // bookkeeping below. Without new rows, with few query rows and 4 waves
+  // (registers to spare; measured to pay only there), each wave keeps two
+  // tiles in flight: tile i + 2 is loaded into the buffer tile i just freed.
   constexpr int PF = (!FUSED && GM <= 2 && NWMAX <= 4) ? 2 : 1;
   u32x4 kA[kSteps], vA[kSteps], kB[PF == 2 ? kSteps : 1], vB[PF == 2 ? kSteps : 1];
   const int stride = nw * TILE;
@@ -129,6 +124,26 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
   if (early_a) load_plain(kA, vA, t0);
   if constexpr (PF == 2) {
     if (early_b) load_plain(kB, vB, t0 + stride);
+  }
+
+  // ---- query rows (their numbering and q's base come from the struct);
+  // vector loads complete in issue order, so they land after the first tiles
+  if constexpr (kLateArgs) a = lead_struct();
+  const int g0 = rt * GM;
+  const int gcount = min(GM, a.G - g0);
+  u32x4 qraw[GM], qpart[GM];
+  size_t orow[GM];  // element offset of each row in q's layout, which out shares
+#pragma unroll
+  for (int g = 0; g < GM; ++g) {
+    qraw[g] = u32x4{0, 0, 0, 0};
+    qpart[g] = u32x4{0, 0, 0, 0};
+    orow[g] = 0;
+    if (g < gcount) {
+      orow[g] = out_row(a, row_id(a, bkv, hk, g0 + g));
+      const char *qrow = static_cast<const char *>(a.q) + orow[g] * Storage<DT>::bytes;
+      qraw[g] = load16(qrow + ds * 16);
+      if (ROPE) qpart[g] = load16(qrow + (ds ^ (LPR / 2)) * 16);
+    }
   }
 
   // ---- which keys each query row sees (indices only, no memory access)
@@ -201,7 +216,7 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
     const char *kn = static_cast<const char *>(a.k_new) + head * a.T_new * ROWB;
     const char *vn = static_cast<const char *>(a.v_new) + head * a.T_new * ROWB;
     const int n = (kspan - nb0) * HALF_VECS;
-    for (int t = threadIdx.x; t < n; t += blockDim.x) {
+    for (int t = threadIdx.x; t < n; t += 64 * nw) {
       const int r = t / HALF_VECS, j = t % HALF_VECS;
       const int pos = nb0 + r;
       const size_t src = (size_t)(pos - sp.new_base) * ROWB;
@@ -463,18 +478,25 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(AttnArgs a) {
     merge_rows<GM>(a, tile_id, a.splits, g0, gcount, bkv, hk, 0, 1);
     return;
   }
-  for (int idx = threadIdx.x; idx < gcount * D; idx += blockDim.x) finish(idx);
+  for (int idx = threadIdx.x; idx < gcount * D; idx += 64 * nw) finish(idx);
   if (a.splits == 1) return;
-  merge_splits<GM>(a, tile_id, g0, gcount, bkv, hk);
+  merge_splits<GM>(a, tile_id, g0, gcount, bkv, hk, nw);
 }
 
 template <int DT, bool FUSED, bool ROPE, bool RAGGED, bool BEAM>
 void launch_gm(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
   switch (a.gm) {
-    case 1: launch_kernel(attn_kernel<DT, 1, FUSED, 4, ROPE, RAGGED, BEAM>, grid, block, s, a); break;
-    case 2: launch_kernel(attn_kernel<DT, 2, FUSED, 4, ROPE, RAGGED, BEAM>, grid, block, s, a); break;
-    case 4: launch_kernel(attn_kernel<DT, 4, FUSED, 4, ROPE, RAGGED, BEAM>, grid, block, s, a); break;
-    default: launch_kernel(attn_kernel<DT, 8, FUSED, 4, ROPE, RAGGED, BEAM>, grid, block, s, a); break;
+    case 1: launch_lead(attn_kernel<DT, 1, FUSED, 4, ROPE, RAGGED, BEAM>, grid, block, s, a); break;
+    case 2: launch_lead(attn_kernel<DT, 2, FUSED, 4, ROPE, RAGGED, BEAM>, grid, block, s, a); break;
+    case 4: launch_lead(attn_kernel<DT, 4, FUSED, 4, ROPE, RAGGED, BEAM>, grid, block, s, a); break;
+    default:
+      // fp32 tiles with rotary work stop at 4 rows (the plan's bucket): the
+      // 8-row fused variant would not fit its registers
+      if constexpr (DT == F32 && ROPE)
+        launch_lead(attn_kernel<DT, 4, FUSED, 4, ROPE, RAGGED, BEAM>, grid, block, s, a);
+      else
+        launch_lead(attn_kernel<DT, 8, FUSED, 4, ROPE, RAGGED, BEAM>, grid, block, s, a);
+      break;
   }
 }
 
@@ -482,7 +504,7 @@ void launch_gm(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
 // rotary work, so that it fits 128 registers without spilling.
 template <int DT, bool FUSED, bool RAGGED, bool BEAM>
 void launch_wide(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
-  launch_kernel(attn_kernel<DT, 1, FUSED, kMaxWaves, false, RAGGED, BEAM>, grid, block, s, a);
+  launch_lead(attn_kernel<DT, 1, FUSED, kMaxWaves, false, RAGGED, BEAM>, grid, block, s, a);
 }
 
 template <int DT, bool FUSED, bool RAGGED, bool BEAM = false>
@@ -635,7 +657,7 @@ AttnPlan plan_attn(int dtype, int units, int G, int N, int L, bool rope, bool al
   const PlanOverride ov = plan_override();
   const bool use_mfma = allow_mfma && dtype != F32 && (N > 1 || G >= 3) && ov.mfma != 0;
   if (use_mfma) return plan_attn_mfma(units, G, L, rope);
-  p.gm = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : 8;
+  p.gm = G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : (dtype == F32 && rope) ? 4 : 8;
   p.row_tiles = (G + p.gm - 1) / p.gm;
   const int tile = (dtype == F32) ? AttnGeom<F32>::TILE : AttnGeom<F16>::TILE;
   const int key_bytes = 2 * kHeadDim * ((dtype == F32) ? 4 : 2);  // K + V row

@@ -4,6 +4,8 @@
 // last workgroup of a tile to arrive.
 #pragma once
 
+#include <stddef.h>
+
 #include "kvd_device.hpp"
 #include "kvd_internal.hpp"
 
@@ -46,8 +48,9 @@ struct RowSpan {
   int L, causal_base, new_base;
 };
 template <bool RAGGED>
-__device__ __forceinline__ RowSpan row_span(const AttnArgs &a, int bkv) {
-  RowSpan s{a.L, a.causal_base, a.new_base};
+__device__ __forceinline__ RowSpan row_span(const AttnArgs &a, int bkv, int L, int causal_base,
+                                            int new_base) {
+  RowSpan s{L, causal_base, new_base};
   if constexpr (RAGGED) {
     const int len = a.lens[bkv];
     const int c = min(max(len, a.N), a.L);
@@ -57,6 +60,76 @@ __device__ __forceinline__ RowSpan row_span(const AttnArgs &a, int bkv) {
     if (a.new_base != INT_MAX) s.new_base = c - a.T_new;
   }
   return s;
+}
+template <bool RAGGED>
+__device__ __forceinline__ RowSpan row_span(const AttnArgs &a, int bkv) {
+  return row_span<RAGGED>(a, bkv, a.L, a.causal_base, a.new_base);
+}
+
+// The values a kernel's first key loads need, passed ahead of the argument
+// struct as plain scalar kernel arguments, which the code object has the
+// hardware preload into SGPRs at wave start (about 0.25 us before a load of
+// the struct would return): the K and V bases, the unit split (Hkv and its
+// divider), the cache row stride, the keys per split and the key range.
+struct Lead {
+  char *k, *v;
+  FastDiv div_Hkv;
+  int Hkv, S_max, chunk, L, causal_base, new_base, nw;  // nw: waves per workgroup
+};
+// A kernel's leading parameters that carry a Lead (in preload order), and the
+// Lead they make.
+#define KVD_LEAD_PARAMS                                                                      \
+  char *lead_k, char *lead_v, uint32_t lead_hkv_m, uint32_t lead_hkv_s, int lead_hkv,       \
+      int lead_smax, int lead_chunk, int lead_L, int lead_cb, int lead_nb, int lead_nw
+#define KVD_LEAD                                                                             \
+  Lead {                                                                                     \
+    lead_k, lead_v, FastDiv{lead_hkv_m, lead_hkv_s}, lead_hkv, lead_smax, lead_chunk, lead_L, \
+        lead_cb, lead_nb, lead_nw                                                            \
+  }
+typedef void (*LeadKernel)(char *, char *, uint32_t, uint32_t, int, int, int, int, int, int,
+                           int, AttnArgs);
+// The kernarg segment of such a kernel: its parameters laid out in order with
+// their natural alignment, then the hidden arguments.
+struct LeadLayout {
+  char *k, *v;
+  uint32_t hkv_m, hkv_s;
+  int hkv, smax, chunk, L, cb, nb, nw;
+  AttnArgs args;
+};
+constexpr size_t kLeadArgsOffset = offsetof(LeadLayout, args);
+static_assert(kLeadArgsOffset == 56, "13 dwords of lead parameters, then the struct 8-aligned");
+// The argument struct of a kernel with Lead parameters, read from the kernarg
+// segment where this is called and not earlier: the segment pointer passes
+// through an empty asm the compiler cannot move, so the struct's scalar loads
+// are issued after the code before the call (the first key loads). Scalar
+// loads complete out of order, so a wait for one of them (the compiler puts
+// one wherever it reuses a register a pending load targets) is a wait for
+// all; issued at the top, they held back the first key loads.
+__device__ __forceinline__ AttnArgs lead_struct() {
+#if __HIP_DEVICE_COMPILE__
+  typedef const __attribute__((address_space(4))) char cchar4;
+  typedef const __attribute__((address_space(4))) uint32_t cword4;
+  cchar4 *p = (cchar4 *)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  // word by word: constant-memory words (scalar loads) into the local struct
+  cword4 *w = reinterpret_cast<cword4 *>(p + kLeadArgsOffset);
+  AttnArgs r;
+  uint32_t *d = reinterpret_cast<uint32_t *>(&r);
+  static_assert(sizeof(AttnArgs) % 4 == 0, "whole words");
+#pragma unroll
+  for (size_t i = 0; i < sizeof(AttnArgs) / 4; ++i) d[i] = w[i];
+  return r;
+#else
+  return AttnArgs{};  // host pass: never called
+#endif
+}
+// Launch of a kernel with Lead parameters: the Lead from the call's arguments.
+inline void launch_lead(LeadKernel kernel, dim3 grid, dim3 block, hipStream_t s,
+                        const AttnArgs &a) {
+  const FastDiv fd = make_fast_div((uint32_t)a.Hkv);
+  launch_kernel(kernel, grid, block, s, static_cast<char *>(a.k), static_cast<char *>(a.v), fd.m,
+                fd.s, a.Hkv, a.S_max, a.chunk, a.L, a.causal_base, a.new_base,
+                (int)(block.x / 64), AttnArgs(a));
 }
 
 // Online softmax (log2 domain), one row, one step of keys: mt is the step's
@@ -108,7 +181,7 @@ __device__ __forceinline__ void hoist_args(const AttnArgs &a) {
 // NB >= S is the load count a lane keeps ready), and the outputs are summed
 // in partial order so that the result does not depend on the arrival order.
 template <int GM, int NB, int MR>
-__device__ void merge_rows_nb(const AttnArgs &a, size_t tile_id, int S, int g0, int gcount,
+__device__ __forceinline__ void merge_rows_nb(const AttnArgs &a, size_t tile_id, int S, int g0, int gcount,
                               int bkv, int hk, int g_first, int g_step) {
   constexpr int D = kHeadDim;
   constexpr int SS = GM * kPStride;  // floats between two partials of one row
@@ -158,7 +231,7 @@ __device__ void merge_rows_nb(const AttnArgs &a, size_t tile_id, int S, int g0, 
 // The merge with a load count sized to S (at most kMaxSplits): up to 8
 // partials, up to 4 rows of a wave load together; more partials, fewer rows.
 template <int GM>
-__device__ void merge_rows(const AttnArgs &a, size_t tile_id, int S, int g0, int gcount, int bkv,
+__device__ __forceinline__ void merge_rows(const AttnArgs &a, size_t tile_id, int S, int g0, int gcount, int bkv,
                            int hk, int g_first, int g_step) {
   constexpr int MR = GM < 4 ? GM : 4;
   static_assert(kMaxSplits == 64, "the largest load count below covers kMaxSplits");
@@ -178,8 +251,8 @@ __device__ void merge_rows(const AttnArgs &a, size_t tile_id, int S, int g0, int
 // each of its waves taking every nw-th row. No LDS and no barrier in the
 // merge.
 template <int GM>
-__device__ void merge_splits(const AttnArgs &a, size_t tile_id, int g0, int gcount, int bkv,
-                             int hk) {
+__device__ __forceinline__ void merge_splits(const AttnArgs &a, size_t tile_id, int g0, int gcount, int bkv,
+                             int hk, int nw) {
   __shared__ int s_last;
   wait_stores();
   __syncthreads();
@@ -191,7 +264,7 @@ __device__ void merge_splits(const AttnArgs &a, size_t tile_id, int g0, int gcou
   }
   __syncthreads();
   if (!s_last) return;
-  merge_rows<GM>(a, tile_id, a.splits, g0, gcount, bkv, hk, threadIdx.x >> 6, blockDim.x >> 6);
+  merge_rows<GM>(a, tile_id, a.splits, g0, gcount, bkv, hk, threadIdx.x >> 6, nw);
 }
 
 }  // namespace kvd

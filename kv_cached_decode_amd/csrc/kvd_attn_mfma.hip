@@ -477,7 +477,7 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
       }
     }
     if (a.splits == 1) return;
-    merge_splits<kRows>(a, tile_id, g0, gcount, bkv, hk);
+    merge_splits<kRows>(a, tile_id, g0, gcount, bkv, hk, NW);
   }
 }
 

@@ -200,9 +200,13 @@ __device__ __forceinline__ double rope_theta_at(const RopeTheta &r, int i) {
   double t = 1.0;
 #pragma unroll
   for (int k = 0; k < 5; ++k) t = t * (((i >> k) & 1) ? r.pw[k] : 1.0);
-  uint32_t w = r.delta[0];
+  // (each word taken as a wave-uniform value first: a select between the
+  // words themselves, which the optimiser would otherwise turn into one load
+  // at a selected offset, a per-lane memory access)
+  uint32_t w = __builtin_amdgcn_readfirstlane(r.delta[0]);
 #pragma unroll
-  for (int q = 1; q < kHeadDim / 8; ++q) w = ((i >> 2) == q) ? r.delta[q] : w;
+  for (int q = 1; q < kHeadDim / 8; ++q)
+    w = ((i >> 2) == q) ? __builtin_amdgcn_readfirstlane(r.delta[q]) : w;
   const int d = (int)(int8_t)(w >> (8 * (i & 3)));
   return __builtin_bit_cast(double, __builtin_bit_cast(int64_t, t) + (int64_t)d);
 }
