@@ -112,11 +112,13 @@ template <int DT> __device__ __forceinline__ u32x4 pack16(const float *in) {
 //    the rotation in fp64 and one rounding to the storage type. The result
 //    is the correctly rounded rotation unless the exact value lies within
 //    about 2^-50 (relative) of a rounding boundary of the storage type.
-//  - Queries (RopeStep, rope_angle_cs): theta_i = 2^(-i step) in fp64 from
-//    the host's step = 2 log2(base) / D (one exp2 per run of pairs, then
-//    multiplies by 2^(-step); a few ulps from the exact theta_i), fp32 Taylor
-//    polynomials of y (degree 10 and 9, truncation below 2^-28) and the
-//    rotation in fp32: queries are not stored, so they only need to be
+//  - Queries (RopeStep, rope_angle_cs): theta_i = ratio^i in fp64 with the
+//    host's ratio = 2^(-step), step = 2 log2(base) / D (squarings and a few
+//    multiplies; a few ulps from the exact theta_i), the reduction with the
+//    first double of pi/2 only (the rest moves y by k * 2^-53.9, below 2^-30
+//    for every position under 2^24, far below fp32's resolution), fp32
+//    Taylor polynomials of y (degree 10 and 9, truncation below 2^-28) and
+//    the rotation in fp32: queries are not stored, so they only need to be
 //    accurate, and one definition serves every kernel and plan, so a query
 //    is rotated with the same bits everywhere. No memory access.
 // The quadrant k mod 4 maps cos y / sin y onto cos / sin of the full angle.
@@ -134,8 +136,10 @@ __device__ __forceinline__ double rope_reduce(int pos, double theta, int &quadra
 }
 
 __device__ __forceinline__ void rope_angle_cs(int pos, double theta, float &c, float &s) {
-  int q;
-  const float y = (float)rope_reduce(pos, theta, q), y2 = y * y;
+  const double ang = (double)pos * theta;
+  const double k = rint(ang * 0x1.45f306dc9c883p-1);  // 2 / pi
+  const int q = (int)k & 3;
+  const float y = (float)fma(-k, 0x1.921fb54442d18p+0, ang), y2 = y * y;  // pi/2, first 53 bits
   float ps = fmaf(y2, 2.7557319e-06f, -1.9841270e-04f);  // 1/9!, -1/7!
   ps = fmaf(ps, y2, 8.3333333e-03f);                     // 1/5!
   ps = fmaf(ps, y2, -1.6666667e-01f);                    // -1/3!
@@ -212,15 +216,31 @@ __device__ __forceinline__ double rope_theta_at(const RopeTheta &r, int i) {
 }
 
 // Query angles: pair i's theta from RopeStep. For a run of n consecutive
-// pairs i0 .. i0 + n - 1 (i0 a multiple of n), theta_i0 = exp2(-i0 step) and
-// each next theta one fp64 multiply by ratio; rope_cos_sin_pair gives pair i
-// alone bit for bit what the run that holds it gives.
+// pairs i0 .. i0 + n - 1 (n a power of two, i0 a multiple of n), theta_i0 =
+// (ratio^n)^(i0 / n), ratio^n by squarings and its power by the bits of
+// i0 / n, and each next theta one fp64 multiply by ratio; rope_cos_sin_pair
+// gives pair i alone bit for bit what the run that holds it gives.
 struct RopeStep {
   double step, ratio;
 };
 template <int n>
+__device__ __forceinline__ double rope_theta_q(int i0, double ratio) {
+  static_assert(n >= 1 && (n & (n - 1)) == 0 && n <= kHeadDim / 2, "runs of a power of two");
+  double p = ratio;
+#pragma unroll
+  for (int b = 1; b < n; b *= 2) p *= p;  // ratio^n
+  const int j = i0 / n;
+  double t = (j & 1) ? p : 1.0;
+#pragma unroll
+  for (int b = 1; (1 << b) < kHeadDim / 2 / n; ++b) {
+    p *= p;
+    t = ((j >> b) & 1) ? t * p : t;
+  }
+  return t;
+}
+template <int n>
 __device__ __forceinline__ void rope_cos_sin_run(int pos, int i0, RopeStep r, float *c, float *s) {
-  double theta = exp2(-(double)i0 * r.step);
+  double theta = rope_theta_q<n>(i0, r.ratio);
 #pragma unroll
   for (int e = 0; e < n; ++e) {
     rope_angle_cs(pos, theta, c[e], s[e]);
@@ -230,7 +250,7 @@ __device__ __forceinline__ void rope_cos_sin_run(int pos, int i0, RopeStep r, fl
 template <int n>
 __device__ __forceinline__ void rope_cos_sin_pair(int pos, int i, RopeStep r, float &c, float &s) {
   const int e = i & (n - 1);
-  double theta = exp2(-(double)(i - e) * r.step);
+  double theta = rope_theta_q<n>(i - e, r.ratio);
 #pragma unroll
   for (int t = 0; t < n - 1; ++t) theta = (t < e) ? theta * r.ratio : theta;
   rope_angle_cs(pos, theta, c, s);

@@ -419,6 +419,30 @@ def test_prefill_blocks_mha(dtype, rope, N, L):
     assert e <= TOL[dtype], e
 
 
+@pytest.mark.parametrize("dtype,rope", [("f16", 0.0), ("bf16", 1e4), ("bf16", 0.0)])
+@pytest.mark.parametrize("B,Hkv,group,N,L", [(2, 2, 3, 384, 384), (1, 4, 1, 256, 600), (3, 1, 2, 320, 330)])
+def test_prefill_long_row_blocks(dtype, rope, B, Hkv, group, N, L):
+    """Causal prefill with row blocks of 64 that tile the sequences and up to
+    10 key blocks per row block: 384 queries from position 0, 256 queries
+    after 344 cached rows, 320 queries after 10 rows; the same call twice
+    gives the same bits."""
+    say(f"case: prefill long row blocks {dtype} rope={rope} B={B} Hkv={Hkv} group={group} N={N} L={L}")
+    g = np.random.default_rng([48, B, Hkv, group, N, L, len(dtype), int(rope)])
+    Hq, S = Hkv * group, L + 8
+    k = O.narrow(g.standard_normal((B, Hkv, S, 64)), dtype)
+    v = O.narrow(g.standard_normal((B, Hkv, S, 64)), dtype)
+    q = O.narrow(g.standard_normal((B, Hq, N, 64)), dtype)
+    cache = kb.Cache.wrap(to_dev(k, dtype), to_dev(v, dtype))
+    ws = _ws()
+    out = kb.decode_attn_self(to_dev(q, dtype), cache, L, 0.125, rope_base=rope, ws=ws)
+    again = kb.decode_attn_self(to_dev(q, dtype), cache, L, 0.125, rope_base=rope, ws=ws)
+    assert torch.equal(out, again)
+    oc = O.ConcatCache(B, Hkv, 64, dtype)
+    oc.append(k[:, :, :L], v[:, :, :L])
+    e = max_err(out, O.attend_self(q, oc, 0.125, rope_base=rope))
+    assert e <= TOL[dtype], e
+
+
 # ------------------------------------------------------ speculative verify ----
 
 @pytest.mark.parametrize("L_before", list(I.WHISPER_VERIFY.extra["L_before"]))
