@@ -288,8 +288,7 @@ int prepare_self(AttnArgs &a, const void *q, const void *k_new, const void *v_ne
   a.T_new = k_new ? N : 0;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.rope_base = rope_base;
-  a.rope_step = rope_base > 0.f ? 2.0 * log2((double)rope_base) / kvd::kHeadDim : 0.0;
-  a.rope_ratio = exp2(-a.rope_step);
+  a.rope_ratio = exp2(-(rope_base > 0.f ? 2.0 * log2((double)rope_base) / kvd::kHeadDim : 0.0));
   if (!rope_theta_of(rope_base, a.rope_theta)) return KVD_ERR_SHAPE;
   return prepare_attn(a, cache->dtype, ws, ws_bytes);
 }

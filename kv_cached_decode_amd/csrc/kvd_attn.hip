@@ -204,7 +204,7 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(KVD_LEAD_PARAMS, AttnA
       for (int e = 0; e < VE; ++e) thn[e] = rope_theta_at(a.rope_theta, (threadIdx.x % HALF_VECS) * VE + e);
     }
     rpos = sp.causal_base + row_id(a, bkv, hk, g0).i;
-    rope_slice_cs<DT>(ds, rpos, RopeStep{a.rope_step, a.rope_ratio}, rc, rs);
+    rope_slice_cs<DT>(ds, rpos, RopeStep{a.rope_ratio}, rc, rs);
   }
 
   // ---- fused append: the new rows of this key range are rotated and
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(KVD_LEAD_PARAMS, AttnA
         const RowId r = row_id(a, bkv, hk, g0 + g);
         const int pos = sp.causal_base + r.i;
         if (pos != rpos) {  // rows of one position share their cos / sin
-          rope_slice_cs<DT>(ds, pos, RopeStep{a.rope_step, a.rope_ratio}, rc, rs);
+          rope_slice_cs<DT>(ds, pos, RopeStep{a.rope_ratio}, rc, rs);
           rpos = pos;
         }
         rope_slice_f32<DT>(qraw[g], qpart[g], ds, rc, rs, qf[g]);

@@ -312,7 +312,7 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
       for (int idx = lane; idx < a.N * 32; idx += 64) {
         const int pos = sp.causal_base + idx / 32, slot = (idx / 32) * 64 + idx % 32;
         float cl, sl;
-        rope_cos_sin_pair<8>(pos, idx % 32, RopeStep{a.rope_step, a.rope_ratio}, cl, sl);
+        rope_cos_sin_pair<8>(pos, idx % 32, RopeStep{a.rope_ratio}, cl, sl);
         tab[slot] = cl;
         tab[slot + 32] = sl;
       }
@@ -332,7 +332,7 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
       if (lane < new_items) rope_cos_sin_run64<8>(nb0 + lane / 4, thn, ncs, nsn);
     }
     if constexpr (ROPE)
-      rope_cos_sin_run<8>(sp.causal_base + r.i, gq * 8, RopeStep{a.rope_step, a.rope_ratio}, qc, qs);
+      rope_cos_sin_run<8>(sp.causal_base + r.i, gq * 8, RopeStep{a.rope_ratio}, qc, qs);
   }
   __builtin_amdgcn_sched_barrier(0);
 

@@ -221,7 +221,7 @@ __device__ __forceinline__ double rope_theta_at(const RopeTheta &r, int i) {
 // i0 / n, and each next theta one fp64 multiply by ratio; rope_cos_sin_pair
 // gives pair i alone bit for bit what the run that holds it gives.
 struct RopeStep {
-  double step, ratio;
+  double ratio;  // 2^(-step), step = 2 log2(base) / D
 };
 template <int n>
 __device__ __forceinline__ double rope_theta_q(int i0, double ratio) {

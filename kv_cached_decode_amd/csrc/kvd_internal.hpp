@@ -101,8 +101,7 @@ struct AttnArgs {
   const int32_t *parent;         // [Bkv] beam step parents (k, v are then the destination), or null
   float scale_log2;              // scale * log2(e)
   float rope_base;               // > 0: rotate q at causal_base + i (and new keys)
-  double rope_step;              // 2 log2(base) / D
-  double rope_ratio;             // 2^(-rope_step): queries turn pair i by theta_i = rope_ratio^i
+  double rope_ratio;             // 2^(-2 log2(base) / D): queries turn pair i by theta_i = rope_ratio^i
   RopeTheta rope_theta;          // new keys: the exact theta_i (as kv_append stores them)
   // plan
   int chunk;                     // keys per workgroup

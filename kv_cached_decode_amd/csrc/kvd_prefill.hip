@@ -208,7 +208,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(AttnArgs a) {
   u32x4 qhi[2], qlo[2];
   if constexpr (ROPE) {
     float qc[8], qs[8], x0[8], x1[8];
-    rope_cos_sin_run<8>(sp.causal_base + rid.i, gq * 8, RopeStep{a.rope_step, a.rope_ratio}, qc, qs);
+    rope_cos_sin_run<8>(sp.causal_base + rid.i, gq * 8, RopeStep{a.rope_ratio}, qc, qs);
     unpack16<DT>(qraw[0], x0);
     unpack16<DT>(qraw[1], x1);
 #pragma unroll
