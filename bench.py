@@ -209,6 +209,11 @@ def _kernel_us(torch, kb, launch, n=64):
     return _event_durations(torch, kb, [lambda i=i: launch(i) for i in range(n)]) * 1e6
 
 
+# GPU clock cycles (about 4 ms at 2.3 GHz) the stream spins before a timed
+# region whose launches the host queues one by one
+GPU_QUEUE_SLEEP_CYCLES = 10_000_000
+
+
 def _graph_period(torch, calls, reps: int = 20):
     """Seconds per call when calls() run back to back inside one captured
     graph (as in a decode step); HIP events on the replay stream."""
@@ -226,6 +231,11 @@ def _graph_period(torch, calls, reps: int = 20):
     torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
+    # the GPU spins (outside the timed region) while the host queues every
+    # replay, so that no replay waits for the host: timed replays run back
+    # to back (without it the beam workload's cross period read 15 us
+    # against 6.7 on the same kernel)
+    torch.cuda._sleep(GPU_QUEUE_SLEEP_CYCLES)
     a.record()
     for _ in range(reps):
         g.replay()
