@@ -452,7 +452,7 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(KVD_LEAD_PARAMS, AttnA
       O = fmaf(ok ? ow : 0.f, f, O);
     }
     if (a.splits == 1) {
-      a.out[orow[g] + d] = O * __builtin_amdgcn_rcpf(Ls);
+      store_f32(a.out + orow[g] + d, O * __builtin_amdgcn_rcpf(Ls));
     } else {
       publish(part + g * kPStride + d, O);
       if (d == 0) {

@@ -222,7 +222,7 @@ __device__ __forceinline__ void merge_rows_nb(const AttnArgs &a, size_t tile_id,
             O = fmaf(ob[r][j], w, O);
           }
         }
-        a.out[out_row(a, row_id(a, bkv, hk, g0 + g)) + lane] = O * inv;
+        store_f32(a.out + out_row(a, row_id(a, bkv, hk, g0 + g)) + lane, O * inv);
       }
     }
   }

@@ -425,7 +425,7 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) orow[4 * i + t] = o[t][i] * inv;
+        for (int t = 0; t < 4; ++t) store_f32(orow + 4 * i + t, o[t][i] * inv);
       }
     }
     return;
@@ -467,7 +467,7 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
         O = fmaf(ok ? ow : 0.f, f, O);
       }
       if (a.splits == 1) {
-        a.out[out_row(a, row_id(a, bkv, hk, g0 + g)) + d] = O * __builtin_amdgcn_rcpf(Ls);
+        store_f32(a.out + out_row(a, row_id(a, bkv, hk, g0 + g)) + d, O * __builtin_amdgcn_rcpf(Ls));
       } else {
         publish(part + g * kPStride + d, O);
         if (d == 0) {

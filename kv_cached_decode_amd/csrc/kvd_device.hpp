@@ -21,12 +21,18 @@ template <> struct Storage<BF16> { static constexpr int bytes = 2; };
 // Elements per 16-byte vector.
 template <int DT> constexpr int vec_elems() { return 16 / Storage<DT>::bytes; }
 
+// Global memory, named as such: pointers that arrive through the argument
+// struct would otherwise be accessed with flat instructions (an address
+// space check per access, and counted in lgkmcnt as well as vmcnt).
+template <typename T>
+using global_ptr = __attribute__((address_space(1))) T *;
 __device__ __forceinline__ u32x4 load16(const void *p) {
-  return *reinterpret_cast<const u32x4 *>(p);
+  return *(const global_ptr<u32x4>)p;
 }
 __device__ __forceinline__ void store16(void *p, u32x4 v) {
-  *reinterpret_cast<u32x4 *>(p) = v;
+  *(global_ptr<u32x4>)p = v;
 }
+__device__ __forceinline__ void store_f32(float *p, float v) { *(global_ptr<float>)p = v; }
 
 // Two storage elements packed in one dword -> two floats (element 2i is the
 // low half of dword i, little endian).
@@ -404,22 +410,20 @@ __device__ __forceinline__ void rope_slice_f32(u32x4 mine, u32x4 partner, int ds
 // because the handed-over data never sits in a non-coherent cache.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void publish(float *p, float v) {
-  __hip_atomic_store(reinterpret_cast<uint32_t *>(p), __builtin_bit_cast(uint32_t, v),
-                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store((global_ptr<uint32_t>)p, __builtin_bit_cast(uint32_t, v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void publish(int32_t *p, int32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store((global_ptr<int32_t>)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void publish(uint64_t *p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store((global_ptr<uint64_t>)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t fetch_u64(const void *p) {
-  return __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load((global_ptr<const uint64_t>)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t fetch_u32(const void *p) {
-  return __hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load((global_ptr<const uint32_t>)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // (the asm orders the compiler's memory accesses around the wait; the
 // builtin, the same wait again and free, tells the compiler's wait counting
@@ -432,10 +436,11 @@ __device__ __forceinline__ void wait_stores() {
 }
 // Returns the arrival count before this one (call from one thread).
 __device__ __forceinline__ uint32_t arrive(uint32_t *counter) {
-  return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_fetch_add((global_ptr<uint32_t>)counter, 1u, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void reset_counter(uint32_t *counter) {
-  __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store((global_ptr<uint32_t>)counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // One rotary pair of 16-byte chunks of a new K/V row (chunk j in the first

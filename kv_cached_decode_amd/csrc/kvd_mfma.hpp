@@ -56,6 +56,8 @@ __device__ __forceinline__ void split_hi_lo(const float *x, u32x4 &hi, u32x4 &lo
   lo = round8<DT>(r);
 }
 
+__device__ __forceinline__ void store_f32x4(float *p, f32x4 v) { *(global_ptr<f32x4>)p = v; }
+
 // Element t (0..3) of two 8-byte chunks as one dword: (c0's, c1's << 16).
 template <int t>
 __device__ __forceinline__ uint32_t pair16(u32x2 c0, u32x2 c1) {

@@ -393,7 +393,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_kernel(AttnArgs a) {
     const float inv = 1.f / l;
     float *orow = a.out + out_row(a, rid) + 4 * gq;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) *reinterpret_cast<f32x4 *>(orow + 16 * t) = o[t] * inv;
+    for (int t = 0; t < 4; ++t) store_f32x4(orow + 16 * t, o[t] * inv);
   }
 }
 
