@@ -128,7 +128,16 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(KVD_LEAD_PARAMS, AttnA
 
   // ---- query rows (their numbering and q's base come from the struct);
   // vector loads complete in issue order, so they land after the first tiles
-  if constexpr (kLateArgs) a = lead_struct();
+  if constexpr (kLateArgs) {
+    a = lead_struct();
+    // the fields the query rows' numbering and addresses (and the new rows'
+    // loads) need, fetched in one round trip: left to the compiler, each
+    // went out at its first use, three scalar round trips before the query
+    // load
+    asm volatile("" ::"s"(a.q), "s"(a.G), "s"(a.N), "s"(a.group), "s"(a.Hq), "s"(a.Bkv),
+                 "s"(a.div_N.m), "s"(a.div_N.s), "s"(a.div_group.m), "s"(a.div_group.s));
+    if constexpr (FUSED) asm volatile("" ::"s"(a.k_new), "s"(a.v_new), "s"(a.T_new));
+  }
   const int g0 = rt * GM;
   const int gcount = min(GM, a.G - g0);
   u32x4 qraw[GM], qpart[GM];
