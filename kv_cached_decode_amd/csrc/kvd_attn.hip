@@ -218,7 +218,8 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(KVD_LEAD_PARAMS, AttnA
 
   // ---- fused append: the new rows of this key range are rotated and
   // rounded once into LDS (the loop reads them there); row tile 0 also writes
-  // them into the cache
+  // them into the cache, after the key loop (a store counts in vmcnt with
+  // the loads: issued here, every wait of the loop would wait for it too)
   __shared__ u32x4 s_new[FUSED ? 2 * kMaxFusedRows * VPR : 1];
   if constexpr (FUSED) {
     constexpr int HALF_VECS = kHeadDim / 2 / VE;
@@ -234,7 +235,6 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(KVD_LEAD_PARAMS, AttnA
       s_new[r * VPR + j + VPR / 2] = c.khi;
       s_new[(kMaxFusedRows + r) * VPR + j] = c.vlo;
       s_new[(kMaxFusedRows + r) * VPR + j + VPR / 2] = c.vhi;
-      if (rt == 0) store_pair<DT>(kc + (size_t)pos * ROWB, vc + (size_t)pos * ROWB, j, c);
     }
     __syncthreads();
   }
@@ -399,6 +399,22 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(KVD_LEAD_PARAMS, AttnA
       // the buffer is free now (see the two-tile form above)
       t0 += stride;
       if (t0 < kend) load_a(t0);
+    }
+  }
+
+  // ---- the fused append's cache writes (from LDS, which holds the rows as
+  // rotated and rounded above)
+  if constexpr (FUSED) {
+    if (rt == 0) {
+      constexpr int HALF_VECS = kHeadDim / 2 / VE;
+      const int n = (kspan - nb0) * HALF_VECS;
+      for (int t = threadIdx.x; t < n; t += 64 * nw) {
+        const int r = t / HALF_VECS, j = t % HALF_VECS;
+        const int pos = nb0 + r;
+        const PairChunks c{s_new[r * VPR + j], s_new[r * VPR + j + VPR / 2],
+                           s_new[(kMaxFusedRows + r) * VPR + j], s_new[(kMaxFusedRows + r) * VPR + j + VPR / 2]};
+        store_pair<DT>(kc + (size_t)pos * ROWB, vc + (size_t)pos * ROWB, j, c);
+      }
     }
   }
 
