@@ -117,7 +117,9 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
 
   // ---- new rows (decode_step_self): a wave that needs them loads them,
   // rotates them (exactly as kv_append does) while its key loads are in
-  // flight, and keeps them in its own slice of LDS, so no barrier is needed.
+  // flight, and keeps them in its own slice of LDS, so no barrier is needed;
+  // the one holding the first of them writes them into the cache after its
+  // key loop.
   // Lane l takes chunk pair l % 4 of new row l / 4 (N <= 16 rows: one each).
   constexpr int kNewSlice = 2 * kMaxFusedRows * VPR;  // K rows, then V rows
   __shared__ u32x4 s_new[FUSED ? NW * kNewSlice : 1];
@@ -350,7 +352,6 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
       my_new[rr * VPR + j + VPR / 2] = nw.khi;
       my_new[(kMaxFusedRows + rr) * VPR + j] = nw.vlo;
       my_new[(kMaxFusedRows + rr) * VPR + j + VPR / 2] = nw.vhi;
-      if (store_new && !pair_rot) store_pair<DT>(kc + (size_t)pos * ROWB, vc + (size_t)pos * ROWB, j, nw);
     }
     asm volatile("" ::: "memory");  // the slice is written before the wave reads it
     if constexpr (ROPE) {
@@ -368,14 +369,7 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
           kr[pr] = (uint16_t)w;
           kr[pr + kHeadDim / 2] = (uint16_t)(w >> 16);
         }
-        asm volatile("" ::: "memory");  // rotated before the wave reads or stores them
-        if (store_new && lane < new_items) {
-          const int rr = lane / 4, j = lane % 4, pos = nb0 + rr;
-          PairChunks c = nw;
-          c.klo = my_new[rr * VPR + j];
-          c.khi = my_new[rr * VPR + j + VPR / 2];
-          store_pair<DT>(kc + (size_t)pos * ROWB, vc + (size_t)pos * ROWB, j, c);
-        }
+        asm volatile("" ::: "memory");  // rotated before the wave reads them
       }
     }
   }
@@ -411,6 +405,19 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
     }
   }
   lsum = groups_sum<16>(lsum);  // the row's keys were spread over the 4 lane groups
+
+  // ---- the new rows into the cache, from the wave's slice, after the key
+  // loop (a store counts in vmcnt with the loads: issued before the loop,
+  // every wait for a key load there would wait for it too)
+  if constexpr (FUSED) {
+    if (store_new && lane < new_items) {
+      const int rr = lane / 4, j = lane % 4, pos = nb0 + rr;
+      const PairChunks c{my_new[rr * VPR + j], my_new[rr * VPR + j + VPR / 2],
+                         my_new[(kMaxFusedRows + rr) * VPR + j],
+                         my_new[(kMaxFusedRows + rr) * VPR + j + VPR / 2]};
+      store_pair<DT>(kc + (size_t)pos * ROWB, vc + (size_t)pos * ROWB, j, c);
+    }
+  }
 
   // ---- lane l holds O[row c][16gq + 4i + t] = o[t][i]; merge the phases
   // that shared the row tile, then write the rows or publish the partial
