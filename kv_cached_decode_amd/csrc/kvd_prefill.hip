@@ -2,16 +2,16 @@
 // head, causal among positions; [N] "nanoVLM における技術的実装", the prefill /
 // decode split) on gfx950 matrix cores, fp16/bf16 storage, no split over keys.
 //
-// A workgroup takes ROWS = 16 * NW * TPW consecutive query rows of one (cache
-// row, KV head) unit: wave w owns the TPW 16-row tiles w*TPW .. w*TPW+TPW-1.
-// The keys the workgroup's rows see, [0, kend), are staged through LDS in
-// blocks of 64: every thread loads its share of the next block's K and V
-// rows (16-byte loads) two blocks ahead, in two register sets used in turn,
-// and writes a block into the free LDS buffer while the waves compute on the
-// other, so each key is fetched from memory once per workgroup instead of
-// once per wave and its loads have two blocks of compute to land. LDS rows are 16-byte chunks
-// XOR-swizzled by the row index, so the 16 rows of one operand load spread
-// over the banks.
+// A workgroup takes ROWS = 16 * NW consecutive query rows of one (cache row,
+// KV head) unit; wave w owns the 16-row tile w. The keys the workgroup's rows
+// see, [0, kend), are staged through LDS in blocks of 64: every thread loads
+// its share of a block's K and V rows (16-byte loads) into one of two
+// register sets and writes it into LDS two iterations later, so each key is
+// fetched from memory once per workgroup instead of once per wave and its
+// loads have two iterations of compute to land. K runs one block ahead of V:
+// the score products of block b + 1 are issued between block b's row maxima
+// and its exponentials. LDS rows are 16-byte chunks XOR-swizzled by the row
+// index, so the 16 rows of one operand load spread over the banks.
 //
 // Per 64-key block and tile (two 32-key halves), as the shared matrix-core
 // tile computes each 32-key step:
@@ -19,12 +19,11 @@
 //   keys 4*(l/16)+i of each 16-key half), online softmax per row in the log2
 //   domain, O^T += V^T P^T with P fed as a high and a low part in the
 //   storage type and V^T read from LDS with the transpose read.
-// The K and V operands of a step are read from LDS once per wave and serve
-// all TPW tiles. Rotated queries are rotated in fp32 at their positions,
-// scaled by scale * log2(e), and fed as a high and a low part; stored
-// queries are exact in the storage type and their scores are scaled after
-// the product. Only the steps a row's causal limit cuts through are masked;
-// a wave skips the steps its tiles' rows do not see.
+// Rotated queries are rotated in fp32 at their positions, scaled by
+// scale * log2(e), and fed as a high and a low part; stored queries are exact
+// in the storage type and their scores are scaled after the product. Only
+// the blocks a row's causal limit cuts through are masked; a wave skips the
+// blocks its tile's rows do not see.
 #include <float.h>
 
 #include <type_traits>
