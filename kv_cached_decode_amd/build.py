@@ -20,14 +20,16 @@ SOURCES = ["kvd_copy.hip", "kvd_attn.hip", "kvd_attn_mfma.hip", "kvd_verify.hip"
            "kvd_probe.hip", "kvd_static.hip", "kvd_prefill.hip",
            "kvd_api.cpp"]
 ARCH = "gfx950"
-# Per-file code generation options. The prefill tile keeps its matrix-core
+# Per-file code generation options. The matrix-core kernels keep their
 # accumulators in ordinary VGPRs (the VGPR form of v_mfma) instead of AGPRs:
-# its softmax reads and rescales them every step, and in AGPRs each of those
-# accesses costs a v_accvgpr copy (measured: 64 copies per 32-key step).
+# their softmax reads and rescales them every step, and in AGPRs each of
+# those accesses costs a v_accvgpr copy (measured: 64 copies per 32-key step
+# in the prefill tile, 127 in the 5-row decode tile).
 # The streaming attention kernel takes its first 11 arguments as plain
 # scalars (the values its first key loads need); the hardware preloads them
 # into SGPRs at wave start, about 0.25 us before a load of them would return.
 FILE_FLAGS = {"kvd_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+              "kvd_attn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
               "kvd_attn.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=11"]}
 
 
