@@ -308,7 +308,14 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
   bool shared_cs = false;
   if constexpr (ROPE && RW == 1)
     shared_cs = FUSED ? (a.N <= kMaxFusedRows && sp.new_base == sp.causal_base) : a.N == 1;  // uniform
+  // pair_rot below: the exact angle of this lane's first new-key pair, here,
+  // under the loads' latency (it needs only the position and the pair)
+  double th_pair = 0.0, c_pair = 1.0, s_pair = 0.0;
   if (shared_cs) {
+    if constexpr (ROPE && RW == 1 && FUSED) {
+      th_pair = rope_theta_at(a.rope_theta, lane & 31);  // exact, as kv_append's
+      if (lane < new_items / (VPR / 2) * 32) rope_angle_cs64(nb0 + lane / 32, th_pair, c_pair, s_pair);
+    }
     if constexpr (ROPE && RW == 1) {
       float *tab = s_rope + wave * kRopeSlice;
       for (int idx = lane; idx < a.N * 32; idx += 64) {
@@ -357,11 +364,10 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
     if constexpr (ROPE) {
       if (pair_rot && new_items > 0) {  // uniform
         const int rows = new_items / (VPR / 2);
-        const double th = rope_theta_at(a.rope_theta, lane & 31);  // exact, as kv_append's
         for (int item = lane; item < rows * 32; item += 64) {  // pair item % 32 == lane % 32
           const int rr = item / 32, pr = item % 32;
-          double c64, s64;
-          rope_angle_cs64(nb0 + rr, th, c64, s64);
+          double c64 = c_pair, s64 = s_pair;
+          if (item != lane) rope_angle_cs64(nb0 + rr, th_pair, c64, s64);
           uint16_t *kr = reinterpret_cast<uint16_t *>(my_new + rr * VPR);
           float lo = widen16<DT>(kr[pr]), hi = widen16<DT>(kr[pr + kHeadDim / 2]);
           rotate_elem64<DT>(lo, hi, c64, s64);
