@@ -443,6 +443,28 @@ def test_prefill_long_row_blocks(dtype, rope, B, Hkv, group, N, L):
     assert e <= TOL[dtype], e
 
 
+@pytest.mark.parametrize("dtype,rope", [("f16", 0.0), ("bf16", 1e4)])
+def test_prefill_per_cu_order_partial_round(dtype, rope):
+    """A prefill grid whose units are a multiple of 8 (the per-CU workgroup
+    order applies) with 40 row blocks per unit: per XCD one full round of 32
+    workgroups and a reversed partial round of 8, so every (unit, row block)
+    pair must still be taken exactly once (8 rows x 1 KV head x 20 query
+    heads, 128 causal queries after 32 cached rows)."""
+    say(f"case: prefill per-CU order, partial round {dtype} rope={rope}")
+    g = np.random.default_rng([49, len(dtype), int(rope)])
+    B, Hkv, group, N, L = 8, 1, 20, 128, 160
+    Hq, S = Hkv * group, L
+    k = O.narrow(g.standard_normal((B, Hkv, S, 64)), dtype)
+    v = O.narrow(g.standard_normal((B, Hkv, S, 64)), dtype)
+    q = O.narrow(g.standard_normal((B, Hq, N, 64)), dtype)
+    cache = kb.Cache.wrap(to_dev(k, dtype), to_dev(v, dtype))
+    out = kb.decode_attn_self(to_dev(q, dtype), cache, L, 0.125, rope_base=rope, ws=_ws())
+    oc = O.ConcatCache(B, Hkv, 64, dtype)
+    oc.append(k, v)
+    e = max_err(out, O.attend_self(q, oc, 0.125, rope_base=rope))
+    assert e <= TOL[dtype], e
+
+
 # ------------------------------------------------------ speculative verify ----
 
 @pytest.mark.parametrize("L_before", list(I.WHISPER_VERIFY.extra["L_before"]))
