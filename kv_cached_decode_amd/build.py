@@ -25,11 +25,13 @@ ARCH = "gfx950"
 # their softmax reads and rescales them every step, and in AGPRs each of
 # those accesses costs a v_accvgpr copy (measured: 64 copies per 32-key step
 # in the prefill tile, 127 in the 5-row decode tile).
-# The streaming attention kernel takes its first 11 arguments as plain
-# scalars (the values its first key loads need); the hardware preloads them
-# into SGPRs at wave start, about 0.25 us before a load of them would return.
+# The streaming and the matrix-core decode kernels take their first 11
+# arguments as plain scalars (the values their first key loads need); the
+# hardware preloads them into SGPRs at wave start, about 0.25 us before a
+# load of them would return.
 FILE_FLAGS = {"kvd_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-              "kvd_attn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+              "kvd_attn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1",
+                                    "-mllvm", "-amdgpu-kernarg-preload-count=11"],
               "kvd_attn.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=11"]}
 
 

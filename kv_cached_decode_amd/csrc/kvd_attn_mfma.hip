@@ -39,27 +39,41 @@ constexpr int kStep = kMfmaStep;  // keys per MFMA step
 constexpr int kWaves = 4;         // prefill (one row tile per wave)
 
 // One 16-row tile `rt` of the workgroup's waves (see the kernel below).
-template <int DT, int RW, int NW, bool FUSED, bool ROPE, bool RAGGED>
-__device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) {
+// LATE: the struct is read from the kernel arguments only once the first key
+// loads are out (the values those need arrive preloaded in ld); otherwise
+// `args` is used from the start (per-row lengths: the first loads need them).
+template <int DT, int RW, int NW, bool FUSED, bool ROPE, bool RAGGED, bool LATE>
+__device__ __forceinline__ void attn_mfma_tile(const Lead &ld, const AttnArgs &args, const int rt) {
   constexpr int D = kHeadDim;
   constexpr int ROWB = kHeadDim * 2;
   constexpr int VPR = ROWB / 16;
   constexpr int NPH = NW / RW;  // waves sharing a row tile
   static_assert(DT != F32, "matrix-core tiles take 16-bit storage");
+  static_assert(!(LATE && RAGGED), "per-row lengths come from the struct");
 
-  hoist_args(a);
+  AttnArgs a;
+  // the struct fields every path uses, fetched in one round of scalar loads
+  auto fetch_args = [&]() {
+    hoist_args(a);
+    asm volatile("" ::"s"(a.scale_log2));
+    if constexpr (ROPE) asm volatile("" ::"s"(a.rope_ratio));
+  };
+  if constexpr (!LATE) {
+    a = args;
+    fetch_args();
+  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar addressing
   const int c = lane & 15, gq = lane >> 4;
   const int split = blockIdx.x, unit = blockIdx.z;
   const int phase = wave / RW;
-  const int bkv = unit / a.Hkv, hk = unit % a.Hkv;
-  const int k0 = split * a.chunk;
-  const RowSpan sp = row_span<RAGGED>(a, bkv);
-  const int kspan = min(k0 + a.chunk, sp.L);
-  const size_t head = (size_t)bkv * a.Hkv + hk;
-  char *kc = static_cast<char *>(a.k) + head * a.S_max * ROWB;
-  char *vc = static_cast<char *>(a.v) + head * a.S_max * ROWB;
+  const int bkv = (int)fast_div((uint32_t)unit, ld.div_Hkv), hk = unit - bkv * ld.Hkv;
+  const int k0 = split * ld.chunk;
+  const RowSpan sp = row_span<RAGGED>(a, bkv, ld.L, ld.causal_base, ld.new_base);
+  const int kspan = min(k0 + ld.chunk, sp.L);
+  const size_t head = (size_t)unit;  // bkv * Hkv + hk
+  char *kc = ld.k + head * ld.S_max * ROWB;
+  char *vc = ld.v + head * ld.S_max * ROWB;
   const int nb0 = max(k0, sp.new_base);
 
   // ---- the wave's first step goes out before anything else is computed
@@ -102,9 +116,13 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
   // start only once they had all landed, instead of under their latency.
   constexpr bool kSmallFirst = !FUSED || ROPE;
   const int grow = rt * kRows + c;
-  const bool active = grow < a.G;
+  bool active = false;
   RowId r{0, 0, 0};
-  if (active) r = row_id(a, bkv, hk, grow);
+  auto number_row = [&]() {
+    active = grow < a.G;
+    if (active) r = row_id(a, bkv, hk, grow);
+  };
+  if constexpr (!LATE) number_row();
   u32x4 qraw[2] = {u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}};
   auto load_q = [&]() {
     if (active) {
@@ -113,7 +131,7 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
       qraw[1] = load16(qrow + 64 + gq * 16);
     }
   };
-  if constexpr (kSmallFirst) load_q();
+  if constexpr (kSmallFirst && !LATE) load_q();
 
   // ---- new rows (decode_step_self): a wave that needs them loads them,
   // rotates them (exactly as kv_append does) while its key loads are in
@@ -139,11 +157,18 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
       nw.vhi = load16(vrow + 64 + j * 16);
     }
   };
-  if constexpr (FUSED && kSmallFirst) load_new();
+  if constexpr (FUSED && kSmallFirst && !LATE) load_new();
 
   const int kend_lo = min(kspan, (sp.causal_base < 0) ? sp.L : sp.causal_base + 1);
   const bool early = s0 + kStep <= kend_lo && (!FUSED || s0 + kStep <= nb0);  // uniform
   if (early) load_whole(s0, kA, vA);
+  if constexpr (LATE) {  // the struct, then what needs it
+    a = lead_struct();
+    fetch_args();
+    number_row();
+    if constexpr (kSmallFirst) load_q();
+    if constexpr (FUSED && kSmallFirst) load_new();
+  }
 
   // ---- the keys this lane's row sees
   const int lim = active ? ((sp.causal_base < 0) ? sp.L : sp.causal_base + r.i + 1) : 0;
@@ -495,19 +520,22 @@ __device__ __forceinline__ void attn_mfma_tile(const AttnArgs &a, const int rt) 
 }
 
 template <int DT, int RW, int NW, bool FUSED, bool ROPE, bool RAGGED>
-__global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(KVD_LEAD_PARAMS, AttnArgs a) {
+  const Lead ld = KVD_LEAD;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if constexpr (RW == NW && !FUSED) {
     if (a.pair) {  // causal prefill: tile t and its complement T - 1 - t
       const int T = (a.G + kRows - 1) / kRows;
       const int t = blockIdx.y * RW + wave;
       if (t >= (T + 1) / 2) return;  // no barrier follows in this mode
-      attn_mfma_tile<DT, RW, NW, FUSED, ROPE, RAGGED>(a, t);
-      if (T - 1 - t > t) attn_mfma_tile<DT, RW, NW, FUSED, ROPE, RAGGED>(a, T - 1 - t);
+      attn_mfma_tile<DT, RW, NW, FUSED, ROPE, RAGGED, false>(ld, a, t);
+      if (T - 1 - t > t) attn_mfma_tile<DT, RW, NW, FUSED, ROPE, RAGGED, false>(ld, a, T - 1 - t);
       return;
     }
+    attn_mfma_tile<DT, RW, NW, FUSED, ROPE, RAGGED, false>(ld, a, blockIdx.y * RW + wave % RW);
+  } else {
+    attn_mfma_tile<DT, RW, NW, FUSED, ROPE, RAGGED, !RAGGED>(ld, a, blockIdx.y * RW + wave % RW);
   }
-  attn_mfma_tile<DT, RW, NW, FUSED, ROPE, RAGGED>(a, blockIdx.y * RW + wave % RW);
 }
 
 template <int DT, int RW, int NW, bool RAGGED>
@@ -518,14 +546,14 @@ void launch_rwr(const AttnArgs &a, dim3 grid, hipStream_t s) {
     // rotary tiles always run on 4 waves (launch_dt): their per-wave LDS
     // tables would not fit 8
     (void)rope;
-    if (fused) launch_kernel(attn_mfma_kernel<DT, RW, NW, true, false, RAGGED>, grid, block, s, a);
-    else launch_kernel(attn_mfma_kernel<DT, RW, NW, false, false, RAGGED>, grid, block, s, a);
+    if (fused) launch_lead(attn_mfma_kernel<DT, RW, NW, true, false, RAGGED>, grid, block, s, a);
+    else launch_lead(attn_mfma_kernel<DT, RW, NW, false, false, RAGGED>, grid, block, s, a);
   } else if (fused) {
-    if (rope) launch_kernel(attn_mfma_kernel<DT, RW, NW, true, true, RAGGED>, grid, block, s, a);
-    else launch_kernel(attn_mfma_kernel<DT, RW, NW, true, false, RAGGED>, grid, block, s, a);
+    if (rope) launch_lead(attn_mfma_kernel<DT, RW, NW, true, true, RAGGED>, grid, block, s, a);
+    else launch_lead(attn_mfma_kernel<DT, RW, NW, true, false, RAGGED>, grid, block, s, a);
   } else {
-    if (rope) launch_kernel(attn_mfma_kernel<DT, RW, NW, false, true, RAGGED>, grid, block, s, a);
-    else launch_kernel(attn_mfma_kernel<DT, RW, NW, false, false, RAGGED>, grid, block, s, a);
+    if (rope) launch_lead(attn_mfma_kernel<DT, RW, NW, false, true, RAGGED>, grid, block, s, a);
+    else launch_lead(attn_mfma_kernel<DT, RW, NW, false, false, RAGGED>, grid, block, s, a);
   }
 }
 
