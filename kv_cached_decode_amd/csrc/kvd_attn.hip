@@ -104,6 +104,11 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(KVD_LEAD_PARAMS, AttnA
   // (registers to spare; measured to pay only there), each wave keeps two
   // tiles in flight: tile i + 2 is loaded into the buffer tile i just freed.
   constexpr int PF = (!FUSED && GM <= 2 && NWMAX <= 4) ? 2 : 1;
+  // Fused steps without rotation or beam parents: the wave whose tile holds
+  // new rows loads them straight from k_new / v_new into the tile's
+  // registers (no LDS staging, no barrier) and row tile 0 writes them into
+  // the cache from there. Otherwise they are staged through LDS.
+  constexpr bool kRegNew = FUSED && !ROPE && !BEAM;
   u32x4 kA[kSteps], vA[kSteps], kB[PF == 2 ? kSteps : 1], vB[PF == 2 ? kSteps : 1];
   const int stride = nw * TILE;
   int t0 = k0 + wave * TILE;
@@ -178,6 +183,13 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(KVD_LEAD_PARAMS, AttnA
   // except with new rows (see the fused loop).
   const int kcap = max((FUSED ? min(kend, nb0) : kend) - 1, 0);
   auto whole = [&](int t) { return t + TILE <= kend && (!FUSED || t + TILE <= nb0); };
+  // new rows of a tile, in registers of their own (kRegNew)
+  u32x4 nk[kRegNew ? kSteps : 1], nv[kRegNew ? kSteps : 1];
+  const char *knb = nullptr, *vnb = nullptr;
+  if constexpr (kRegNew) {
+    knb = static_cast<const char *>(a.k_new) + head * a.T_new * ROWB;
+    vnb = static_cast<const char *>(a.v_new) + head * a.T_new * ROWB;
+  }
   auto load_tile = [&](u32x4 *kd, u32x4 *vd, int t) {
     // one code path for both kinds of tile (a branch between two sets of
     // loads makes the compiler wait on the other set's registers); the base
@@ -192,6 +204,17 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(KVD_LEAD_PARAMS, AttnA
       const uint32_t off = (uint32_t)(min(t + s * RPL + kr, klast) - kbase) * ROWB + ds * 16;
       kd[s] = load16(kb + off);
       vd[s] = load16(vb + off);
+    }
+    if constexpr (kRegNew) {
+      if (t + TILE > nb0) {  // uniform: the tile holds new rows; every lane loads one (clamped)
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+          const int r = min(max(t + s * RPL + kr - sp.new_base, 0), a.T_new - 1);
+          const uint32_t off = (uint32_t)r * ROWB + ds * 16;
+          nk[s] = load16(knb + off);
+          nv[s] = load16(vnb + off);
+        }
+      }
     }
   };
   auto load_a = [&](int t) { load_tile(kA, vA, t); };
@@ -220,8 +243,8 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(KVD_LEAD_PARAMS, AttnA
   // rounded once into LDS (the loop reads them there); row tile 0 also writes
   // them into the cache, after the key loop (a store counts in vmcnt with
   // the loads: issued here, every wait of the loop would wait for it too)
-  __shared__ u32x4 s_new[FUSED ? 2 * kMaxFusedRows * VPR : 1];
-  if constexpr (FUSED) {
+  __shared__ u32x4 s_new[(FUSED && !kRegNew) ? 2 * kMaxFusedRows * VPR : 1];
+  if constexpr (FUSED && !kRegNew) {
     constexpr int HALF_VECS = kHeadDim / 2 / VE;
     const char *kn = static_cast<const char *>(a.k_new) + head * a.T_new * ROWB;
     const char *vn = static_cast<const char *>(a.v_new) + head * a.T_new * ROWB;
@@ -293,7 +316,7 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(KVD_LEAD_PARAMS, AttnA
 
   // one tile: the keys [t0, t0 + TILE) of this wave, held in (kv, vv)
   auto step = [&](u32x4 *kv, u32x4 *vv) {
-    if constexpr (FUSED) overlay_new(kv, vv);
+    if constexpr (FUSED && !kRegNew) overlay_new(kv, vv);
     float sc[kSteps][GM];
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
@@ -364,7 +387,28 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(KVD_LEAD_PARAMS, AttnA
           }
         }
       }
-      if constexpr (FUSED) overlay_new(kA, vA);
+      if constexpr (FUSED && !kRegNew) overlay_new(kA, vA);
+      if constexpr (kRegNew) {
+        // the tile's new rows over its clamped ones; row tile 0 writes them
+        // into the cache (no load of this wave follows a tile with new rows
+        // unless it has a single wave)
+        if (t0 + TILE > nb0) {  // uniform
+#pragma unroll
+          for (int s = 0; s < kSteps; ++s) {
+            const int key = t0 + s * RPL + kr;
+            const bool fresh = key >= nb0 && key < kend;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              kA[s][i] = fresh ? nk[s][i] : kA[s][i];
+              vA[s][i] = fresh ? nv[s][i] : vA[s][i];
+            }
+            if (rt == 0 && fresh) {
+              store16(kc + (size_t)key * ROWB + ds * 16, nk[s]);
+              store16(vc + (size_t)key * ROWB + ds * 16, nv[s]);
+            }
+          }
+        }
+      }
       float sc[kSteps][GM];
 #pragma unroll
       for (int s = 0; s < kSteps; ++s) {
@@ -402,9 +446,25 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(KVD_LEAD_PARAMS, AttnA
     }
   }
 
+  // ---- new rows past every query row of this tile (a row tile of early
+  // queries sees only the first ones) are not in its tiles: row tile 0
+  // copies them into the cache as they are
+  if constexpr (kRegNew) {
+    if (rt == 0) {
+      const int from = max(kend, nb0);
+      const int n = (kspan - from) * VPR;  // 16-byte chunks
+      for (int t = threadIdx.x; t < n; t += 64 * nw) {
+        const int key = from + t / VPR, j = t % VPR;
+        const size_t src = (head * a.T_new + (size_t)(key - sp.new_base)) * ROWB + j * 16;
+        const size_t dst = (size_t)key * ROWB + j * 16;
+        store16(kc + dst, load16(static_cast<const char *>(a.k_new) + src));
+        store16(vc + dst, load16(static_cast<const char *>(a.v_new) + src));
+      }
+    }
+  }
   // ---- the fused append's cache writes (from LDS, which holds the rows as
   // rotated and rounded above)
-  if constexpr (FUSED) {
+  if constexpr (FUSED && !kRegNew) {
     if (rt == 0) {
       constexpr int HALF_VECS = kHeadDim / 2 / VE;
       const int n = (kspan - nb0) * HALF_VECS;

@@ -376,7 +376,7 @@ __device__ __forceinline__ void attn_mfma_tile(const Lead &ld, const AttnArgs &a
   if constexpr (FUSED) {
     const bool pair_rot = ROPE && shared_cs;  // uniform
     if (lane < new_items) {
-      const int rr = lane / 4, j = lane % 4, pos = nb0 + rr;
+      const int rr = lane / 4, j = lane % 4;
       if constexpr (ROPE) {
         if (!pair_rot) rotate_key_pair_cs<DT>(nw.klo, nw.khi, ncs, nsn);
       }
