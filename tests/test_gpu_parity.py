@@ -861,6 +861,42 @@ def test_step_self_equals_append_then_attend(dtype, B, Hq, Hkv, N, L, rope, plan
     assert max_err(o2, O.attend_self(q, oc, 0.125, rope_base=rope)) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype,B,Hq,Hkv,N,L", [
+    ("f16", 1, 4, 4, 2, 33),      # new rows straddle two 32-key tiles
+    ("f16", 2, 6, 2, 9, 95),      # grouped rows: early row tiles see only the first new rows
+    ("f16", 1, 3, 3, 16, 16),     # every key new
+    ("f16", 1, 5, 5, 16, 161),
+    ("f32", 2, 4, 4, 7, 70),
+    ("f32", 1, 2, 2, 16, 47),
+])
+@pytest.mark.parametrize("plan_name", ["stream", "w1", "w2_chunk64", "stream_chunk128"])
+def test_step_self_streaming_new_rows(dtype, B, Hq, Hkv, N, L, plan_name):
+    """Fused steps on the streaming kernel without rotation: the wave whose
+    tile holds new rows takes them from k_new / v_new, row tile 0 writes them,
+    and new rows past every query row of a row tile are copied after its key
+    loop. The cache must hold exactly the appended rows (all N of them, with
+    row tiles and splits cutting through the new rows and one-wave
+    workgroups holding two tiles of them) and the output must match."""
+    with kb.plan_override(**PLANS[plan_name]):
+        say(f"case: streaming new rows {dtype} B={B} Hq={Hq} Hkv={Hkv} N={N} L={L} plan={plan_name}")
+        g = np.random.default_rng([51, B, N, L, len(dtype)])
+        k_all = O.narrow(g.standard_normal((B, Hkv, L, 64)), dtype)
+        v_all = O.narrow(g.standard_normal((B, Hkv, L, 64)), dtype)
+        q = O.narrow(g.standard_normal((B, Hq, N, 64)), dtype)
+        old, new = slice(0, L - N), slice(L - N, L)
+        c = kb.Cache(B, Hkv, L + 5, TORCH_DTYPE[dtype])
+        if L > N:
+            kb.kv_append(c, to_dev(k_all[:, :, old], dtype), to_dev(v_all[:, :, old], dtype), 0)
+        out = kb.decode_step_self(to_dev(q, dtype), to_dev(k_all[:, :, new], dtype),
+                                  to_dev(v_all[:, :, new], dtype), c, L, 0.125, ws=_ws())
+        torch.cuda.synchronize()
+        oc = O.ConcatCache(B, Hkv, 64, dtype)
+        oc.append(k_all, v_all)
+        assert _same_bits(from_dev(c.k, dtype)[:, :, :L], oc.k, "appended keys")
+        assert _same_bits(from_dev(c.v, dtype)[:, :, :L], oc.v, "appended values")
+        assert max_err(out, O.attend_self(q, oc, 0.125)) <= TOL[dtype]
+
+
 @pytest.mark.parametrize("dtype,B,Hq,Hkv,N,L,rope", [
     ("bf16", 1, 9, 3, 1, 448, 10000.0),     # the rotary tile splits where the plain one does not
     ("bf16", 1, 9, 3, 1, 448, 0.0),
