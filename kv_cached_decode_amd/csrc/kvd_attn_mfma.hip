@@ -81,8 +81,8 @@ __device__ __forceinline__ void attn_mfma_tile(const Lead &ld, const AttnArgs &a
   // keys 0 .. causal_base) and none of them is new
   const int kstride = NPH * kStep;
   int s0 = k0 + phase * kStep;
-  u32x4 kA[2][2];
-  u32x2 vA[8];
+  u32x4 kA[2][2], kB[2][2];
+  u32x2 vA[8], vB[8];
   // K: tile t, dims chunk kk -> key s + 16t + c, 16 bytes at dims 8gq + 32kk
   // V: lane's 8 keys s + {4gq + j (j < 4), 16 + 4gq + j - 4}, bytes [8c, 8c + 8)
   auto load_whole = [&](int s, u32x4 (&ka)[2][2], u32x2 (&vv)[8]) {
@@ -309,8 +309,19 @@ __device__ __forceinline__ void attn_mfma_tile(const Lead &ld, const AttnArgs &a
     }
   };
 
-  // ---- otherwise the wave's first step goes out now
-  if (!early && s0 < kend) load_step(s0, kA, vA);
+  // ---- otherwise the wave's first step goes out now, into the second
+  // buffer: loaded into the first, whose early loads the compiler cannot rule
+  // out on this path, it waited for every load issued so far (the query's and
+  // the new rows' included) before issuing these. The fused rotary kernel
+  // keeps the first buffer (measured faster there: 6.72 against 6.84 us for
+  // the GQA step at length 768; elsewhere the second buffer wins, e.g. the
+  // 5-draft step at length 448, 6.33 -> 6.01 us).
+  constexpr bool kFirstB = !(FUSED && ROPE);
+  const bool first_b = kFirstB && !early;  // uniform
+  if (!early && s0 < kend) {
+    if (kFirstB) load_step(s0, kB, vB);
+    else load_step(s0, kA, vA);
+  }
 
   // ---- cos / sin of the new rows' keys and of the query row: no memory
   // access, so they are all computed while the loads above are in flight (the
@@ -423,13 +434,16 @@ __device__ __forceinline__ void attn_mfma_tile(const Lead &ld, const AttnArgs &a
   {
     // the next step's loads go out before this step's math (two register
     // buffers in turn; three steps ahead measured no faster in prefill)
-    u32x4 kB[2][2];
-    u32x2 vB[8];
+    // (a wave whose first step is in the second buffer enters at its half)
+    bool skip_a = first_b;  // uniform
     while (s0 < kend) {
-      if (s0 + kstride < kend) load_step(s0 + kstride, kB, vB);
-      compute_step(s0, kA, vA);
-      s0 += kstride;
-      if (s0 >= kend) break;
+      if (!skip_a) {
+        if (s0 + kstride < kend) load_step(s0 + kstride, kB, vB);
+        compute_step(s0, kA, vA);
+        s0 += kstride;
+        if (s0 >= kend) break;
+      }
+      skip_a = false;
       if (s0 + kstride < kend) load_step(s0 + kstride, kA, vA);
       compute_step(s0, kB, vB);
       s0 += kstride;
