@@ -227,7 +227,45 @@ __device__ __forceinline__ void attn_mfma_tile(const Lead &ld, const AttnArgs &a
         const int key = s0 + ((j < 4) ? 4 * gq + j : 16 + 4 * gq + j - 4);
         if (key >= kend) vv[j] = u32x2{0, 0};
       }
-      if constexpr (FUSED) {  // the step's new rows come from the wave's LDS slice
+      if constexpr (FUSED && ROPE) {
+        // the step's new rows come from the wave's LDS slice: every lane reads
+        // at its row clamped into the slice and selects. In the rotary tile a
+        // read inside a per-lane branch waited for its own round trip, one
+        // after another: about 1 us for the step holding the new row of a GQA
+        // decode step (6.71 -> 6.50 us at length 768). The other fused tiles
+        // keep the reads in the branch (the 5-draft step at length 448
+        // measured 6.01 against 6.28 us the other way).
+        u32x4 nk[2][2];
+        u32x4 nvr[8];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int r = min(max(s0 + 16 * t + c - nb0, 0), kMaxFusedRows - 1);
+          nk[t][0] = my_new[r * VPR + gq];
+          nk[t][1] = my_new[r * VPR + gq + VPR / 2];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int key = s0 + ((j < 4) ? 4 * gq + j : 16 + 4 * gq + j - 4);
+          const int r = min(max(key - nb0, 0), kMaxFusedRows - 1);
+          nvr[j] = my_new[(kMaxFusedRows + r) * VPR + c / 2];
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int key = s0 + 16 * t + c;
+          const bool fresh = key < kend && key >= nb0;
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ka[t][kk][i] = fresh ? nk[t][kk][i] : ka[t][kk][i];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int key = s0 + ((j < 4) ? 4 * gq + j : 16 + 4 * gq + j - 4);
+          const bool fresh = key < kend && key >= nb0;
+          const u32x2 nv2 = (c & 1) ? u32x2{nvr[j][2], nvr[j][3]} : u32x2{nvr[j][0], nvr[j][1]};
+          vv[j] = fresh ? nv2 : vv[j];
+        }
+      } else if constexpr (FUSED) {  // the step's new rows come from the wave's LDS slice
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int key = s0 + 16 * t + c;
@@ -349,8 +387,10 @@ __device__ __forceinline__ void attn_mfma_tile(const Lead &ld, const AttnArgs &a
   double th_pair = 0.0, c_pair = 1.0, s_pair = 0.0;
   if (shared_cs) {
     if constexpr (ROPE && RW == 1 && FUSED) {
-      th_pair = rope_theta_at(a.rope_theta, lane & 31);  // exact, as kv_append's
-      if (lane < new_items / (VPR / 2) * 32) rope_angle_cs64(nb0 + lane / 32, th_pair, c_pair, s_pair);
+      if (new_items > 0) {  // uniform: only the waves that take new rows rotate them
+        th_pair = rope_theta_at(a.rope_theta, lane & 31);  // exact, as kv_append's
+        if (lane < new_items / (VPR / 2) * 32) rope_angle_cs64(nb0 + lane / 32, th_pair, c_pair, s_pair);
+      }
     }
     if constexpr (ROPE && RW == 1) {
       float *tab = s_rope + wave * kRopeSlice;
