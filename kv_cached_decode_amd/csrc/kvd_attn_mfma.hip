@@ -232,9 +232,10 @@ __device__ __forceinline__ void attn_mfma_tile(const Lead &ld, const AttnArgs &a
         // at its row clamped into the slice and selects. In the rotary tile a
         // read inside a per-lane branch waited for its own round trip, one
         // after another: about 1 us for the step holding the new row of a GQA
-        // decode step (6.71 -> 6.50 us at length 768). The other fused tiles
-        // keep the reads in the branch (the 5-draft step at length 448
-        // measured 6.01 against 6.28 us the other way).
+        // decode step (with the new-key angles computed only by the waves that
+        // take new rows, below: 6.70 -> 6.47 us at length 768). The other
+        // fused tiles keep the reads in the branch (the 5-draft step at length
+        // 448 measured 6.01 against 6.28 us the other way).
         u32x4 nk[2][2];
         u32x4 nvr[8];
 #pragma unroll
