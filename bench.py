@@ -234,14 +234,20 @@ def _graph_period(torch, calls, reps: int = 20):
     # the GPU spins (outside the timed region) while the host queues every
     # replay, so that no replay waits for the host: timed replays run back
     # to back (without it the beam workload's cross period read 15 us
-    # against 6.7 on the same kernel)
-    torch.cuda._sleep(GPU_QUEUE_SLEEP_CYCLES)
-    a.record()
-    for _ in range(reps):
-        g.replay()
-    b.record()
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) * 1e-3 / (reps * len(calls))
+    # against 6.7 on the same kernel). Three such rounds, the fastest kept:
+    # a round the host still fell behind in (19.7 us once, in the full run's
+    # beam record) is not a period of the kernels.
+    best = None
+    for _ in range(3):
+        torch.cuda._sleep(GPU_QUEUE_SLEEP_CYCLES)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b) * 1e-3 / (reps * len(calls))
+        best = t if best is None else min(best, t)
+    return best
 
 
 def time_cross_kernel(torch, kb, eng: Engine, reps: int = 8):
@@ -538,7 +544,7 @@ def headline(torch, kb, I, args) -> dict:
     r = roof(CROSS_BYTES, k_period, "decode_attn_cross (attn_kernel<f16, 1 row, 4 waves>, 12 splits x 20 heads)")
     r["traffic"] = measured_traffic()
     r["timing"] = ("per-launch time of 32 back-to-back launches (one per layer) in a hipGraph, "
-                   "HIP events on the replay stream, 20 replays; the same kernel launched alone, "
+                   "HIP events on the replay stream, 20 replays, fastest of 3 rounds; the same kernel launched alone, "
                    f"HIP events at its begin/end (hipExtLaunchKernel, 256 launches): {k_avg * 1e6:.3f} us")
     lengths = [s + 1 for s in seq]
     return {
