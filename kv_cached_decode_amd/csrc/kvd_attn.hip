@@ -478,15 +478,31 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(KVD_LEAD_PARAMS, AttnA
     }
   }
 
-  // ---- merge the key-row groups of the wave
+  // ---- merge the key-row groups of the wave. With 8 lanes per key row and
+  // 8 values per lane (16-bit caches), lanes 8 apart first split the values:
+  // each keeps one half and adds its partner's copy of that half, so the
+  // exchanges over lanes 16 and 32 apart sum 4 values instead of 8 (12
+  // exchanges instead of 24); the lane then holds dims ds * VE + 4 * (kr & 1)
+  // onward (the rest of o is not read again).
+  constexpr bool kSplitMerge = LPR == 8 && VE == 8;
+  const bool upper = (lane & 8) != 0;  // kr & 1
 #pragma unroll
   for (int g = 0; g < GM; ++g) {
     if (g < gcount) {
       const float M = groups_max<LPR>(m[g]);
       const float f = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[g] - M);
       l[g] = groups_sum<LPR>(l[g] * f);
+      if constexpr (kSplitMerge) {
 #pragma unroll
-      for (int e = 0; e < VE; ++e) o[g][e] = groups_sum<LPR>(o[g][e] * f);
+        for (int j = 0; j < 4; ++j) {
+          const float lo_v = o[g][j] * f, hi_v = o[g][j + 4] * f;
+          const float keep = upper ? hi_v : lo_v, send = upper ? lo_v : hi_v;
+          o[g][j] = pair_sum32(pair_sum16(keep + lane_xor8(send)));
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < VE; ++e) o[g][e] = groups_sum<LPR>(o[g][e] * f);
+      }
       m[g] = M;
     }
   }
@@ -497,13 +513,18 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(KVD_LEAD_PARAMS, AttnA
   float *sm_o = smem;                   // [nw][GM][D]
   float *sm_m = smem + NWMAX * GM * D;  // [nw][GM]
   float *sm_l = sm_m + NWMAX * GM;      // [nw][GM]
-  if (kr == 0) {
+  if (kSplitMerge ? kr < 2 : kr == 0) {
 #pragma unroll
     for (int g = 0; g < GM; ++g) {
       if (g < gcount) {
+        if constexpr (kSplitMerge) {
 #pragma unroll
-        for (int e = 0; e < VE; ++e) sm_o[(wave * GM + g) * D + ds * VE + e] = o[g][e];
-        if (ds == 0) {
+          for (int j = 0; j < 4; ++j) sm_o[(wave * GM + g) * D + ds * VE + (upper ? 4 : 0) + j] = o[g][j];
+        } else {
+#pragma unroll
+          for (int e = 0; e < VE; ++e) sm_o[(wave * GM + g) * D + ds * VE + e] = o[g][e];
+        }
+        if (ds == 0 && kr == 0) {
           sm_m[wave * GM + g] = m[g];
           sm_l[wave * GM + g] = l[g];
         }
