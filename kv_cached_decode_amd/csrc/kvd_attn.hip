@@ -479,13 +479,13 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(KVD_LEAD_PARAMS, AttnA
   }
 
   // ---- merge the key-row groups of the wave. With 8 lanes per key row and
-  // 8 values per lane (16-bit caches), lanes 8 apart first split the values:
-  // each keeps one half and adds its partner's copy of that half, so the
-  // exchanges over lanes 16 and 32 apart sum 4 values instead of 8 (12
-  // exchanges instead of 24); the lane then holds dims ds * VE + 4 * (kr & 1)
-  // onward (the rest of o is not read again).
+  // 8 values per lane (16-bit caches), each exchange level splits the values
+  // (a lane keeps one half and adds its partner's copy of that half): lanes
+  // 8 apart 8 -> 4, 16 apart 4 -> 2, 32 apart 2 -> 1, 7 exchanges instead of
+  // 24, the same additions in the same pairs; every lane ends with one dim
+  // of the wave's output (the rest of o is not read again).
   constexpr bool kSplitMerge = LPR == 8 && VE == 8;
-  const bool upper = (lane & 8) != 0;  // kr & 1
+  const bool upper = (lane & 8) != 0, upper16 = (lane & 16) != 0, upper32 = (lane & 32) != 0;
 #pragma unroll
   for (int g = 0; g < GM; ++g) {
     if (g < gcount) {
@@ -493,12 +493,17 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(KVD_LEAD_PARAMS, AttnA
       const float f = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[g] - M);
       l[g] = groups_sum<LPR>(l[g] * f);
       if constexpr (kSplitMerge) {
+        float v4[4], v2[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 4; ++j) {  // lanes 8 apart: 8 values -> 4
           const float lo_v = o[g][j] * f, hi_v = o[g][j + 4] * f;
-          const float keep = upper ? hi_v : lo_v, send = upper ? lo_v : hi_v;
-          o[g][j] = pair_sum32(pair_sum16(keep + lane_xor8(send)));
+          v4[j] = (upper ? hi_v : lo_v) + lane_xor8(upper ? lo_v : hi_v);
         }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)  // lanes 16 apart: 4 -> 2
+          v2[j] = (upper16 ? v4[j + 2] : v4[j]) + partner16(upper16 ? v4[j] : v4[j + 2], upper16);
+        // lanes 32 apart: 2 -> 1, dim ds * VE + 4 * (lane bit 3) + 2 * (bit 4) + (bit 5)
+        o[g][0] = (upper32 ? v2[1] : v2[0]) + partner32(upper32 ? v2[0] : v2[1], upper32);
       } else {
 #pragma unroll
         for (int e = 0; e < VE; ++e) o[g][e] = groups_sum<LPR>(o[g][e] * f);
@@ -513,13 +518,12 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(KVD_LEAD_PARAMS, AttnA
   float *sm_o = smem;                   // [nw][GM][D]
   float *sm_m = smem + NWMAX * GM * D;  // [nw][GM]
   float *sm_l = sm_m + NWMAX * GM;      // [nw][GM]
-  if (kSplitMerge ? kr < 2 : kr == 0) {
+  if (kSplitMerge || kr == 0) {
 #pragma unroll
     for (int g = 0; g < GM; ++g) {
       if (g < gcount) {
         if constexpr (kSplitMerge) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) sm_o[(wave * GM + g) * D + ds * VE + (upper ? 4 : 0) + j] = o[g][j];
+          sm_o[(wave * GM + g) * D + ds * VE + (upper ? 4 : 0) + (upper16 ? 2 : 0) + (upper32 ? 1 : 0)] = o[g][0];
         } else {
 #pragma unroll
           for (int e = 0; e < VE; ++e) sm_o[(wave * GM + g) * D + ds * VE + e] = o[g][e];

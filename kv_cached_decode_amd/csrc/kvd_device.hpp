@@ -333,6 +333,22 @@ __device__ __forceinline__ float pair_max32(float x) {
   return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
 }
 
+// The value x holds in the lane 16 (resp. 32) apart: v_permlane16_swap with
+// both operands x leaves the lower row of each pair of 16-lane rows its own
+// value in the first result and the partner's in the second, the upper row
+// the other way round (resp. the lower and upper 32 lanes); `upper` is this
+// lane's bit 4 (resp. 5).
+__device__ __forceinline__ float partner16(float x, bool upper) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)(upper ? r[0] : r[1]));
+}
+__device__ __forceinline__ float partner32(float x, bool upper) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)(upper ? r[0] : r[1]));
+}
+
 // Reduce over the 64 / FROM aligned groups of FROM lanes (lanes that differ
 // only in the bits >= FROM): max or sum, every lane ends with the result.
 // (FROM = 1: the whole wavefront.)
