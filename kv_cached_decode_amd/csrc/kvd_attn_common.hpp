@@ -210,9 +210,12 @@ __device__ __forceinline__ void merge_rows_nb(const AttnArgs &a, size_t tile_id,
       if (g < gcount) {
         const float m = (lane < S) ? mj[r] : -INFINITY;
         const float l = (lane < S) ? lj[r] : 0.f;
-        const float M = groups_max<1>(m);
+        // over the first NB lanes only (every partial sits in one; the rest
+        // add -inf and zeros, so the full wavefront reduction gives the same
+        // bits): the max where the weights are taken, the sum broadcast
+        const float M = lanes_max<NB>(m);
         const float wj = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M);
-        const float inv = __builtin_amdgcn_rcpf(groups_sum<1>(l * wj));
+        const float inv = __builtin_amdgcn_rcpf(lanes_sum_all<NB>(l * wj));
         float O = 0.f;
 #pragma unroll
         for (int j = 0; j < NB; ++j) {

@@ -371,6 +371,32 @@ __device__ __forceinline__ float groups_sum(float x) {
   return pair_sum32(x);
 }
 
+// Max over lanes 0 .. N - 1 (N a power of two, 8 to 64), left in those
+// lanes; sum over them, given to every lane. The same steps, in the same
+// order, as the first ones of the wavefront reductions above.
+template <int N>
+__device__ __forceinline__ float lanes_max(float x) {
+  static_assert(N >= 8 && N <= 64 && (N & (N - 1)) == 0, "8, 16, 32 or 64 lanes");
+  if constexpr (N == 64) return groups_max<1>(x);
+  x = fmaxf(x, dpp_mov<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp_mov<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp_mov<kDppHalfMirror>(x));
+  if constexpr (N >= 16) x = fmaxf(x, lane_xor8(x));
+  if constexpr (N >= 32) x = pair_max16(x);
+  return x;
+}
+template <int N>
+__device__ __forceinline__ float lanes_sum_all(float x) {
+  static_assert(N >= 8 && N <= 64 && (N & (N - 1)) == 0, "8, 16, 32 or 64 lanes");
+  if constexpr (N == 64) return groups_sum<1>(x);
+  x += dpp_mov<kDppQuadXor1>(x);
+  x += dpp_mov<kDppQuadXor2>(x);
+  x += dpp_mov<kDppHalfMirror>(x);
+  if constexpr (N >= 16) x += lane_xor8(x);
+  if constexpr (N >= 32) x = pair_sum16(x);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+}
+
 template <int LANES> __device__ __forceinline__ float group_sum(float x);
 template <> __device__ __forceinline__ float group_sum<8>(float x) {
   x += dpp_mov<kDppQuadXor1>(x);
