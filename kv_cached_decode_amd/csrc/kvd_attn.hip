@@ -77,7 +77,7 @@ __global__ __launch_bounds__(64 * NWMAX) void attn_kernel(KVD_LEAD_PARAMS, AttnA
   const RowSpan sp = row_span<RAGGED>(a, bkv, ld.L, ld.causal_base, ld.new_base);
   const int kspan = min(k0 + ld.chunk, sp.L);
 
-  const size_t head = (size_t)bkv * ld.Hkv + hk;
+  const size_t head = (size_t)unit;  // bkv * Hkv + hk: no division in front of the first loads
   char *kc = ld.k + head * ld.S_max * ROWB;
   char *vc = ld.v + head * ld.S_max * ROWB;
   const int nb0 = max(k0, sp.new_base);  // first new row of this key range
