@@ -172,10 +172,12 @@ __device__ __forceinline__ void attn_mfma_tile(const Lead &ld, const AttnArgs &a
 
   // ---- the keys this lane's row sees
   const int lim = active ? ((sp.causal_base < 0) ? sp.L : sp.causal_base + r.i + 1) : 0;
-  const int kend = __builtin_amdgcn_readfirstlane(min(kspan, (int)groups_max<1>((float)lim)));
+  // (lanes 16 apart hold the same row: the 16 rows' bound is a max over
+  // lanes 0 .. 15, taken from lane 0)
+  const int kend = __builtin_amdgcn_readlane(min(kspan, (int)lanes_max<16>((float)lim)), 0);
   // below lim_lo every row of the wave sees every key
   const int lim_lo =
-      __builtin_amdgcn_readfirstlane(-(int)groups_max<1>(-(float)(active ? lim : INT_MAX / 2)));
+      __builtin_amdgcn_readlane(-(int)lanes_max<16>(-(float)(active ? lim : INT_MAX / 2)), 0);
 
   // ---- query operand: dims [8gq, +8) and [32 + 8gq, +8) of the row; a rotary
   // pair (i, i + 32) sits in one lane
