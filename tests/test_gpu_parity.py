@@ -817,6 +817,35 @@ def test_cross_shared_grouped_rows(dtype, B, Hq, Hkv, N, F, plan):
     assert max_err(out, O.attend_cross(q, ox, 0.125)) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("N", [1, 5])
+@pytest.mark.parametrize("F,waves,chunk", [
+    (1500, 1, 192),   # 8 partials: the smallest merge load count, full
+    (1100, 1, 128),   # 9: the next load count (16) with 7 partials unused
+    (1500, 1, 96),    # 16
+    (2100, 1, 128),   # 17: load count 32
+    (1499, 2, 64),    # 24, ragged last split
+    (1056, 1, 32),    # 33: load count 64
+    (2048, 1, 32),    # 64: the most partials a merge takes
+])
+def test_cross_split_counts(dtype, N, F, waves, chunk):
+    """Split counts on both sides of every load count of the merge (8, 16,
+    32, 64 partials): the merge's max and sum run over the first 8, 16, 32
+    or 64 lanes only, so each width is checked with every lane of it used
+    and with lanes past the split count."""
+    say(f"case: cross split counts {dtype} N={N} F={F} waves={waves} chunk={chunk}")
+    g = np.random.default_rng(F + N)
+    xk = O.narrow(g.standard_normal((1, 4, F, 64)), dtype)
+    xv = O.narrow(g.standard_normal((1, 4, F, 64)), dtype)
+    q = O.narrow(g.standard_normal((2, 4, N, 64)) / 4, dtype)
+    shared = kb.Cache.wrap(to_dev(xk, dtype), to_dev(xv, dtype))
+    with kb.plan_override(waves=waves, chunk=chunk):
+        out = kb.decode_attn_cross(to_dev(q, dtype), shared, F, 0.125, ws=_ws())
+    ox = O.ConcatCache(1, 4, 64, dtype)
+    ox.set_once(xk, xv)
+    assert max_err(out, O.attend_cross(q, ox, 0.125)) <= TOL[dtype]
+
+
 # --------------------------------------------------- fused append + attend ----
 
 @pytest.mark.parametrize("dtype,B,Hq,Hkv,N,L,rope", [
